@@ -1,0 +1,159 @@
+/*
+ * laplex.h -- C ABI of the MI355X (gfx950) LAPLEX operator library.
+ *
+ * LAPLEX is the exact Laplace-kernel operator of "LAPLEX: The FFT of
+ * Learnable Laplace Kernels" (Struski, Blazhko, Kubaty, Tabor).  Citations
+ * below name the section of the technical summary published with the
+ * gist.science pages of that title ("summary §2.1" ...).
+ *
+ *   operator (summary §2.1):  K = LAPLEX(a, phi; b, psi),
+ *       K_ij = exp(-|a_i - b_j|) * cos(phi_i - psi_j),   a in R^n, b in R^k.
+ *   Without phases the cosine factor is 1.  A symmetric plan has b = a.
+ *   The temperature of the pages is fixed to 1 (scale the anchors by 1/t for
+ *   another temperature).
+ *
+ *   algorithm (summary §2.2): sort the anchors; apply the lower and upper
+ *   triangular parts by a prefix and a suffix scan of the recurrence
+ *   y_{i+1} = x_{i+1} + exp(a_i - a_{i+1}) y_i; for a != b collect the
+ *   contributions of one side into the intervals of the other (vectors u, v)
+ *   and run the same scans; weighted Gram M = A diag(D) A^T in O(n^2 + k log n).
+ *   The dense matrix is never formed.
+ *
+ * Conventions for every call:
+ *   - All array arguments are DEVICE pointers to float32 (fp32) data on the
+ *     current HIP device, except where stated.  Vectors are contiguous; a
+ *     batch of vectors is row-major [batch][length].  Offsets are 64-bit.
+ *   - `stream` is a hipStream_t passed as void* (NULL = legacy default stream).
+ *   - Functions return a laplex_status and never abort or throw.  Argument
+ *     checks run on the host before any HIP call, so an invalid call returns
+ *     LAPLEX_ERR_INVALID_ARGUMENT without touching the device.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Inputs are borrowed only for the duration of the call.
+ */
+#ifndef LAPLEX_H
+#define LAPLEX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct laplex_plan_s* laplex_plan;
+
+typedef enum {
+    LAPLEX_OK = 0,
+    LAPLEX_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, flag or overlap */
+    LAPLEX_ERR_NONFINITE_ANCHOR = 2, /* NaN or +-Inf in a, b, phi or psi       */
+    LAPLEX_ERR_OUT_OF_MEMORY = 3,    /* device allocation failed               */
+    LAPLEX_ERR_UNSUPPORTED = 4,      /* valid request this build does not do   */
+    LAPLEX_ERR_DEVICE = 5,           /* a HIP call failed: see laplex_last_error */
+    LAPLEX_ERR_NO_DEVICE = 6         /* no HIP device visible                  */
+} laplex_status;
+
+/* Plan flags reported by laplex_plan_info. */
+#define LAPLEX_PLAN_SYMMETRIC 1
+#define LAPLEX_PLAN_PHASED 2
+
+/*
+ * laplex_plan_create -- sort the anchors and keep what apply/gram need.
+ *   (summary §2.2: "after sorting the anchors")
+ *
+ *   out    host pointer; receives the plan, or NULL on any error.
+ *   a      device, float32[n], the row anchors.  1 <= n <= 2^31 - 1.
+ *   b      device, float32[k], the column anchors, or NULL for a symmetric
+ *          plan (b := a; then k must be 0 or n).  1 <= k <= 2^31 - 1.
+ *   phi    device, float32[n] row phases, and
+ *   psi    device, float32[k] (float32[n] if symmetric) column phases;
+ *          both NULL (unphased) or both non-NULL (phased operator).
+ *   stream stream on which all device work is ordered.
+ *
+ *   The sort order of each anchor set is ascending IEEE order with -0.0
+ *   before +0.0 and ties kept in ascending original index (a stable sort),
+ *   so the permutation is deterministic.  NaN/Inf anchors or phases give
+ *   LAPLEX_ERR_NONFINITE_ANCHOR.  The plan copies everything it needs into
+ *   device memory it owns; the call synchronizes `stream` once before it
+ *   returns, after which a, b, phi, psi may be freed.
+ */
+laplex_status laplex_plan_create(laplex_plan* out, const float* a, int64_t n,
+                                 const float* b, int64_t k,
+                                 const float* phi, const float* psi, void* stream);
+
+/*
+ * laplex_apply -- y = K x (transpose = 0) or y = K^T x (transpose = 1).
+ *   (summary §2.2: prefix/suffix scans; general case via vectors u, v)
+ *
+ *   x, y   device float32 arrays, [batch][in] and [batch][out] row-major with
+ *          (in, out) = (k, n) for transpose = 0 and (n, k) for transpose = 1
+ *          (a symmetric plan has k = n).  x and y must not overlap.
+ *   batch  number of vectors, >= 1.
+ *   Asynchronous on `stream`; the caller keeps x and y alive until the stream
+ *   reaches this work.  One apply or gram per plan may be in flight at a
+ *   time (they share the plan's workspace).  The workspace grows on demand
+ *   (the only allocation on this path).  NaN/Inf in x propagate per IEEE.
+ */
+laplex_status laplex_apply(laplex_plan plan, const float* x, float* y, int64_t batch,
+                           int transpose, void* stream);
+
+/*
+ * laplex_gram -- weighted Gram matrix M = A diag(D) A^T with A = K (n x k).
+ *   (summary §2.2, Gram operators: O(n^2 + k log n), not O(n^2 k))
+ *
+ *   D      device float32[k] weights (k = n for a symmetric plan); any finite
+ *          real values.
+ *   M      device float32[n][n], row-major, rows and columns in the original
+ *          order of a.  Needs n * n <= 2^40 (else INVALID_ARGUMENT).
+ *   Phased plans return LAPLEX_ERR_UNSUPPORTED.  Asynchronous on `stream`.
+ */
+laplex_status laplex_gram(laplex_plan plan, const float* D, float* M, void* stream);
+
+/* Releases all device memory of the plan (synchronizes the device first).
+ * NULL is accepted. */
+laplex_status laplex_plan_destroy(laplex_plan plan);
+
+/*
+ * Introspection.  laplex_plan_perm: *perm_dev receives a DEVICE pointer to the
+ * plan's permutation uint32[len] (rank r -> original index) of side 0 (a) or
+ * side 1 (b; the same as side 0 for a symmetric plan).  It stays valid until
+ * the plan is destroyed.  laplex_plan_sorted likewise gives the sorted
+ * anchors float32[len].  laplex_plan_info reports n, k and LAPLEX_PLAN_* flags.
+ */
+laplex_status laplex_plan_perm(laplex_plan plan, int side, const uint32_t** perm_dev);
+laplex_status laplex_plan_sorted(laplex_plan plan, int side, const float** sorted_dev);
+laplex_status laplex_plan_info(laplex_plan plan, int64_t* n, int64_t* k, int* flags);
+
+/*
+ * Algorithm choice for a != b (both give the same operator, exactly up to
+ * rounding):
+ *   LAPLEX_ALGO_AUTO      scan over the smaller side (default);
+ *   LAPLEX_ALGO_BUCKET    the pages' general case: bucket the input side into
+ *                         the intervals of the sorted output side (u, v), scan
+ *                         over the output side, write back in original order;
+ *   LAPLEX_ALGO_EVALUATE  scan over the sorted input side, then evaluate each
+ *                         output by bisection into the sorted input side.
+ * Symmetric plans ignore the setting.
+ */
+#define LAPLEX_OPT_GENERAL_ALGO 1
+#define LAPLEX_ALGO_AUTO 0
+#define LAPLEX_ALGO_BUCKET 1
+#define LAPLEX_ALGO_EVALUATE 2
+laplex_status laplex_plan_set_option(laplex_plan plan, int option, int64_t value);
+
+/* Kernel timing: while enabled, every kernel the library launches is
+ * bracketed by HIP events on its stream.  laplex_profile_collect waits for
+ * the recorded events and folds their durations into per-kernel totals;
+ * laplex_profile_entry reads entry `i` (returns INVALID_ARGUMENT past the
+ * end).  Names are static strings.  Not thread-safe; for benchmarks. */
+laplex_status laplex_profile_enable(int on);
+laplex_status laplex_profile_reset(void);
+laplex_status laplex_profile_collect(void);
+laplex_status laplex_profile_entry(int i, const char** name, int64_t* launches, double* total_ms);
+
+const char* laplex_status_str(laplex_status s);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* laplex_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LAPLEX_H */

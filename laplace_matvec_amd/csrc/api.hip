@@ -1,0 +1,653 @@
+// C ABI of the LAPLEX library: plans, argument checks, dispatch, timing.
+//
+// The operator and its fast algorithm follow the technical summary of
+// "LAPLEX: The FFT of Learnable Laplace Kernels" (§2.1 operator, §2.2 scan
+// algebra, general case and Gram); see include/laplex.h for the contract.
+//
+// Every argument check runs before the first HIP call, so invalid calls are
+// rejected on any host, GPU or not.  Device memory comes from a pool owned
+// by the library (stream-ordered allocation, memory kept for reuse), so
+// repeated plans and growing workspaces do not pay for fresh allocations.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "laplex.h"
+#include "lx_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int64_t kMaxLen = 0x7FFFFFFFll;  // permutations are uint32
+
+laplex_status fail(laplex_status st, const std::string& msg)
+{
+    g_last_error = msg;
+    return st;
+}
+
+laplex_status from_hip(hipError_t e, const char* where)
+{
+    if (e == hipSuccess) return LAPLEX_OK;
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
+        return fail(LAPLEX_ERR_OUT_OF_MEMORY, std::string(where) + ": " + hipGetErrorString(e));
+    if (e == hipErrorNoDevice || e == hipErrorInvalidDevice)
+        return fail(LAPLEX_ERR_NO_DEVICE, std::string(where) + ": " + hipGetErrorString(e));
+    return fail(LAPLEX_ERR_DEVICE, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+#define LX_TRY(call, where)                                          \
+    do {                                                             \
+        const laplex_status lx_s_ = from_hip((call), (where));       \
+        if (lx_s_ != LAPLEX_OK) return lx_s_;                        \
+    } while (0)
+
+inline int64_t pad64(int64_t x) { return (x + 63) & ~(int64_t)63; }
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// ------------------------------------------------------------ memory pool
+
+struct DevicePool {
+    hipMemPool_t pool = nullptr;
+    bool tried = false;
+};
+std::mutex g_pool_mu;
+std::vector<DevicePool> g_pools;
+
+hipMemPool_t pool_for(int dev)
+{
+    std::lock_guard<std::mutex> lk(g_pool_mu);
+    if ((int)g_pools.size() <= dev) g_pools.resize(dev + 1);
+    DevicePool& p = g_pools[dev];
+    if (!p.tried) {
+        p.tried = true;
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        if (hipMemPoolCreate(&p.pool, &props) == hipSuccess) {
+            uint64_t keep = UINT64_MAX;
+            (void)hipMemPoolSetAttribute(p.pool, hipMemPoolAttrReleaseThreshold, &keep);
+        } else {
+            p.pool = nullptr;
+            (void)hipGetLastError();
+        }
+    }
+    return p.pool;
+}
+
+hipError_t dev_alloc(void** ptr, size_t bytes, int dev, hipStream_t s)
+{
+    *ptr = nullptr;
+    if (bytes == 0) bytes = 256;
+    hipMemPool_t pool = pool_for(dev);
+    if (pool) return hipMallocFromPoolAsync(ptr, bytes, pool, s);
+    return hipMalloc(ptr, bytes);
+}
+
+void dev_free(void* ptr, int dev, hipStream_t s)
+{
+    if (!ptr) return;
+    if (pool_for(dev)) (void)hipFreeAsync(ptr, s);
+    else (void)hipFree(ptr);
+}
+
+// ------------------------------------------------------------- profiling
+
+struct ProfEntry {
+    const char* name;
+    int64_t launches;
+    double total_ms;
+};
+struct Pending {
+    const char* name;
+    hipEvent_t a, b;
+};
+bool g_prof_on = false;
+std::vector<ProfEntry> g_prof;
+std::vector<Pending> g_pending;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event()
+{
+    if (!g_event_pool.empty()) {
+        hipEvent_t e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+}  // namespace
+
+namespace lx {
+
+int prof_begin(const char* name, hipStream_t s)
+{
+    if (!g_prof_on) return -1;
+    Pending p{name, take_event(), take_event()};
+    if (!p.a || !p.b) return -1;
+    (void)hipEventRecord(p.a, s);
+    g_pending.push_back(p);
+    return (int)g_pending.size() - 1;
+}
+
+void prof_end(int token, hipStream_t s)
+{
+    if (token < 0 || token >= (int)g_pending.size()) return;
+    (void)hipEventRecord(g_pending[token].b, s);
+}
+
+}  // namespace lx
+
+// ----------------------------------------------------------------- plans
+
+struct laplex_plan_s {
+    int device = 0;
+    int64_t n = 0, k = 0;
+    bool sym = true, phased = false;
+    int algo = LAPLEX_ALGO_AUTO;
+    int lds_bytes = 0;
+    // sorted sides
+    float* sa = nullptr;
+    uint32_t* pa = nullptr;
+    float* sb = nullptr;  // general only (symmetric: aliases sa)
+    uint32_t* pb = nullptr;
+    // copies in original order (general only)
+    float* a0 = nullptr;
+    float* b0 = nullptr;
+    float* phi0 = nullptr;
+    float* psi0 = nullptr;
+    // phase factors by rank: phi by a's order, psi by b's order (a's if symmetric)
+    float* cphi = nullptr;
+    float* sphi = nullptr;
+    float* cpsi = nullptr;
+    float* spsi = nullptr;
+    // workspace for apply / gram
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    std::vector<void*> owned;
+};
+
+namespace {
+
+struct DeviceGuard {
+    int prev = -1;
+    explicit DeviceGuard(int dev)
+    {
+        if (hipGetDevice(&prev) == hipSuccess && prev != dev) (void)hipSetDevice(dev);
+        else prev = -1;
+    }
+    ~DeviceGuard()
+    {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+hipError_t plan_alloc(laplex_plan p, void** out, size_t bytes, hipStream_t s)
+{
+    hipError_t e = dev_alloc(out, bytes, p->device, s);
+    if (e == hipSuccess) p->owned.push_back(*out);
+    return e;
+}
+
+void plan_release(laplex_plan p)
+{
+    if (!p) return;
+    hipStream_t s = nullptr;
+    for (void* q : p->owned) dev_free(q, p->device, s);
+    if (p->ws) dev_free(p->ws, p->device, s);
+    (void)hipStreamSynchronize(s);
+    delete p;
+}
+
+hipError_t ensure_ws(laplex_plan p, size_t bytes, hipStream_t s)
+{
+    if (p->ws_bytes >= bytes) return hipSuccess;
+    if (p->ws) dev_free(p->ws, p->device, s);
+    p->ws = nullptr;
+    p->ws_bytes = 0;
+    const size_t want = align256(bytes + bytes / 8);
+    hipError_t e = dev_alloc(&p->ws, want, p->device, s);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        e = dev_alloc(&p->ws, align256(bytes), p->device, s);
+        if (e != hipSuccess) return e;
+        p->ws_bytes = align256(bytes);
+        return hipSuccess;
+    }
+    p->ws_bytes = want;
+    return hipSuccess;
+}
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb)
+{
+    const char* x = (const char*)a;
+    const char* y = (const char*)b;
+    return x < y + nb && y < x + na;
+}
+
+laplex_status check_device()
+{
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return fail(LAPLEX_ERR_NO_DEVICE, "no HIP device visible");
+    }
+    return LAPLEX_OK;
+}
+
+// Bump allocator over the plan workspace.
+struct Carve {
+    char* base;
+    size_t off = 0;
+    explicit Carve(void* b) : base((char*)b) {}
+    template <class T>
+    T* take(size_t count)
+    {
+        T* p = (T*)(base + off);
+        off += align256(count * sizeof(T));
+        return p;
+    }
+};
+
+// Workspace of one scan along a side of length len.
+size_t scan_ws_bytes(int64_t len, int64_t batch, int ch, bool keep_xs, bool tables, bool uv)
+{
+    const int64_t ld = pad64(len);
+    const int64_t tiles = (len + lx::kScanTile - 1) / lx::kScanTile;
+    size_t b = 0;
+    const size_t row = align256((size_t)ch * batch * ld * 4);
+    if (keep_xs) b += row;
+    if (tables) b += 2 * row;
+    if (uv) b += 2 * row;
+    b += align256((size_t)ch * batch * tiles * 4 * 8);
+    b += align256((size_t)ch * batch * tiles * 2 * 8);
+    return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* laplex_status_str(laplex_status s)
+{
+    switch (s) {
+        case LAPLEX_OK: return "ok";
+        case LAPLEX_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case LAPLEX_ERR_NONFINITE_ANCHOR: return "non-finite anchor or phase";
+        case LAPLEX_ERR_OUT_OF_MEMORY: return "out of device memory";
+        case LAPLEX_ERR_UNSUPPORTED: return "unsupported";
+        case LAPLEX_ERR_DEVICE: return "device error";
+        case LAPLEX_ERR_NO_DEVICE: return "no device";
+    }
+    return "unknown status";
+}
+
+const char* laplex_last_error(void) { return g_last_error.c_str(); }
+
+laplex_status laplex_plan_create(laplex_plan* out, const float* a, int64_t n, const float* b, int64_t k,
+                                 const float* phi, const float* psi, void* stream)
+{
+    if (out) *out = nullptr;
+    if (!out) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "out is NULL");
+    if (!a) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "a is NULL");
+    if (n < 1 || n > kMaxLen) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "n must be in [1, 2^31-1]");
+    const bool sym = b == nullptr;
+    if (sym && k != 0 && k != n) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "symmetric plan: k must be 0 or n");
+    if (!sym && (k < 1 || k > kMaxLen)) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "k must be in [1, 2^31-1]");
+    if ((phi == nullptr) != (psi == nullptr))
+        return fail(LAPLEX_ERR_INVALID_ARGUMENT, "phi and psi: give both or neither");
+    if (sym) k = n;
+    laplex_status st = check_device();
+    if (st != LAPLEX_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    laplex_plan p = new laplex_plan_s();
+    p->n = n;
+    p->k = k;
+    p->sym = sym;
+    p->phased = phi != nullptr;
+    void* scratch = nullptr;
+    uint32_t* flag = nullptr;
+    uint32_t host_flag = 0;
+    auto bail = [&](laplex_status code) {
+        if (scratch) dev_free(scratch, p->device, s);
+        plan_release(p);
+        return code;
+    };
+#define LX_PLAN_TRY(call, where)                                  \
+    do {                                                         \
+        const laplex_status lx_s2_ = from_hip((call), (where));  \
+        if (lx_s2_ != LAPLEX_OK) return bail(lx_s2_);            \
+    } while (0)
+
+    LX_PLAN_TRY(hipGetDevice(&p->device), "hipGetDevice");
+    {
+        int lds = 0;
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, p->device) != hipSuccess) lds = 65536;
+        if (lds > 160 * 1024) lds = 160 * 1024;
+        p->lds_bytes = lds - 1024;
+    }
+    LX_PLAN_TRY(plan_alloc(p, (void**)&flag, 256, s), "alloc flag");
+    LX_PLAN_TRY(lx::fill_u32(flag, 0u, 1, s), "clear flag");
+    LX_PLAN_TRY(plan_alloc(p, (void**)&p->sa, (size_t)n * 4, s), "alloc sorted a");
+    LX_PLAN_TRY(plan_alloc(p, (void**)&p->pa, (size_t)n * 4, s), "alloc perm a");
+    const int64_t big = sym ? n : (n > k ? n : k);
+    LX_PLAN_TRY(dev_alloc(&scratch, lx::sort_scratch_bytes(big), p->device, s), "alloc sort scratch");
+    LX_PLAN_TRY(lx::sort_launch(a, n, p->sa, p->pa, scratch, flag, s), "sort a");
+    if (sym) {
+        p->sb = p->sa;
+        p->pb = p->pa;
+        if (p->phased) {
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->cphi, (size_t)n * 4, s), "alloc phases");
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->sphi, (size_t)n * 4, s), "alloc phases");
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->cpsi, (size_t)n * 4, s), "alloc phases");
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->spsi, (size_t)n * 4, s), "alloc phases");
+            LX_PLAN_TRY(lx::phase_factors_launch(phi, p->pa, n, p->cphi, p->sphi, flag, s), "phi factors");
+            LX_PLAN_TRY(lx::phase_factors_launch(psi, p->pa, n, p->cpsi, p->spsi, flag, s), "psi factors");
+        }
+    } else {
+        LX_PLAN_TRY(plan_alloc(p, (void**)&p->sb, (size_t)k * 4, s), "alloc sorted b");
+        LX_PLAN_TRY(plan_alloc(p, (void**)&p->pb, (size_t)k * 4, s), "alloc perm b");
+        LX_PLAN_TRY(lx::sort_launch(b, k, p->sb, p->pb, scratch, flag, s), "sort b");
+        LX_PLAN_TRY(plan_alloc(p, (void**)&p->a0, (size_t)n * 4, s), "alloc a copy");
+        LX_PLAN_TRY(plan_alloc(p, (void**)&p->b0, (size_t)k * 4, s), "alloc b copy");
+        LX_PLAN_TRY(hipMemcpyAsync(p->a0, a, (size_t)n * 4, hipMemcpyDeviceToDevice, s), "copy a");
+        LX_PLAN_TRY(hipMemcpyAsync(p->b0, b, (size_t)k * 4, hipMemcpyDeviceToDevice, s), "copy b");
+        if (p->phased) {
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->phi0, (size_t)n * 4, s), "alloc phases");
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->psi0, (size_t)k * 4, s), "alloc phases");
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->cphi, (size_t)n * 4, s), "alloc phases");
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->sphi, (size_t)n * 4, s), "alloc phases");
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->cpsi, (size_t)k * 4, s), "alloc phases");
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->spsi, (size_t)k * 4, s), "alloc phases");
+            LX_PLAN_TRY(hipMemcpyAsync(p->phi0, phi, (size_t)n * 4, hipMemcpyDeviceToDevice, s), "copy phi");
+            LX_PLAN_TRY(hipMemcpyAsync(p->psi0, psi, (size_t)k * 4, hipMemcpyDeviceToDevice, s), "copy psi");
+            LX_PLAN_TRY(lx::phase_factors_launch(phi, p->pa, n, p->cphi, p->sphi, flag, s), "phi factors");
+            LX_PLAN_TRY(lx::phase_factors_launch(psi, p->pb, k, p->cpsi, p->spsi, flag, s), "psi factors");
+        }
+    }
+    dev_free(scratch, p->device, s);
+    scratch = nullptr;
+    LX_PLAN_TRY(hipMemcpyAsync(&host_flag, flag, 4, hipMemcpyDeviceToHost, s), "read flag");
+    LX_PLAN_TRY(hipStreamSynchronize(s), "synchronize");
+    if (host_flag & 1u) return bail(fail(LAPLEX_ERR_NONFINITE_ANCHOR, "NaN or Inf among anchors or phases"));
+#undef LX_PLAN_TRY
+    *out = p;
+    return LAPLEX_OK;
+}
+
+laplex_status laplex_plan_destroy(laplex_plan p)
+{
+    if (!p) return LAPLEX_OK;
+    DeviceGuard g(p->device);
+    plan_release(p);
+    return LAPLEX_OK;
+}
+
+laplex_status laplex_plan_perm(laplex_plan p, int side, const uint32_t** perm_dev)
+{
+    if (!p || !perm_dev || (side != 0 && side != 1)) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "bad plan_perm arguments");
+    *perm_dev = side == 0 ? p->pa : p->pb;
+    return LAPLEX_OK;
+}
+
+laplex_status laplex_plan_sorted(laplex_plan p, int side, const float** sorted_dev)
+{
+    if (!p || !sorted_dev || (side != 0 && side != 1))
+        return fail(LAPLEX_ERR_INVALID_ARGUMENT, "bad plan_sorted arguments");
+    *sorted_dev = side == 0 ? p->sa : p->sb;
+    return LAPLEX_OK;
+}
+
+laplex_status laplex_plan_info(laplex_plan p, int64_t* n, int64_t* k, int* flags)
+{
+    if (!p) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (n) *n = p->n;
+    if (k) *k = p->k;
+    if (flags) *flags = (p->sym ? LAPLEX_PLAN_SYMMETRIC : 0) | (p->phased ? LAPLEX_PLAN_PHASED : 0);
+    return LAPLEX_OK;
+}
+
+laplex_status laplex_plan_set_option(laplex_plan p, int option, int64_t value)
+{
+    if (!p) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (option != LAPLEX_OPT_GENERAL_ALGO) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "unknown option");
+    if (value != LAPLEX_ALGO_AUTO && value != LAPLEX_ALGO_BUCKET && value != LAPLEX_ALGO_EVALUATE)
+        return fail(LAPLEX_ERR_INVALID_ARGUMENT, "unknown algorithm");
+    p->algo = (int)value;
+    return LAPLEX_OK;
+}
+
+laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batch, int transpose, void* stream)
+{
+    if (!p) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (!x || !y) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "x or y is NULL");
+    if (batch < 1) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "batch must be >= 1");
+    if (transpose != 0 && transpose != 1) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "transpose must be 0 or 1");
+    const int64_t len_in = transpose ? p->n : p->k;
+    const int64_t len_out = transpose ? p->k : p->n;
+    if (batch > (int64_t)1 << 40 || (double)batch * (double)(len_in > len_out ? len_in : len_out) > 4.0e18 / 4)
+        return fail(LAPLEX_ERR_INVALID_ARGUMENT, "batch too large");
+    if (ranges_overlap(x, (size_t)(batch * len_in) * 4, y, (size_t)(batch * len_out) * 4))
+        return fail(LAPLEX_ERR_INVALID_ARGUMENT, "x and y overlap");
+    DeviceGuard g(p->device);
+    hipStream_t s = (hipStream_t)stream;
+    const int ch = p->phased ? 2 : 1;
+
+    if (p->sym) {
+        const int64_t n = p->n;
+        LX_TRY(ensure_ws(p, scan_ws_bytes(n, batch, ch, true, false, false), s), "workspace");
+        Carve cv(p->ws);
+        lx::ScanArgs A;
+        A.mode = lx::kScanSym;
+        A.channels = ch;
+        A.n = n;
+        A.tiles = (n + lx::kScanTile - 1) / lx::kScanTile;
+        A.batch = batch;
+        A.ld = pad64(n);
+        A.s = p->sa;
+        A.perm = p->pa;
+        A.x = x;
+        A.y = y;
+        A.xs = cv.take<float>((size_t)ch * batch * A.ld);
+        A.agg = cv.take<double>((size_t)ch * batch * A.tiles * 4);
+        A.carry = cv.take<double>((size_t)ch * batch * A.tiles * 2);
+        if (p->phased) {
+            // K = LAPLEX(a, phi; a, psi): inputs carry psi, outputs phi; K^T swaps them
+            A.in_c = transpose ? p->cphi : p->cpsi;
+            A.in_s = transpose ? p->sphi : p->spsi;
+            A.out_c = transpose ? p->cpsi : p->cphi;
+            A.out_s = transpose ? p->spsi : p->sphi;
+        }
+        LX_TRY(lx::scan_launch(A, s), "symmetric apply");
+        return LAPLEX_OK;
+    }
+
+    // General case: side "o" receives the outputs, side "i" holds the inputs.
+    const bool out_is_a = transpose == 0;
+    const int64_t no = out_is_a ? p->n : p->k;
+    const int64_t ni = out_is_a ? p->k : p->n;
+    const float* s_o = out_is_a ? p->sa : p->sb;
+    const uint32_t* p_o = out_is_a ? p->pa : p->pb;
+    const float* s_i = out_is_a ? p->sb : p->sa;
+    const uint32_t* p_i = out_is_a ? p->pb : p->pa;
+    const float* anchor_o = out_is_a ? p->a0 : p->b0;
+    const float* anchor_i = out_is_a ? p->b0 : p->a0;
+    const float* phase_o = out_is_a ? p->phi0 : p->psi0;
+    const float* phase_i = out_is_a ? p->psi0 : p->phi0;
+    const float* c_o = out_is_a ? p->cphi : p->cpsi;
+    const float* sn_o = out_is_a ? p->sphi : p->spsi;
+    const float* c_i = out_is_a ? p->cpsi : p->cphi;
+    const float* sn_i = out_is_a ? p->spsi : p->sphi;
+    int algo = p->algo;
+    if (algo == LAPLEX_ALGO_AUTO) algo = ni <= no ? LAPLEX_ALGO_EVALUATE : LAPLEX_ALGO_BUCKET;
+
+    if (algo == LAPLEX_ALGO_EVALUATE) {
+        LX_TRY(ensure_ws(p, scan_ws_bytes(ni, batch, ch, true, true, false), s), "workspace");
+        Carve cv(p->ws);
+        lx::ScanArgs A;
+        A.mode = lx::kScanPLPR;
+        A.channels = ch;
+        A.n = ni;
+        A.tiles = (ni + lx::kScanTile - 1) / lx::kScanTile;
+        A.batch = batch;
+        A.ld = pad64(ni);
+        A.s = s_i;
+        A.perm = p_i;
+        A.x = x;
+        A.xs = cv.take<float>((size_t)ch * batch * A.ld);
+        A.pl = cv.take<float>((size_t)ch * batch * A.ld);
+        A.pr = cv.take<float>((size_t)ch * batch * A.ld);
+        A.agg = cv.take<double>((size_t)ch * batch * A.tiles * 4);
+        A.carry = cv.take<double>((size_t)ch * batch * A.tiles * 2);
+        if (p->phased) {
+            A.in_c = c_i;
+            A.in_s = sn_i;
+        }
+        LX_TRY(lx::scan_launch(A, s), "scan over the input side");
+        lx::EvalArgs E;
+        E.channels = ch;
+        E.n_out = no;
+        E.n_in = ni;
+        E.batch = batch;
+        E.out_anchor = anchor_o;
+        E.out_phase = p->phased ? phase_o : nullptr;
+        E.s_in = s_i;
+        E.ld = A.ld;
+        E.pl = A.pl;
+        E.pr = A.pr;
+        E.y = y;
+        E.lds_bytes = p->lds_bytes;
+        LX_TRY(lx::eval_launch(E, s), "evaluate outputs");
+        return LAPLEX_OK;
+    }
+
+    // BUCKET: inputs into the intervals of the sorted output side, then scan it.
+    lx::BucketArgs Bk;
+    Bk.channels = ch;
+    Bk.n_out = no;
+    Bk.n_in = ni;
+    Bk.batch = batch;
+    Bk.s_out = s_o;
+    Bk.in_anchor = anchor_i;
+    Bk.in_phase = p->phased ? phase_i : nullptr;
+    Bk.x = x;
+    Bk.ld = pad64(no);
+    Bk.lds_bytes = p->lds_bytes;
+    Bk.partial_floats = lx::bucket_partial_floats(Bk, nullptr, nullptr);
+    const size_t need = scan_ws_bytes(no, batch, ch, false, false, true) + align256((size_t)Bk.partial_floats * 4);
+    LX_TRY(ensure_ws(p, need, s), "workspace");
+    Carve cv(p->ws);
+    lx::ScanArgs A;
+    A.mode = lx::kScanUV;
+    A.channels = ch;
+    A.n = no;
+    A.tiles = (no + lx::kScanTile - 1) / lx::kScanTile;
+    A.batch = batch;
+    A.ld = Bk.ld;
+    A.s = s_o;
+    A.perm = p_o;
+    float* u = cv.take<float>((size_t)ch * batch * A.ld);
+    float* v = cv.take<float>((size_t)ch * batch * A.ld);
+    A.u = u;
+    A.v = v;
+    A.agg = cv.take<double>((size_t)ch * batch * A.tiles * 4);
+    A.carry = cv.take<double>((size_t)ch * batch * A.tiles * 2);
+    A.y = y;
+    if (p->phased) {
+        A.out_c = c_o;
+        A.out_s = sn_o;
+    }
+    Bk.u = u;
+    Bk.v = v;
+    Bk.partial = Bk.partial_floats ? cv.take<float>((size_t)Bk.partial_floats) : nullptr;
+    LX_TRY(lx::bucket_launch(Bk, s), "bucket inputs");
+    LX_TRY(lx::scan_launch(A, s), "scan over the output side");
+    (void)p_i;
+    return LAPLEX_OK;
+}
+
+laplex_status laplex_gram(laplex_plan p, const float* D, float* M, void* stream)
+{
+    if (!p) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (!D || !M) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "D or M is NULL");
+    if (p->phased) return fail(LAPLEX_ERR_UNSUPPORTED, "Gram of a phased operator");
+    if ((double)p->n * (double)p->n > (double)((int64_t)1 << 40))
+        return fail(LAPLEX_ERR_INVALID_ARGUMENT, "n * n too large for a dense Gram matrix");
+    if (ranges_overlap(D, (size_t)p->k * 4, M, (size_t)(p->n * p->n) * 4))
+        return fail(LAPLEX_ERR_INVALID_ARGUMENT, "D and M overlap");
+    DeviceGuard g(p->device);
+    hipStream_t s = (hipStream_t)stream;
+    LX_TRY(ensure_ws(p, lx::gram_scratch_bytes(p->n), s), "workspace");
+    lx::GramArgs G;
+    G.n = p->n;
+    G.k = p->k;
+    G.sa = p->sa;
+    G.pa = p->pa;
+    G.sb = p->sb;
+    G.pb = p->pb;
+    G.D = D;
+    G.stats = (double*)p->ws;
+    G.M = M;
+    LX_TRY(lx::gram_launch(G, s), "gram");
+    return LAPLEX_OK;
+}
+
+laplex_status laplex_profile_enable(int on)
+{
+    g_prof_on = on != 0;
+    return LAPLEX_OK;
+}
+
+laplex_status laplex_profile_reset(void)
+{
+    laplex_profile_collect();
+    g_prof.clear();
+    return LAPLEX_OK;
+}
+
+laplex_status laplex_profile_collect(void)
+{
+    laplex_status st = LAPLEX_OK;
+    for (const Pending& q : g_pending) {
+        float ms = 0.f;
+        if (hipEventSynchronize(q.b) == hipSuccess && hipEventElapsedTime(&ms, q.a, q.b) == hipSuccess) {
+            bool found = false;
+            for (ProfEntry& e : g_prof)
+                if (std::strcmp(e.name, q.name) == 0) {
+                    e.launches += 1;
+                    e.total_ms += ms;
+                    found = true;
+                    break;
+                }
+            if (!found) g_prof.push_back(ProfEntry{q.name, 1, (double)ms});
+        } else {
+            (void)hipGetLastError();
+            st = fail(LAPLEX_ERR_DEVICE, "profiling event failed");
+        }
+        g_event_pool.push_back(q.a);
+        g_event_pool.push_back(q.b);
+    }
+    g_pending.clear();
+    return st;
+}
+
+laplex_status laplex_profile_entry(int i, const char** name, int64_t* launches, double* total_ms)
+{
+    if (i < 0 || i >= (int)g_prof.size()) return LAPLEX_ERR_INVALID_ARGUMENT;
+    if (name) *name = g_prof[i].name;
+    if (launches) *launches = g_prof[i].launches;
+    if (total_ms) *total_ms = g_prof[i].total_ms;
+    return LAPLEX_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,325 @@
+// General case a != b (gfx950).
+//
+// Technical summary of "LAPLEX: The FFT of Learnable Laplace Kernels", §2.2:
+// the contributions of one anchor set are collected into the intervals of
+// the other, sorted, set (vectors u and v) and then propagated with the
+// symmetric scan.  With outputs on sorted anchors s and an input at anchor q
+// with value x, and t = #{r : s_r < q} (so q lies in (s_{t-1}, s_t]):
+//     u_t     += exp(-(s_t - q)) x      reaches every rank >= t via L,
+//     v_{t-1} += exp(-(q - s_{t-1})) x  reaches every rank <= t-1 via R,
+// so each output receives the input exactly once, including ties q = s_r.
+//
+// Kernels here:
+//   lx_bucket_lds    + lx_bucket_reduce : u, v when the sorted output side
+//                      fits in LDS (one private bin set per workgroup,
+//                      per-workgroup partials summed in a fixed order);
+//   lx_bucket_global : u, v with device-wide float atomics, any size;
+//   lx_eval          : the transposed reading of the same identity: with
+//                      the scan run over the sorted INPUT side (PL = prefix,
+//                      PR = suffix, both inclusive), an output at anchor o
+//                      with t = #{s_j < o} is
+//                        exp(-(o - s_{t-1})) PL_{t-1} + exp(-(s_t - o)) PR_t,
+//                      evaluated for every output in its original order (no
+//                      sort or scatter of the output side).
+// The cos/sin split of a phased operator (cos(p - q) = cos p cos q +
+// sin p sin q) gives two channels: inputs scaled by cos q_j and sin q_j,
+// outputs combined with cos p_i and sin p_i.
+#include "lx_device.h"
+#include "lx_internal.h"
+
+namespace lx {
+
+constexpr int kGenThreads = 1024;
+
+// #{r : s[r] < q} by bisection.
+__device__ __forceinline__ int64_t lower_bound_f(const float* __restrict__ s, int64_t n, float q)
+{
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (s[mid] < q) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ float decay_f(float lo, float hi) { return expf(lo - hi); }
+
+__device__ __forceinline__ void phase_cs(const float* __restrict__ ph, int64_t j, float& c, float& s)
+{
+    double sd, cd;
+    sincos((double)ph[j], &sd, &cd);
+    c = (float)cd;
+    s = (float)sd;
+}
+
+__host__ __device__ inline int64_t pad64(int64_t x) { return (x + 63) & ~(int64_t)63; }
+
+// ------------------------------------------------------------- bucketing
+
+template <int C>
+__global__ __launch_bounds__(kGenThreads) void lx_bucket_lds(BucketArgs A, int VG, int groups,
+                                                            int64_t chunk_len)
+{
+    extern __shared__ float lds[];
+    const int64_t no = A.n_out;
+    float* so = lds;
+    float* bins = lds + pad64(no);  // [VG][C][2][no]
+    const int g = (int)(blockIdx.x % groups);
+    const int64_t chunk = blockIdx.x / groups;
+    const int64_t v0 = (int64_t)g * VG;
+    const int nv = (int)((A.batch - v0) < VG ? (A.batch - v0) : VG);
+
+    for (int64_t i = threadIdx.x; i < no; i += kGenThreads) so[i] = A.s_out[i];
+    for (int64_t i = threadIdx.x; i < (int64_t)VG * C * 2 * no; i += kGenThreads) bins[i] = 0.f;
+    __syncthreads();
+
+    const int64_t j0 = chunk * chunk_len;
+    int64_t j1 = j0 + chunk_len;
+    if (j1 > A.n_in) j1 = A.n_in;
+    for (int64_t j = j0 + threadIdx.x; j < j1; j += kGenThreads) {
+        const float q = A.in_anchor[j];
+        const int64_t t = lower_bound_f(so, no, q);
+        const float al = t < no ? decay_f(q, so[t]) : 0.f;
+        const float be = t > 0 ? decay_f(so[t - 1], q) : 0.f;
+        float f[C];
+        if (C == 2) phase_cs(A.in_phase, j, f[0], f[C - 1]);
+        else f[0] = 1.f;
+        for (int vi = 0; vi < nv; ++vi) {
+            const float xv = A.x[(v0 + vi) * A.n_in + j];
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const float val = f[c] * xv;
+                float* b = bins + ((int64_t)(vi * C + c) * 2) * no;
+                if (t < no) atomicAdd(b + t, al * val);
+                if (t > 0) atomicAdd(b + no + (t - 1), be * val);
+            }
+        }
+    }
+    __syncthreads();
+    // partial layout [chunk][batch][C][2][no]
+    for (int64_t i = threadIdx.x; i < (int64_t)nv * C * 2 * no; i += kGenThreads) {
+        const int64_t vi = i / (C * 2 * no);
+        const int64_t rest = i - vi * (C * 2 * no);
+        A.partial[((chunk * A.batch + v0 + vi) * C * 2) * no + rest] = bins[i];
+    }
+}
+
+__global__ __launch_bounds__(256) void lx_bucket_reduce(const float* __restrict__ partial, int64_t chunks,
+                                                       int64_t batch, int C, int64_t no, int64_t ld,
+                                                       float* __restrict__ u, float* __restrict__ v)
+{
+    const int64_t total = batch * C * 2 * no;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        double acc = 0.0;
+        for (int64_t ch = 0; ch < chunks; ++ch) acc += (double)partial[ch * total + i];
+        const int64_t t = i % no;
+        int64_t rest = i / no;
+        const int w = (int)(rest % 2);
+        rest /= 2;
+        const int64_t c = rest % C;
+        const int64_t vv = rest / C;
+        (w == 0 ? u : v)[(c * batch + vv) * ld + t] = (float)acc;
+    }
+}
+
+template <int C>
+__global__ __launch_bounds__(256) void lx_bucket_global(BucketArgs A)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t no = A.n_out;
+    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < A.n_in; j += stride) {
+        const float q = A.in_anchor[j];
+        const int64_t t = lower_bound_f(A.s_out, no, q);
+        const float al = t < no ? decay_f(q, A.s_out[t]) : 0.f;
+        const float be = t > 0 ? decay_f(A.s_out[t - 1], q) : 0.f;
+        float f[C];
+        if (C == 2) phase_cs(A.in_phase, j, f[0], f[C - 1]);
+        else f[0] = 1.f;
+        for (int64_t vv = 0; vv < A.batch; ++vv) {
+            const float xv = A.x[vv * A.n_in + j];
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const float val = f[c] * xv;
+                const int64_t row = ((int64_t)c * A.batch + vv) * A.ld;
+                if (t < no) atomicAdd(A.u + row + t, al * val);
+                if (t > 0) atomicAdd(A.v + row + t - 1, be * val);
+            }
+        }
+    }
+}
+
+static void bucket_shape(const BucketArgs& a, int* vg, int* groups, int* chunks, int64_t* chunk_len)
+{
+    const int64_t lds_floats = a.lds_bytes / 4;
+    const int64_t per_vec = (int64_t)a.channels * 2 * a.n_out;
+    int64_t v = (lds_floats - pad64(a.n_out)) / (per_vec > 0 ? per_vec : 1);
+    if (v > 16) v = 16;
+    if (v > a.batch) v = a.batch;
+    if (a.lds_bytes <= 0 || v < 1) {
+        *vg = 0;
+        *groups = *chunks = 0;
+        *chunk_len = 0;
+        return;
+    }
+    *vg = (int)v;
+    *groups = (int)((a.batch + v - 1) / v);
+    int64_t c = (a.n_in + 16383) / 16384;
+    int64_t cap = (1024 + *groups - 1) / *groups;
+    if (c > cap) c = cap;
+    if (c < 1) c = 1;
+    *chunk_len = (a.n_in + c - 1) / c;
+    if (*chunk_len < 1) *chunk_len = 1;
+    *chunks = (int)((a.n_in + *chunk_len - 1) / *chunk_len);
+    if (*chunks < 1) *chunks = 1;
+}
+
+int64_t bucket_partial_floats(const BucketArgs& a, int* groups, int* chunks)
+{
+    int vg, g, c;
+    int64_t cl;
+    bucket_shape(a, &vg, &g, &c, &cl);
+    if (groups) *groups = g;
+    if (chunks) *chunks = c;
+    if (vg == 0) return 0;
+    return (int64_t)c * a.batch * a.channels * 2 * a.n_out;
+}
+
+hipError_t bucket_launch(BucketArgs& a, hipStream_t s)
+{
+    if (a.n_out <= 0 || a.batch <= 0) return hipSuccess;
+    int vg, groups, chunks;
+    int64_t chunk_len;
+    bucket_shape(a, &vg, &groups, &chunks, &chunk_len);
+    const bool two = a.channels == 2;
+    if (vg > 0 && a.partial && a.n_in > 0) {
+        const size_t shmem = (size_t)(pad64(a.n_out) + (int64_t)vg * a.channels * 2 * a.n_out) * 4;
+        const unsigned blocks = (unsigned)((int64_t)chunks * groups);
+        if (two) {
+            (void)hipFuncSetAttribute((const void*)lx_bucket_lds<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+            LX_LAUNCH("bucket_lds", s, (lx_bucket_lds<2><<<blocks, kGenThreads, shmem, s>>>(a, vg, groups, chunk_len)));
+        } else {
+            (void)hipFuncSetAttribute((const void*)lx_bucket_lds<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+            LX_LAUNCH("bucket_lds", s, (lx_bucket_lds<1><<<blocks, kGenThreads, shmem, s>>>(a, vg, groups, chunk_len)));
+        }
+        const int64_t total = a.batch * a.channels * 2 * a.n_out;
+        int64_t rb = (total + 255) / 256;
+        if (rb > 8192) rb = 8192;
+        LX_LAUNCH("bucket_reduce", s,
+                  (lx_bucket_reduce<<<(unsigned)rb, 256, 0, s>>>(a.partial, chunks, a.batch, a.channels,
+                                                                 a.n_out, a.ld, a.u, a.v)));
+        return hipSuccess;
+    }
+    // global path: clear u and v, then accumulate with device atomics
+    const int64_t words = (int64_t)a.channels * a.batch * a.ld;
+    hipError_t e = fill_u32((uint32_t*)a.u, 0u, words, s);
+    if (e != hipSuccess) return e;
+    e = fill_u32((uint32_t*)a.v, 0u, words, s);
+    if (e != hipSuccess) return e;
+    if (a.n_in <= 0) return hipSuccess;
+    int64_t blocks = (a.n_in + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (two) LX_LAUNCH("bucket_global", s, (lx_bucket_global<2><<<(unsigned)blocks, 256, 0, s>>>(a)));
+    else LX_LAUNCH("bucket_global", s, (lx_bucket_global<1><<<(unsigned)blocks, 256, 0, s>>>(a)));
+    return hipSuccess;
+}
+
+// ------------------------------------------------------------- evaluation
+
+template <int C, bool USE_LDS>
+__global__ __launch_bounds__(kGenThreads) void lx_eval(EvalArgs A, int VG, int groups, int64_t chunk_len)
+{
+    extern __shared__ float lds[];
+    const int64_t ni = A.n_in;
+    const int g = (int)(blockIdx.x % groups);
+    const int64_t chunk = blockIdx.x / groups;
+    const int64_t v0 = (int64_t)g * VG;
+    const int nv = (int)((A.batch - v0) < VG ? (A.batch - v0) : VG);
+    const float* si = A.s_in;
+    float* tl = nullptr;  // [ni][VG][C]
+    float* tr = nullptr;
+    if (USE_LDS) {
+        float* s_l = lds;
+        tl = lds + pad64(ni);
+        tr = tl + ni * VG * C;
+        for (int64_t i = threadIdx.x; i < ni; i += kGenThreads) s_l[i] = A.s_in[i];
+        for (int64_t i = threadIdx.x; i < ni * VG * C; i += kGenThreads) {
+            const int64_t t = i / (VG * C);
+            const int64_t rem = i - t * (VG * C);
+            const int64_t vi = rem / C;
+            const int64_t c = rem - vi * C;
+            const int64_t src = (c * A.batch + v0 + vi) * A.ld + t;
+            tl[i] = vi < nv ? A.pl[src] : 0.f;
+            tr[i] = vi < nv ? A.pr[src] : 0.f;
+        }
+        __syncthreads();
+        si = s_l;
+    }
+    const int64_t i0 = chunk * chunk_len;
+    int64_t i1 = i0 + chunk_len;
+    if (i1 > A.n_out) i1 = A.n_out;
+    for (int64_t i = i0 + threadIdx.x; i < i1; i += kGenThreads) {
+        const float o = A.out_anchor[i];
+        const int64_t t = lower_bound_f(si, ni, o);
+        const float al = t > 0 ? decay_f(si[t - 1], o) : 0.f;
+        const float be = t < ni ? decay_f(o, si[t]) : 0.f;
+        float gc[C];
+        if (C == 2) phase_cs(A.out_phase, i, gc[0], gc[C - 1]);
+        else gc[0] = 1.f;
+        for (int vi = 0; vi < nv; ++vi) {
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                float lv = 0.f, rv = 0.f;
+                if (USE_LDS) {
+                    if (t > 0) lv = tl[((t - 1) * VG + vi) * C + c];
+                    if (t < ni) rv = tr[(t * VG + vi) * C + c];
+                } else {
+                    const int64_t row = ((int64_t)c * A.batch + v0 + vi) * A.ld;
+                    if (t > 0) lv = A.pl[row + t - 1];
+                    if (t < ni) rv = A.pr[row + t];
+                }
+                acc = fmaf(gc[c], fmaf(al, lv, be * rv), acc);
+            }
+            A.y[(v0 + vi) * A.n_out + i] = acc;
+        }
+    }
+}
+
+hipError_t eval_launch(const EvalArgs& a, hipStream_t s)
+{
+    if (a.n_out <= 0 || a.batch <= 0) return hipSuccess;
+    const int64_t lds_floats = a.lds_bytes / 4;
+    int64_t vg = (lds_floats - pad64(a.n_in)) / (2 * (int64_t)a.channels * (a.n_in > 0 ? a.n_in : 1));
+    if (vg > 16) vg = 16;
+    if (vg > a.batch) vg = a.batch;
+    const bool use_lds = a.lds_bytes > 0 && vg >= 1;
+    if (!use_lds) vg = a.batch < 16 ? a.batch : 16;
+    const int groups = (int)((a.batch + vg - 1) / vg);
+    int64_t chunks = (a.n_out + 16383) / 16384;
+    const int64_t cap = (2048 + groups - 1) / groups;
+    if (chunks > cap) chunks = cap;
+    if (chunks < 1) chunks = 1;
+    const int64_t chunk_len = (a.n_out + chunks - 1) / chunks;
+    chunks = (a.n_out + chunk_len - 1) / chunk_len;
+    const unsigned blocks = (unsigned)(chunks * groups);
+    const size_t shmem = use_lds ? (size_t)(pad64(a.n_in) + 2 * vg * a.channels * a.n_in) * 4 : 0;
+    const int v = (int)vg;
+#define LX_EVAL(CC, LL)                                                                                  \
+    do {                                                                                                 \
+        if (LL) (void)hipFuncSetAttribute((const void*)lx_eval<CC, LL>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem); \
+        LX_LAUNCH("eval", s, (lx_eval<CC, LL><<<blocks, kGenThreads, shmem, s>>>(a, v, groups, chunk_len))); \
+    } while (0)
+    if (a.channels == 2) {
+        if (use_lds) LX_EVAL(2, true);
+        else LX_EVAL(2, false);
+    } else {
+        if (use_lds) LX_EVAL(1, true);
+        else LX_EVAL(1, false);
+    }
+#undef LX_EVAL
+    return hipSuccess;
+}
+
+}  // namespace lx

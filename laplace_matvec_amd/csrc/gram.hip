@@ -1,0 +1,180 @@
+// Weighted Gram matrix M = A diag(D) A^T, A = K(a, b) (n x k), gfx950.
+//
+// Technical summary of "LAPLEX: The FFT of Learnable Laplace Kernels", §2.2
+// (Gram operators): the sorted order gives M exactly in O(n^2 + k log n)
+// instead of O(n^2 k).  With sorted row anchors s_0 <= ... <= s_{n-1} and
+// ranks r <= c, split the sum over b by position:
+//   b <= s_r       : D e^{-(s_r-b)} e^{-(s_c-b)} = e^{-(s_c-s_r)} D e^{-2(s_r-b)}
+//   s_r < b <= s_c : D e^{-(b-s_r)} e^{-(s_c-b)} = e^{-(s_c-s_r)} D
+//   b > s_c        : D e^{-(b-s_r)} e^{-(b-s_c)} = e^{-(s_c-s_r)} D e^{-2(b-s_c)}
+// so M_rc = e^{-(s_c - s_r)} (P_r + (S_c - S_r) + Q_c) with
+//   S_r = sum of D over b <= s_r,
+//   P_r = sum over b <= s_r of D e^{-2(s_r - b)},
+//   Q_c = sum over b >  s_c of D e^{-2(b - s_c)}.
+// These are prefix sums of exp(+-2b) D rescaled to the interval end points,
+// so nothing overflows for large |b|; S is kept in float64 because S_c - S_r
+// cancels.  Per interval r (b in (s_{r-1}, s_r], r = 0..n) the kernels sum
+//   sigma_r = sum D,  p_r = sum D e^{-2(s_r - b)},  q_{r-1} = sum D e^{-2(b - s_{r-1})}
+// and then run P_r = e^{-2(s_r - s_{r-1})} P_{r-1} + p_r (forward),
+// Q_r = e^{-2(s_{r+1} - s_r)} Q_{r+1} + q_r (backward), S by a prefix sum.
+// Equal anchors get equal (S, P, Q), so the order among ties is irrelevant.
+//
+//   lx_gram_bins : one workgroup per interval; its b-range in the sorted b
+//                  by bisection (k log n in total), fixed-order reduction.
+//   lx_gram_scan : one workgroup, the three scans, stats in original order.
+//   lx_gram_tile : 64 x 64 tiles of M in the original order, O(1) per entry.
+#include "lx_device.h"
+#include "lx_internal.h"
+
+namespace lx {
+
+constexpr int kBinThreads = 256;
+constexpr int kGramScanThreads = 1024;
+constexpr int kGT = 64;  // tile edge
+
+// #{j : s[j] <= q}
+__device__ __forceinline__ int64_t upper_bound_f(const float* __restrict__ s, int64_t n, float q)
+{
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (s[mid] <= q) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ double block_sum_d(double x, double* sh)
+{
+    const int lane = lane_id();
+    const int w = (int)threadIdx.x / kWave;
+#pragma unroll
+    for (int d = kWave / 2; d > 0; d >>= 1) x += __shfl_down(x, d);
+    if (lane == 0) sh[w] = x;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < kBinThreads / kWave; ++i) t += sh[i];
+    __syncthreads();
+    return t;
+}
+
+__global__ __launch_bounds__(kBinThreads) void lx_gram_bins(GramArgs A, double* __restrict__ sigma,
+                                                           double* __restrict__ p, double* __restrict__ q)
+{
+    __shared__ double sh[kBinThreads / kWave];
+    const int64_t n = A.n, k = A.k;
+    const int64_t r = blockIdx.x;  // interval (s_{r-1}, s_r], r = 0..n
+    const int64_t lo = r == 0 ? 0 : upper_bound_f(A.sb, k, A.sa[r - 1]);
+    const int64_t hi = r == n ? k : upper_bound_f(A.sb, k, A.sa[r]);
+    const double right = r < n ? (double)A.sa[r] : 0.0;
+    const double left = r > 0 ? (double)A.sa[r - 1] : 0.0;
+    double sg = 0.0, pp = 0.0, qq = 0.0;
+    for (int64_t j = lo + threadIdx.x; j < hi; j += kBinThreads) {
+        const double d = (double)A.D[A.pb[j]];
+        const double b = (double)A.sb[j];
+        sg += d;
+        if (r < n) pp += d * exp(-2.0 * (right - b));
+        if (r > 0) qq += d * exp(-2.0 * (b - left));
+    }
+    sg = block_sum_d(sg, sh);
+    pp = block_sum_d(pp, sh);
+    qq = block_sum_d(qq, sh);
+    if (threadIdx.x == 0) {
+        sigma[r] = sg;
+        if (r < n) p[r] = pp;
+        if (r > 0) q[r - 1] = qq;
+    }
+}
+
+__global__ __launch_bounds__(kGramScanThreads) void lx_gram_scan(GramArgs A, const double* __restrict__ sigma,
+                                                                const double* __restrict__ p,
+                                                                const double* __restrict__ q,
+                                                                double* __restrict__ st)
+{
+    __shared__ Aff<double> sh[kGramScanThreads / kWave];
+    const int64_t n = A.n;
+    const float* s = A.sa;
+    const int64_t per = (n + kGramScanThreads - 1) / kGramScanThreads;
+    int64_t r0 = (int64_t)threadIdx.x * per;
+    if (r0 > n) r0 = n;
+    int64_t r1 = r0 + per;
+    if (r1 > n) r1 = n;
+
+    // forward: S (multiplier 1) and P (multiplier e^{-2 gap}); rank 0 starts both
+    Aff<double> S = aff_identity<double>(), P = aff_identity<double>();
+    for (int64_t r = r0; r < r1; ++r) {
+        const double m = r > 0 ? exp(-2.0 * ((double)s[r] - (double)s[r - 1])) : 0.0;
+        S = compose(S, Aff<double>{1.0, sigma[r]});
+        P = compose(P, Aff<double>{m, p[r]});
+    }
+    Aff<double> tot;
+    double runS = block_exscan_up<double, kGramScanThreads / kWave>(S, sh, tot).v;
+    double runP = block_exscan_up<double, kGramScanThreads / kWave>(P, sh, tot).v;
+    for (int64_t r = r0; r < r1; ++r) {
+        const double m = r > 0 ? exp(-2.0 * ((double)s[r] - (double)s[r - 1])) : 0.0;
+        runS += sigma[r];
+        runP = m * runP + p[r];
+        double* o = st + (int64_t)A.pa[r] * 4;
+        o[0] = (double)s[r];
+        o[1] = runP;
+        o[2] = runS;
+    }
+    Aff<double> Q = aff_identity<double>();
+    for (int64_t r = r1 - 1; r >= r0; --r) {
+        const double m = r + 1 < n ? exp(-2.0 * ((double)s[r + 1] - (double)s[r])) : 0.0;
+        Q = compose(Q, Aff<double>{m, q[r]});
+    }
+    double runQ = block_exscan_down<double, kGramScanThreads / kWave>(Q, sh, tot).v;
+    for (int64_t r = r1 - 1; r >= r0; --r) {
+        const double m = r + 1 < n ? exp(-2.0 * ((double)s[r + 1] - (double)s[r])) : 0.0;
+        runQ = m * runQ + q[r];
+        st[(int64_t)A.pa[r] * 4 + 3] = runQ;
+    }
+}
+
+__global__ __launch_bounds__(256) void lx_gram_tile(const double* __restrict__ st, int64_t n,
+                                                   float* __restrict__ M)
+{
+    __shared__ double rs[kGT][4];
+    __shared__ double cs[kGT][4];
+    const int64_t i0 = (int64_t)blockIdx.y * kGT, j0 = (int64_t)blockIdx.x * kGT;
+    for (int t = threadIdx.x; t < kGT * 4; t += 256) {
+        const int e = t / 4, f = t % 4;
+        rs[e][f] = (i0 + e < n) ? st[(i0 + e) * 4 + f] : 0.0;
+        cs[e][f] = (j0 + e < n) ? st[(j0 + e) * 4 + f] : 0.0;
+    }
+    __syncthreads();
+    const int jj = threadIdx.x % kGT;
+    const int64_t j = j0 + jj;
+#pragma unroll 4
+    for (int ii = threadIdx.x / kGT; ii < kGT; ii += 256 / kGT) {
+        const int64_t i = i0 + ii;
+        if (i < n && j < n) {
+            const bool row_first = rs[ii][0] <= cs[jj][0];
+            const double* lo = row_first ? rs[ii] : cs[jj];
+            const double* hi = row_first ? cs[jj] : rs[ii];
+            const double val = exp(lo[0] - hi[0]) * (lo[1] + (hi[2] - lo[2]) + hi[3]);
+            M[i * n + j] = (float)val;
+        }
+    }
+}
+
+size_t gram_scratch_bytes(int64_t n) { return (size_t)((n + 1) + 2 * n + 4 * n + 64) * 8; }
+
+hipError_t gram_launch(const GramArgs& a, hipStream_t s)
+{
+    const int64_t n = a.n;
+    if (n <= 0) return hipSuccess;
+    double* sigma = a.stats;
+    double* p = sigma + (n + 1);
+    double* q = p + n;
+    double* st = q + n;
+    LX_LAUNCH("gram_bins", s, (lx_gram_bins<<<(unsigned)(n + 1), kBinThreads, 0, s>>>(a, sigma, p, q)));
+    LX_LAUNCH("gram_scan", s, (lx_gram_scan<<<1, kGramScanThreads, 0, s>>>(a, sigma, p, q, st)));
+    const unsigned nb = (unsigned)((n + kGT - 1) / kGT);
+    LX_LAUNCH("gram_tile", s, (lx_gram_tile<<<dim3(nb, nb), 256, 0, s>>>(st, n, a.M)));
+    return hipSuccess;
+}
+
+}  // namespace lx

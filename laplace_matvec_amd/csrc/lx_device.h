@@ -1,0 +1,193 @@
+// Device primitives for the LAPLEX kernels (gfx950, wave64).
+//
+// The scans of the operator (technical summary of "LAPLEX: The FFT of
+// Learnable Laplace Kernels", §2.2) are scans of affine maps: the recurrence
+// y_r = x_r + w * y_{r-1} is the map t -> w*t + x, and running two such
+// steps one after the other is again affine.  `Aff` holds (m, v) for
+// t -> m*t + v and `compose(p, q)` is "p, then q".
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lx {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// Order-preserving map of float bits to uint32 (IEEE order, -0.0 < +0.0).
+__device__ __forceinline__ uint32_t key_of(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float float_of_key(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+__device__ __forceinline__ bool finite_bits(float f)
+{
+    return (__float_as_uint(f) & 0x7F800000u) != 0x7F800000u;
+}
+
+// Agent-scope relaxed atomics: look-back state words are read by workgroups
+// on other XCDs, so they must bypass the per-XCD caches.
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Number of lanes below this one whose bit is set in `mask`.
+__device__ __forceinline__ uint32_t count_below(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Lanes of this wave whose 8-bit digit equals ours.
+__device__ __forceinline__ uint64_t match_digit8(uint32_t d)
+{
+    uint64_t peers = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const uint64_t bal = __ballot(bit);
+        peers &= bit ? bal : ~bal;
+    }
+    return peers;
+}
+
+template <class T>
+struct Aff {
+    T m, v;
+};
+
+template <class T>
+__device__ __forceinline__ Aff<T> aff_identity()
+{
+    return Aff<T>{T(1), T(0)};
+}
+
+// p first, then q:  t -> q.m*(p.m*t + p.v) + q.v
+template <class T>
+__device__ __forceinline__ Aff<T> compose(Aff<T> p, Aff<T> q)
+{
+    return Aff<T>{p.m * q.m, q.m * p.v + q.v};
+}
+
+// Inclusive scan over the lanes of a wave in ascending lane order.
+template <class T>
+__device__ __forceinline__ Aff<T> wave_scan_up(Aff<T> x)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const T m = __shfl_up(x.m, d);
+        const T v = __shfl_up(x.v, d);
+        if (lane >= d) x = compose(Aff<T>{m, v}, x);
+    }
+    return x;
+}
+
+// Inclusive scan over the lanes in descending lane order (lane 63 first).
+template <class T>
+__device__ __forceinline__ Aff<T> wave_scan_down(Aff<T> x)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const T m = __shfl_down(x.m, d);
+        const T v = __shfl_down(x.v, d);
+        if (lane + d < kWave) x = compose(Aff<T>{m, v}, x);
+    }
+    return x;
+}
+
+// Block-wide exclusive scans of one Aff per thread, ascending (up) or
+// descending (down) thread order.  `sh` needs NW entries.  Returns the
+// exclusive prefix of this thread; `total` receives the block's composite.
+// Ends with a barrier, so `sh` may be reused right after.
+template <class T, int NW>
+__device__ __forceinline__ Aff<T> block_exscan_up(Aff<T> x, Aff<T>* sh, Aff<T>& total)
+{
+    const int lane = lane_id();
+    const int w = (int)threadIdx.x / kWave;
+    const Aff<T> inc = wave_scan_up(x);
+    Aff<T> ex{__shfl_up(inc.m, 1), __shfl_up(inc.v, 1)};
+    if (lane == 0) ex = aff_identity<T>();
+    if (lane == kWave - 1) sh[w] = inc;
+    __syncthreads();
+    Aff<T> pre = aff_identity<T>();
+    Aff<T> tot = aff_identity<T>();
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        if (i < w) pre = compose(pre, sh[i]);
+        tot = compose(tot, sh[i]);
+    }
+    total = tot;
+    __syncthreads();
+    return compose(pre, ex);
+}
+
+template <class T, int NW>
+__device__ __forceinline__ Aff<T> block_exscan_down(Aff<T> x, Aff<T>* sh, Aff<T>& total)
+{
+    const int lane = lane_id();
+    const int w = (int)threadIdx.x / kWave;
+    const Aff<T> inc = wave_scan_down(x);
+    Aff<T> ex{__shfl_down(inc.m, 1), __shfl_down(inc.v, 1)};
+    if (lane == kWave - 1) ex = aff_identity<T>();
+    if (lane == 0) sh[w] = inc;
+    __syncthreads();
+    Aff<T> pre = aff_identity<T>();
+    Aff<T> tot = aff_identity<T>();
+#pragma unroll
+    for (int i = NW - 1; i >= 0; --i) {
+        if (i > w) pre = compose(pre, sh[i]);
+        tot = compose(tot, sh[i]);
+    }
+    total = tot;
+    __syncthreads();
+    return compose(pre, ex);
+}
+
+// Block-wide exclusive sum of uint32 over NW waves.
+template <int NW>
+__device__ __forceinline__ uint32_t block_exsum_u32(uint32_t x, uint32_t* sh, uint32_t& total)
+{
+    const int lane = lane_id();
+    const int w = (int)threadIdx.x / kWave;
+    uint32_t inc = x;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t y = __shfl_up(inc, d);
+        if (lane >= d) inc += y;
+    }
+    if (lane == kWave - 1) sh[w] = inc;
+    __syncthreads();
+    uint32_t pre = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        if (i < w) pre += sh[i];
+        tot += sh[i];
+    }
+    total = tot;
+    __syncthreads();
+    return pre + inc - x;
+}
+
+// Decay factor exp(-(hi - lo)) between two float32 anchors, in float64.
+// The difference of two float32 values is exact in float64, and float64
+// factors keep long chains of equal gaps (common where many anchors sit on
+// one float32 grid) free of the bias a repeated float32 rounding of
+// exp(-gap) would accumulate.
+__device__ __forceinline__ double decay(float lo, float hi)
+{
+    return exp((double)lo - (double)hi);
+}
+
+}  // namespace lx

@@ -189,3 +189,90 @@ def config_inputs(cfg: int, n: int | None = None, k: int | None = None,
         out["phi"] = uniform(n, cfg, S_PHI, 0.0, TWO_PI)
         out["psi"] = uniform(k if wl.kind == "general" else n, cfg, S_PSI, 0.0, TWO_PI)
     return out
+
+
+# --------------------------------------------------------------- device side
+
+_gen_lib = None
+
+
+def _gen():
+    """liblaplex_inputs.so: the same Philox streams drawn on the GPU."""
+    global _gen_lib
+    if _gen_lib is None:
+        import ctypes
+        import os
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblaplex_inputs.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build the package first")
+        lib = ctypes.CDLL(path)
+        lib.laplex_inputs_generate.restype = ctypes.c_int
+        lib.laplex_inputs_generate.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                               ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int,
+                                               ctypes.c_double, ctypes.c_double, ctypes.c_void_p]
+        _gen_lib = lib
+    return _gen_lib
+
+
+def _device_draw(shape, key0, key1, kind, p, q, device, dtype=None):
+    import ctypes
+    import torch
+    dtype = dtype or torch.float32
+    out = torch.empty(shape, dtype=dtype, device=device)
+    if out.numel():
+        rc = _gen().laplex_inputs_generate(ctypes.c_void_p(out.data_ptr()), out.numel(), 0, key0, key1,
+                                           kind, float(p), float(q),
+                                           ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"device input generator failed ({rc})")
+    return out
+
+
+def device_normal(shape, key0, key1, mean=0.0, scale=1.0, device="cuda"):
+    return _device_draw(shape, key0, key1, 0, mean, scale, device)
+
+
+def device_uniform(shape, key0, key1, lo, hi, device="cuda"):
+    return _device_draw(shape, key0, key1, 1, lo, hi, device)
+
+
+def device_u32(shape, key0, key1, device="cuda"):
+    import torch
+    return _device_draw(shape, key0, key1, 2, 0.0, 0.0, device, dtype=torch.int32)
+
+
+def device_draw(dist, shape, key0, key1, device="cuda"):
+    kind, p, q = dist
+    if kind == "normal":
+        return device_normal(shape, key0, key1, p, q, device)
+    return device_uniform(shape, key0, key1, p, q, device)
+
+
+def device_config_inputs(cfg: int, n: int | None = None, k: int | None = None,
+                         batch: int | None = None, device="cuda", with_w: bool = True) -> dict:
+    """The inputs of :func:`config_inputs`, drawn on the GPU (same streams).
+
+    Duplicate injection (config 2) runs on the host copy of the anchors."""
+    import torch
+    wl = WORKLOADS[cfg]
+    n = wl.n if n is None else n
+    k = wl.k if k is None else k
+    batch = wl.batch if batch is None else batch
+    out = {"a": device_draw(wl.a_dist, (n,), cfg, S_A, device)}
+    if wl.dup_frac:
+        host = inject_duplicates(out["a"].cpu().numpy(), cfg, wl.dup_frac)
+        out["a"] = torch.from_numpy(host).to(device)
+    if wl.kind == "sym":
+        out["x"] = device_normal((batch, n), cfg, S_X, device=device)
+    elif wl.kind == "general":
+        out["b"] = device_draw(wl.b_dist, (k,), cfg, S_B, device)
+        out["x"] = device_normal((batch, k), cfg, S_X, device=device)
+        if with_w:
+            out["w"] = device_normal((batch, n), cfg, S_W, device=device)
+    elif wl.kind == "gram":
+        out["b"] = device_draw(wl.b_dist, (k,), cfg, S_B, device)
+        out["D"] = device_uniform((k,), cfg, S_D, 0.0, 1.0, device)
+    if wl.phased:
+        out["phi"] = device_uniform((n,), cfg, S_PHI, 0.0, TWO_PI, device)
+        out["psi"] = device_uniform((k if wl.kind == "general" else n,), cfg, S_PSI, 0.0, TWO_PI, device)
+    return out
