@@ -40,27 +40,40 @@ def parse():
     p.add_argument("--n", type=int, default=None, help="override n (testing only)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=1 << 25)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a plain 1 GiB device copy (counter calibration)")
     return p.parse_args()
 
 
 # --------------------------------------------------------------- byte model
-# Algorithmic bytes per launch of each kernel, per element of the sorted side
-# (B vectors, C channels).  First and last radix passes move less (the first
-# reads float anchors and makes indices; the last writes floats + indices).
+# Algorithmic bytes per launch of each kernel (what the algorithm must move,
+# not what the counters see), for a sorted side of n anchors, B vectors and
+# C phase channels.  Radix passes: 4 B key in, 4 B key out, 2 B replay record
+# per key, plus a 6 B x 256 table per 8192-key tile.
 
-def model_bytes(kernel: str, n: int, batch: int = 1, launches: int = 1) -> float | None:
-    if kernel == "sort_hist":
-        return 4.0 * n
-    if kernel == "sort_pass":
-        # per pass average: (12 + 16 + 16 + 16) / 4 bytes per key
-        return 15.0 * n
-    if kernel == "scan_reduce_gather":
-        # perm 4 + s 4 + x[perm] 4B + xs 4B
-        return (8.0 + 8.0 * batch) * n
-    if kernel == "scan_apply_scatter":
-        # perm 4 + s 4 + xs 4B + y[perm] 4B
-        return (8.0 + 8.0 * batch) * n
-    return None
+TILE_TABLE = 6.0 * 256 / 8192
+
+
+def model_bytes(kernel: str, n: int, batch: int = 1, channels: int = 1) -> float | None:
+    factors = 8.0 if channels == 2 else 0.0
+    per = {
+        "sort_hist": 4.0,
+        "sort_pass": 10.0 + TILE_TABLE,
+        "replay_forward": 2.0 + TILE_TABLE + 8.0 * batch,
+        "replay_backward": 2.0 + TILE_TABLE + 8.0 * batch,
+        "scan_reduce": 4.0 + factors + 4.0 * batch,
+        "scan_apply": 4.0 + 2 * factors + 8.0 * batch,
+        "scan_reduce_gather": 8.0 + factors + 8.0 * batch,
+        "scan_apply_scatter": 8.0 + 2 * factors + 8.0 * batch,
+    }.get(kernel)
+    return None if per is None else per * n
+
+
+def model_step_bytes(n: int, batch: int) -> float:
+    """Whole symmetric step (plan + apply on the replay path)."""
+    launches = {"sort_hist": 1, "sort_pass": 4, "replay_forward": 4, "scan_reduce": 1,
+                "scan_apply": 1, "replay_backward": 4}
+    return sum(c * model_bytes(k, n, batch) for k, c in launches.items())
 
 
 def counter_traffic(kernel: str, workload: str):
@@ -120,6 +133,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch
+        # give the factor between those counters and bytes moved
+        src = torch.ones(1 << 28, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cfg = int(args.workload[1])
     W = wl.WORKLOADS[cfg]
     n = args.n or W.n
@@ -190,9 +212,10 @@ def main():
     # whole-step model bandwidth (symmetric end to end: 4 + 60 sort + 32 apply bytes/elem at B=1)
     extra = {}
     if W.kind == "sym":
-        model = (64.0 + 16.0 + 16.0 * batch) * n
+        model = model_step_bytes(n, batch)
         extra["model_bytes_per_step"] = model
         extra["model_gbps_end_to_end"] = round(model / (ms / 1e3) / 1e9, 1)
+        extra["model_frac_end_to_end"] = round(model / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
     out = {
         "metric": METRIC if cfg == 5 else f"LAPLEX {W.kind} elements/s ({W.name})",
         "value": elements / (ms / 1e3),

@@ -10,6 +10,7 @@
 // repeated plans and growing workspaces do not pay for fresh allocations.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -155,10 +156,12 @@ struct laplex_plan_s {
     bool sym = true, phased = false;
     int algo = LAPLEX_ALGO_AUTO;
     int lds_bytes = 0;
-    // sorted sides
+    // sorted sides and the replay records of their sorts
     float* sa = nullptr;
-    uint32_t* pa = nullptr;
     float* sb = nullptr;  // general only (symmetric: aliases sa)
+    lx::SortRecords ra, rb;
+    // permutations (rank -> original index), made from the records on demand
+    uint32_t* pa = nullptr;
     uint32_t* pb = nullptr;
     // copies in original order (general only)
     float* a0 = nullptr;
@@ -244,6 +247,8 @@ laplex_status check_device()
     return LAPLEX_OK;
 }
 
+
+
 // Bump allocator over the plan workspace.
 struct Carve {
     char* base;
@@ -258,19 +263,69 @@ struct Carve {
     }
 };
 
-// Workspace of one scan along a side of length len.
-size_t scan_ws_bytes(int64_t len, int64_t batch, int ch, bool keep_xs, bool tables, bool uv)
+// Workspace of one scan along a side of length len: `vecs` single-channel
+// rows [batch][ld], `chrows` rows per channel [ch][batch][ld], and the tile
+// composites and carries.
+size_t scan_ws_bytes(int64_t len, int64_t batch, int ch, int vecs, int chrows)
 {
     const int64_t ld = pad64(len);
     const int64_t tiles = (len + lx::kScanTile - 1) / lx::kScanTile;
+    const int64_t groups = (tiles + lx::kCarryGroup - 1) / lx::kCarryGroup;
     size_t b = 0;
-    const size_t row = align256((size_t)ch * batch * ld * 4);
-    if (keep_xs) b += row;
-    if (tables) b += 2 * row;
-    if (uv) b += 2 * row;
+    b += (size_t)vecs * align256((size_t)batch * ld * 4);
+    b += (size_t)chrows * align256((size_t)ch * batch * ld * 4);
     b += align256((size_t)ch * batch * tiles * 4 * 8);
+    b += align256((size_t)ch * batch * groups * 4 * 8);
     b += align256((size_t)ch * batch * tiles * 2 * 8);
     return b;
+}
+
+void scan_common(lx::ScanArgs& A, Carve& cv, int64_t len, int64_t batch, int ch)
+{
+    A.channels = ch;
+    A.n = len;
+    A.tiles = (len + lx::kScanTile - 1) / lx::kScanTile;
+    A.batch = batch;
+    A.ld = pad64(len);
+    const int64_t groups = (A.tiles + lx::kCarryGroup - 1) / lx::kCarryGroup;
+    A.agg = cv.take<double>((size_t)ch * batch * A.tiles * 4);
+    A.gagg = cv.take<double>((size_t)ch * batch * groups * 4);
+    A.carry = cv.take<double>((size_t)ch * batch * A.tiles * 2);
+}
+
+// Sides at least this long move x into sorted order and y back by replaying
+// the sort (streaming passes); shorter ones gather/scatter through the
+// permutation directly (fewer launches).
+int64_t replay_min()
+{
+    static int64_t v = [] {
+        const char* e = getenv("LAPLEX_REPLAY_MIN");
+        return e ? atoll(e) : (int64_t)1 << 20;
+    }();
+    return v;
+}
+
+// Make the permutation of side 0 (a) or 1 (b) from the sort records.
+hipError_t ensure_perm(laplex_plan p, int side, hipStream_t s)
+{
+    uint32_t** dst = side == 0 ? &p->pa : &p->pb;
+    if (*dst) return hipSuccess;
+    if (side == 1 && p->sym) {
+        hipError_t e = ensure_perm(p, 0, s);
+        p->pb = p->pa;
+        return e;
+    }
+    const lx::SortRecords& R = side == 0 ? p->ra : p->rb;
+    void* perm = nullptr;
+    void* tmp = nullptr;
+    hipError_t e = plan_alloc(p, &perm, (size_t)R.n * 4, s);
+    if (e != hipSuccess) return e;
+    e = dev_alloc(&tmp, (size_t)R.n * 4, p->device, s);
+    if (e != hipSuccess) return e;
+    e = lx::perm_from_records(R, (uint32_t*)perm, (uint32_t*)tmp, s);
+    dev_free(tmp, p->device, s);
+    if (e == hipSuccess) *dst = (uint32_t*)perm;
+    return e;
 }
 
 }  // namespace
@@ -339,13 +394,19 @@ laplex_status laplex_plan_create(laplex_plan* out, const float* a, int64_t n, co
     LX_PLAN_TRY(plan_alloc(p, (void**)&flag, 256, s), "alloc flag");
     LX_PLAN_TRY(lx::fill_u32(flag, 0u, 1, s), "clear flag");
     LX_PLAN_TRY(plan_alloc(p, (void**)&p->sa, (size_t)n * 4, s), "alloc sorted a");
-    LX_PLAN_TRY(plan_alloc(p, (void**)&p->pa, (size_t)n * 4, s), "alloc perm a");
+    {
+        void* rec = nullptr;
+        LX_PLAN_TRY(plan_alloc(p, &rec, lx::sort_record_bytes(n), s), "alloc sort records");
+        p->ra = lx::sort_records_at(rec, n);
+    }
     const int64_t big = sym ? n : (n > k ? n : k);
     LX_PLAN_TRY(dev_alloc(&scratch, lx::sort_scratch_bytes(big), p->device, s), "alloc sort scratch");
-    LX_PLAN_TRY(lx::sort_launch(a, n, p->sa, p->pa, scratch, flag, s), "sort a");
+    LX_PLAN_TRY(lx::sort_launch(a, n, p->sa, p->ra, scratch, flag, s), "sort a");
     if (sym) {
         p->sb = p->sa;
-        p->pb = p->pa;
+        p->rb = p->ra;
+        // short sides gather through the permutation, and phases need it once
+        if (n < replay_min() || p->phased) LX_PLAN_TRY(ensure_perm(p, 0, s), "permutation");
         if (p->phased) {
             LX_PLAN_TRY(plan_alloc(p, (void**)&p->cphi, (size_t)n * 4, s), "alloc phases");
             LX_PLAN_TRY(plan_alloc(p, (void**)&p->sphi, (size_t)n * 4, s), "alloc phases");
@@ -356,8 +417,14 @@ laplex_status laplex_plan_create(laplex_plan* out, const float* a, int64_t n, co
         }
     } else {
         LX_PLAN_TRY(plan_alloc(p, (void**)&p->sb, (size_t)k * 4, s), "alloc sorted b");
-        LX_PLAN_TRY(plan_alloc(p, (void**)&p->pb, (size_t)k * 4, s), "alloc perm b");
-        LX_PLAN_TRY(lx::sort_launch(b, k, p->sb, p->pb, scratch, flag, s), "sort b");
+        {
+            void* rec = nullptr;
+            LX_PLAN_TRY(plan_alloc(p, &rec, lx::sort_record_bytes(k), s), "alloc sort records");
+            p->rb = lx::sort_records_at(rec, k);
+        }
+        LX_PLAN_TRY(lx::sort_launch(b, k, p->sb, p->rb, scratch, flag, s), "sort b");
+        LX_PLAN_TRY(ensure_perm(p, 0, s), "permutation of a");
+        LX_PLAN_TRY(ensure_perm(p, 1, s), "permutation of b");
         LX_PLAN_TRY(plan_alloc(p, (void**)&p->a0, (size_t)n * 4, s), "alloc a copy");
         LX_PLAN_TRY(plan_alloc(p, (void**)&p->b0, (size_t)k * 4, s), "alloc b copy");
         LX_PLAN_TRY(hipMemcpyAsync(p->a0, a, (size_t)n * 4, hipMemcpyDeviceToDevice, s), "copy a");
@@ -396,6 +463,9 @@ laplex_status laplex_plan_destroy(laplex_plan p)
 laplex_status laplex_plan_perm(laplex_plan p, int side, const uint32_t** perm_dev)
 {
     if (!p || !perm_dev || (side != 0 && side != 1)) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "bad plan_perm arguments");
+    DeviceGuard g(p->device);
+    LX_TRY(ensure_perm(p, side, nullptr), "permutation");
+    LX_TRY(hipStreamSynchronize(nullptr), "synchronize");
     *perm_dev = side == 0 ? p->pa : p->pb;
     return LAPLEX_OK;
 }
@@ -445,22 +515,15 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
 
     if (p->sym) {
         const int64_t n = p->n;
-        LX_TRY(ensure_ws(p, scan_ws_bytes(n, batch, ch, true, false, false), s), "workspace");
+        const bool replay = n >= replay_min();
+        if (!replay) LX_TRY(ensure_perm(p, 0, s), "permutation");
+        LX_TRY(ensure_ws(p, scan_ws_bytes(n, batch, ch, replay ? 2 : 1, 0), s), "workspace");
         Carve cv(p->ws);
         lx::ScanArgs A;
         A.mode = lx::kScanSym;
-        A.channels = ch;
-        A.n = n;
-        A.tiles = (n + lx::kScanTile - 1) / lx::kScanTile;
-        A.batch = batch;
-        A.ld = pad64(n);
+        scan_common(A, cv, n, batch, ch);
         A.s = p->sa;
         A.perm = p->pa;
-        A.x = x;
-        A.y = y;
-        A.xs = cv.take<float>((size_t)ch * batch * A.ld);
-        A.agg = cv.take<double>((size_t)ch * batch * A.tiles * 4);
-        A.carry = cv.take<double>((size_t)ch * batch * A.tiles * 2);
         if (p->phased) {
             // K = LAPLEX(a, phi; a, psi): inputs carry psi, outputs phi; K^T swaps them
             A.in_c = transpose ? p->cphi : p->cpsi;
@@ -468,7 +531,31 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
             A.out_c = transpose ? p->cpsi : p->cphi;
             A.out_s = transpose ? p->spsi : p->sphi;
         }
+        if (!replay) {
+            A.random = true;
+            A.x = x;
+            A.y = y;
+            A.xs = cv.take<float>((size_t)batch * A.ld);
+            LX_TRY(lx::scan_launch(A, s), "symmetric apply");
+            return LAPLEX_OK;
+        }
+        // x -> sorted order by replaying the four radix passes, scan in place,
+        // then replay them backwards into y.
+        float* t1 = cv.take<float>((size_t)batch * A.ld);
+        float* t2 = cv.take<float>((size_t)batch * A.ld);
+        const lx::SortRecords& R = p->ra;
+        LX_TRY(lx::replay_launch(R, 0, true, x, n, t1, A.ld, batch, s), "replay");
+        LX_TRY(lx::replay_launch(R, 1, true, t1, A.ld, t2, A.ld, batch, s), "replay");
+        LX_TRY(lx::replay_launch(R, 2, true, t2, A.ld, t1, A.ld, batch, s), "replay");
+        LX_TRY(lx::replay_launch(R, 3, true, t1, A.ld, t2, A.ld, batch, s), "replay");
+        A.random = false;
+        A.xs = t2;
+        A.ys = t2;
         LX_TRY(lx::scan_launch(A, s), "symmetric apply");
+        LX_TRY(lx::replay_launch(R, 3, false, t2, A.ld, t1, A.ld, batch, s), "replay");
+        LX_TRY(lx::replay_launch(R, 2, false, t1, A.ld, t2, A.ld, batch, s), "replay");
+        LX_TRY(lx::replay_launch(R, 1, false, t2, A.ld, t1, A.ld, batch, s), "replay");
+        LX_TRY(lx::replay_launch(R, 0, false, t1, A.ld, y, n, batch, s), "replay");
         return LAPLEX_OK;
     }
 
@@ -492,23 +579,18 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
     if (algo == LAPLEX_ALGO_AUTO) algo = ni <= no ? LAPLEX_ALGO_EVALUATE : LAPLEX_ALGO_BUCKET;
 
     if (algo == LAPLEX_ALGO_EVALUATE) {
-        LX_TRY(ensure_ws(p, scan_ws_bytes(ni, batch, ch, true, true, false), s), "workspace");
+        LX_TRY(ensure_ws(p, scan_ws_bytes(ni, batch, ch, 1, 2), s), "workspace");
         Carve cv(p->ws);
         lx::ScanArgs A;
         A.mode = lx::kScanPLPR;
-        A.channels = ch;
-        A.n = ni;
-        A.tiles = (ni + lx::kScanTile - 1) / lx::kScanTile;
-        A.batch = batch;
-        A.ld = pad64(ni);
+        A.random = true;
+        scan_common(A, cv, ni, batch, ch);
         A.s = s_i;
         A.perm = p_i;
         A.x = x;
-        A.xs = cv.take<float>((size_t)ch * batch * A.ld);
+        A.xs = cv.take<float>((size_t)batch * A.ld);
         A.pl = cv.take<float>((size_t)ch * batch * A.ld);
         A.pr = cv.take<float>((size_t)ch * batch * A.ld);
-        A.agg = cv.take<double>((size_t)ch * batch * A.tiles * 4);
-        A.carry = cv.take<double>((size_t)ch * batch * A.tiles * 2);
         if (p->phased) {
             A.in_c = c_i;
             A.in_s = sn_i;
@@ -544,24 +626,19 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
     Bk.ld = pad64(no);
     Bk.lds_bytes = p->lds_bytes;
     Bk.partial_floats = lx::bucket_partial_floats(Bk, nullptr, nullptr);
-    const size_t need = scan_ws_bytes(no, batch, ch, false, false, true) + align256((size_t)Bk.partial_floats * 4);
+    const size_t need = scan_ws_bytes(no, batch, ch, 0, 2) + align256((size_t)Bk.partial_floats * 4);
     LX_TRY(ensure_ws(p, need, s), "workspace");
     Carve cv(p->ws);
     lx::ScanArgs A;
     A.mode = lx::kScanUV;
-    A.channels = ch;
-    A.n = no;
-    A.tiles = (no + lx::kScanTile - 1) / lx::kScanTile;
-    A.batch = batch;
-    A.ld = Bk.ld;
+    A.random = true;
+    scan_common(A, cv, no, batch, ch);
     A.s = s_o;
     A.perm = p_o;
     float* u = cv.take<float>((size_t)ch * batch * A.ld);
     float* v = cv.take<float>((size_t)ch * batch * A.ld);
     A.u = u;
     A.v = v;
-    A.agg = cv.take<double>((size_t)ch * batch * A.tiles * 4);
-    A.carry = cv.take<double>((size_t)ch * batch * A.tiles * 2);
     A.y = y;
     if (p->phased) {
         A.out_c = c_o;
@@ -587,6 +664,8 @@ laplex_status laplex_gram(laplex_plan p, const float* D, float* M, void* stream)
         return fail(LAPLEX_ERR_INVALID_ARGUMENT, "D and M overlap");
     DeviceGuard g(p->device);
     hipStream_t s = (hipStream_t)stream;
+    LX_TRY(ensure_perm(p, 0, s), "permutation of a");
+    LX_TRY(ensure_perm(p, 1, s), "permutation of b");
     LX_TRY(ensure_ws(p, lx::gram_scratch_bytes(p->n), s), "workspace");
     lx::GramArgs G;
     G.n = p->n;

@@ -48,10 +48,10 @@ __device__ __forceinline__ uint32_t count_below(uint64_t mask)
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Lanes of this wave whose 8-bit digit equals ours.
+// Active lanes of this wave whose 8-bit digit equals ours.
 __device__ __forceinline__ uint64_t match_digit8(uint32_t d)
 {
-    uint64_t peers = ~0ull;
+    uint64_t peers = __ballot(1);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
         const bool bit = (d >> b) & 1u;

@@ -7,7 +7,13 @@
 
 namespace lx {
 
-constexpr int kSortTileSize = 8192;  // keys per onesweep tile
+#ifndef LX_SORT_THREADS
+#define LX_SORT_THREADS 512
+#endif
+#ifndef LX_SORT_ITEMS
+#define LX_SORT_ITEMS 16
+#endif
+constexpr int kSortTileSize = LX_SORT_THREADS * LX_SORT_ITEMS;  // keys per onesweep tile
 constexpr int kScanTile = 4096;      // elements per scan tile
 
 // ---- kernel timing hooks (implemented in api.cpp) ----
@@ -29,12 +35,30 @@ void prof_end(int token, hipStream_t s);
 hipError_t fill_u32(uint32_t* p, uint32_t v, int64_t count, hipStream_t s);
 
 // ---- sort (sort.hip) ----
-// Scratch bytes needed to sort n keys.
-size_t sort_scratch_bytes(int64_t n);
-// Stable argsort of a[0..n): sorted[r] = a[perm[r]].  *flag (device) gets
-// bit 0 set if any anchor is NaN/Inf.  `scratch` holds sort_scratch_bytes(n).
-hipError_t sort_launch(const float* a, int64_t n, float* sorted, uint32_t* perm, void* scratch,
+// Replay records of the four radix passes: for pass k and tile t, slot i of
+// the tile (its keys in digit order) came from tile position rec[k][t*8192+i]
+// and went to global position base[k][t*256+b] + i, b being the bin of slot
+// i (the last b with start[k][t*256+b] <= i).
+struct SortRecords {
+    int64_t n = 0, tiles = 0;
+    uint16_t* rec[4] = {};
+    uint32_t* base[4] = {};
+    uint16_t* start[4] = {};
+};
+size_t sort_scratch_bytes(int64_t n);   // temporary, during the sort
+size_t sort_record_bytes(int64_t n);    // kept by the plan
+SortRecords sort_records_at(void* base, int64_t n);
+// Stable argsort of a[0..n): sorted[r] = a[perm[r]] for the permutation the
+// records describe.  *flag (device) gets bit 0 if any anchor is NaN/Inf.
+hipError_t sort_launch(const float* a, int64_t n, float* sorted, const SortRecords& R, void* scratch,
                        uint32_t* flag, hipStream_t s);
+// One replayed pass: forward moves pass-k input order to pass-k output
+// order, backward the reverse.  Rows of `batch` vectors with strides in_ld,
+// out_ld (elements).
+hipError_t replay_launch(const SortRecords& R, int pass, bool forward, const float* in, int64_t in_ld,
+                         float* out, int64_t out_ld, int64_t batch, hipStream_t s);
+// perm[r] = original index of rank r, by replaying an index ramp; tmp: n words.
+hipError_t perm_from_records(const SortRecords& R, uint32_t* perm, uint32_t* tmp, hipStream_t s);
 
 // ---- phases (sort.hip) ----
 // c[r] = cos(ph[perm[r]]), s[r] = sin(ph[perm[r]]); flag bit 0 if non-finite.
@@ -45,34 +69,38 @@ hipError_t check_finite_launch(const float* v, int64_t n, uint32_t* flag, hipStr
 
 // ---- scans along a sorted side (scan.hip) ----
 enum ScanMode : int {
-    kScanSym = 0,   // value stream x gathered through perm; output L + U - x, scattered
-    kScanUV = 1,    // forward stream u, backward stream v (sorted order); output L + R, scattered
-    kScanPLPR = 2,  // value stream x gathered; outputs L and U kept apart, sorted order
+    kScanSym = 0,   // values x (by rank); output L + U - x
+    kScanUV = 1,    // forward stream u, backward stream v (by rank); output L + R
+    kScanPLPR = 2,  // values x (by rank); outputs L and U kept apart, by rank
 };
 
 struct ScanArgs {
     int mode = kScanSym;
     int channels = 1;          // 1, or 2 for the cos/sin split of a phased operator
+    bool random = false;       // x read through perm and y written through perm (else xs/ys by rank)
     int64_t n = 0;             // length of the sorted side
     int64_t tiles = 0;         // ceil(n / kScanTile)
     int64_t batch = 0;         // vectors
     int64_t ld = 0;            // row stride of the internal [channels][batch][ld] buffers
     const float* s = nullptr;  // sorted anchors [n]
     const uint32_t* perm = nullptr;  // rank -> original index [n]
-    const float* x = nullptr;        // Sym/PLPR: [batch][n], original order
+    const float* x = nullptr;        // random Sym/PLPR: [batch][n], original order
     const float* in_c = nullptr;     // input factors by rank (cos, sin), or null
     const float* in_s = nullptr;
     const float* u = nullptr;        // UV: [channels][batch][ld], by rank
     const float* v = nullptr;
-    float* xs = nullptr;             // Sym/PLPR scratch [channels][batch][ld]
+    float* xs = nullptr;             // Sym/PLPR values by rank [batch][ld] (written when random)
     double* agg = nullptr;           // [channels][batch][tiles][4]: fwd (m, v), bwd (m, v)
+    double* gagg = nullptr;          // [channels][batch][groups][4]: composites of tile groups
     double* carry = nullptr;         // [channels][batch][tiles][2]: fwd, bwd carry-in
     const float* out_c = nullptr;    // output factors by rank, or null
     const float* out_s = nullptr;
-    float* y = nullptr;              // Sym/UV: [batch][n], original order
+    float* y = nullptr;              // random Sym/UV: [batch][n], original order
+    float* ys = nullptr;             // Sym/UV by rank [batch][ld] (may alias xs) when not random
     float* pl = nullptr;             // PLPR: [channels][batch][ld], by rank
     float* pr = nullptr;
 };
+constexpr int kCarryGroup = 4096;    // tiles per carry group
 hipError_t scan_launch(const ScanArgs& a, hipStream_t s);
 
 // ---- general case a != b (general.hip) ----

@@ -10,18 +10,20 @@
 // the values are the interval sums u (forward) and v (backward) and the
 // product is L + R.  The "evaluate" path keeps L and U apart (PL, PR).
 //
-// Three launches (reduce-then-scan; every workgroup runs to completion
-// without waiting on another, and the combine tree is fixed, so results are
-// deterministic):
+// Reduce-then-scan (every workgroup runs to completion without waiting on
+// another, and the combine tree is fixed, so results are deterministic):
 //   lx_scan_reduce : per tile of 4096 ranks and per vector, the composite
-//                    affine map of the tile in both directions.  In the
-//                    gathering modes it also reads x through the permutation
-//                    (x[perm[r]]) and stores the sorted copy xs.
-//   lx_scan_carry  : per vector, an exclusive scan of the tile composites in
-//                    both directions -> the value entering each tile.
+//                    affine map of the tile in both directions.  In random
+//                    mode it reads x through the permutation (x[perm[r]]) and
+//                    stores the copy by rank, xs; otherwise xs was filled by
+//                    replaying the sort.
+//   lx_scan_carry_*: per vector, exclusive scans of the tile composites in
+//                    both directions (two levels) -> the value entering each
+//                    tile.
 //   lx_scan_apply  : per tile and vector, the final recurrences from the
-//                    carries; writes y[perm[r]] (scatter back to the original
-//                    order) or the sorted PL/PR tables.
+//                    carries; writes y by rank (ys, replayed back to the
+//                    original order afterwards), y[perm[r]] in random mode,
+//                    or the PL/PR tables.
 // Arithmetic is float64 (storage stays float32): the decay factors and the
 // recurrence would otherwise accumulate the rounding of exp(-gap), which is
 // the same for every equal gap.  Layout: vectors [batch][n]; channels (the
@@ -93,53 +95,60 @@ __device__ __forceinline__ int64_t row_off(const ScanArgs& A, int c, int64_t vec
     return ((int64_t)c * A.batch + vec) * A.ld;
 }
 
-template <int C, int MODE>
-__global__ __launch_bounds__(kScanThreads) void lx_scan_reduce(ScanArgs A)
+// Values of this thread's ranks for every channel.  Sym/PLPR: one value per
+// rank (x[perm[r]] when random, else xs by rank), times cos/sin of the input
+// phase for a phased operator.  UV: the u (forward) and v (backward) rows.
+template <int C, int MODE, bool RANDOM, bool WRITE_XS>
+__device__ __forceinline__ void load_values(const ScanArgs& A, int64_t vec, int64_t r0,
+                                            float (&fv)[C][kScanItems], float (&bv)[C][kScanItems])
 {
-    __shared__ Aff<double> sh[kScanWaves];
-    const int64_t vec = blockIdx.x / A.tiles;
-    const int64_t tile = blockIdx.x - vec * A.tiles;
     const int64_t n = A.n;
-    const int64_t r0 = tile * kScanTile + (int64_t)threadIdx.x * kScanItems;
-
-    double e[kScanItems + 1];
-    load_decays<kScanItems>(A.s, r0, n, e);
-
-    float fv[C][kScanItems];  // forward values
-    float bv[C][kScanItems];  // backward values (same as forward unless UV)
     if (MODE == kScanUV) {
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             load_run<kScanItems>(A.u + row_off(A, c, vec), r0, n, fv[c]);
             load_run<kScanItems>(A.v + row_off(A, c, vec), r0, n, bv[c]);
         }
-    } else {
+        return;
+    }
+    float g[kScanItems];
+    if (RANDOM) {
         uint32_t idx[kScanItems];
         load_run<kScanItems>(A.perm, r0, n, idx);
         const float* xv = A.x + vec * n;
-        float g[kScanItems];
 #pragma unroll
         for (int i = 0; i < kScanItems; ++i) g[i] = (r0 + i < n) ? xv[idx[i]] : 0.f;
-        if (C == 2) {
-            float fc[kScanItems], fs[kScanItems];
-            load_run<kScanItems>(A.in_c, r0, n, fc);
-            load_run<kScanItems>(A.in_s, r0, n, fs);
-#pragma unroll
-            for (int i = 0; i < kScanItems; ++i) {
-                fv[0][i] = fc[i] * g[i];
-                fv[C - 1][i] = fs[i] * g[i];
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < kScanItems; ++i) fv[0][i] = g[i];
-        }
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-            store_run<kScanItems>(A.xs + row_off(A, c, vec), r0, n, fv[c]);
-#pragma unroll
-            for (int i = 0; i < kScanItems; ++i) bv[c][i] = fv[c][i];
-        }
+        if (WRITE_XS) store_run<kScanItems>(A.xs + vec * A.ld, r0, n, g);
+    } else {
+        load_run<kScanItems>(A.xs + vec * A.ld, r0, n, g);
     }
+    if (C == 2) {
+        float fc[kScanItems], fs[kScanItems];
+        load_run<kScanItems>(A.in_c, r0, n, fc);
+        load_run<kScanItems>(A.in_s, r0, n, fs);
+#pragma unroll
+        for (int i = 0; i < kScanItems; ++i) {
+            fv[0][i] = bv[0][i] = fc[i] * g[i];
+            fv[C - 1][i] = bv[C - 1][i] = fs[i] * g[i];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kScanItems; ++i) fv[0][i] = bv[0][i] = g[i];
+    }
+}
+
+template <int C, int MODE, bool RANDOM>
+__global__ __launch_bounds__(kScanThreads) void lx_scan_reduce(ScanArgs A)
+{
+    __shared__ Aff<double> sh[kScanWaves];
+    const int64_t vec = blockIdx.x / A.tiles;
+    const int64_t tile = blockIdx.x - vec * A.tiles;
+    const int64_t r0 = tile * kScanTile + (int64_t)threadIdx.x * kScanItems;
+
+    double e[kScanItems + 1];
+    load_decays<kScanItems>(A.s, r0, A.n, e);
+    float fv[C][kScanItems], bv[C][kScanItems];
+    load_values<C, MODE, RANDOM, true>(A, vec, r0, fv, bv);
 
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -162,40 +171,80 @@ __global__ __launch_bounds__(kScanThreads) void lx_scan_reduce(ScanArgs A)
     }
 }
 
-constexpr int kCarryThreads = 1024;
+// Carries in two levels: composites of groups of kCarryGroup tiles, then
+// each group rescans its tiles from the fold of the groups before (after) it.
+constexpr int kCarryThreads = 256;
+constexpr int kCarryPer = kCarryGroup / kCarryThreads;  // 16 tiles per thread
 
-__global__ __launch_bounds__(kCarryThreads) void lx_scan_carry(const double* __restrict__ agg,
-                                                              double* __restrict__ carry, int64_t T)
+__global__ __launch_bounds__(kCarryThreads) void lx_scan_carry_groups(const double* __restrict__ agg,
+                                                                     double* __restrict__ gagg, int64_t T,
+                                                                     int64_t G)
 {
     __shared__ Aff<double> sh[kCarryThreads / kWave];
-    const int64_t row = blockIdx.x;
+    const int64_t row = blockIdx.x / G;
+    const int64_t g = blockIdx.x - row * G;
     const double* ag = agg + row * T * 4;
-    double* ca = carry + row * T * 2;
-    const int64_t per = (T + kCarryThreads - 1) / kCarryThreads;
-    int64_t t0 = (int64_t)threadIdx.x * per;
+    int64_t t0 = g * kCarryGroup + (int64_t)threadIdx.x * kCarryPer;
+    int64_t t1 = t0 + kCarryPer;
     if (t0 > T) t0 = T;
-    int64_t t1 = t0 + per;
     if (t1 > T) t1 = T;
-
-    Aff<double> f = aff_identity<double>();
+    Aff<double> f = aff_identity<double>(), b = aff_identity<double>();
     for (int64_t t = t0; t < t1; ++t) f = compose(f, Aff<double>{ag[4 * t], ag[4 * t + 1]});
-    Aff<double> tot;
-    Aff<double> run = block_exscan_up<double, kCarryThreads / kWave>(f, sh, tot);
-    for (int64_t t = t0; t < t1; ++t) {
-        ca[2 * t] = run.v;  // value entering tile t from the left (start value 0)
-        run = compose(run, Aff<double>{ag[4 * t], ag[4 * t + 1]});
-    }
-
-    Aff<double> b = aff_identity<double>();
     for (int64_t t = t1 - 1; t >= t0; --t) b = compose(b, Aff<double>{ag[4 * t + 2], ag[4 * t + 3]});
-    run = block_exscan_down<double, kCarryThreads / kWave>(b, sh, tot);
-    for (int64_t t = t1 - 1; t >= t0; --t) {
-        ca[2 * t + 1] = run.v;  // value entering tile t from the right
-        run = compose(run, Aff<double>{ag[4 * t + 2], ag[4 * t + 3]});
+    Aff<double> ft, bt;
+    (void)block_exscan_up<double, kCarryThreads / kWave>(f, sh, ft);
+    (void)block_exscan_down<double, kCarryThreads / kWave>(b, sh, bt);
+    if (threadIdx.x == 0) {
+        double* o = gagg + (row * G + g) * 4;
+        o[0] = ft.m;
+        o[1] = ft.v;
+        o[2] = bt.m;
+        o[3] = bt.v;
     }
 }
 
-template <int C, int MODE>
+__global__ __launch_bounds__(kCarryThreads) void lx_scan_carry_tiles(const double* __restrict__ agg,
+                                                                    const double* __restrict__ gagg,
+                                                                    double* __restrict__ carry, int64_t T,
+                                                                    int64_t G)
+{
+    __shared__ Aff<double> sh[kCarryThreads / kWave];
+    __shared__ double cin[2];
+    const int64_t row = blockIdx.x / G;
+    const int64_t g = blockIdx.x - row * G;
+    const double* ag = agg + row * T * 4;
+    double* ca = carry + row * T * 2;
+    if (threadIdx.x == 0) {
+        const double* gg = gagg + row * G * 4;
+        double lf = 0.0, lb = 0.0;  // values entering the group from the left / right
+        for (int64_t q = 0; q < g; ++q) lf = gg[4 * q] * lf + gg[4 * q + 1];
+        for (int64_t q = G - 1; q > g; --q) lb = gg[4 * q + 2] * lb + gg[4 * q + 3];
+        cin[0] = lf;
+        cin[1] = lb;
+    }
+    int64_t t0 = g * kCarryGroup + (int64_t)threadIdx.x * kCarryPer;
+    int64_t t1 = t0 + kCarryPer;
+    if (t0 > T) t0 = T;
+    if (t1 > T) t1 = T;
+    Aff<double> f = aff_identity<double>(), b = aff_identity<double>();
+    for (int64_t t = t0; t < t1; ++t) f = compose(f, Aff<double>{ag[4 * t], ag[4 * t + 1]});
+    for (int64_t t = t1 - 1; t >= t0; --t) b = compose(b, Aff<double>{ag[4 * t + 2], ag[4 * t + 3]});
+    Aff<double> tot;
+    const Aff<double> fx = block_exscan_up<double, kCarryThreads / kWave>(f, sh, tot);
+    const Aff<double> bx = block_exscan_down<double, kCarryThreads / kWave>(b, sh, tot);
+    double lv = fx.m * cin[0] + fx.v;
+    for (int64_t t = t0; t < t1; ++t) {
+        ca[2 * t] = lv;  // value entering tile t from the left
+        lv = ag[4 * t] * lv + ag[4 * t + 1];
+    }
+    double rv = bx.m * cin[1] + bx.v;
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+        ca[2 * t + 1] = rv;  // value entering tile t from the right
+        rv = ag[4 * t + 2] * rv + ag[4 * t + 3];
+    }
+}
+
+template <int C, int MODE, bool RANDOM>
 __global__ __launch_bounds__(kScanThreads) void lx_scan_apply(ScanArgs A)
 {
     __shared__ Aff<double> sh[kScanWaves];
@@ -206,6 +255,9 @@ __global__ __launch_bounds__(kScanThreads) void lx_scan_apply(ScanArgs A)
 
     double e[kScanItems + 1];
     load_decays<kScanItems>(A.s, r0, n, e);
+    float fv[C][kScanItems], bv[C][kScanItems];
+    // the reduce step already stored x by rank: read it back
+    load_values<C, MODE, false, false>(A, vec, r0, fv, bv);
 
     float out[kScanItems];
 #pragma unroll
@@ -213,21 +265,12 @@ __global__ __launch_bounds__(kScanThreads) void lx_scan_apply(ScanArgs A)
 
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-        float fv[kScanItems], bv[kScanItems];
-        if (MODE == kScanUV) {
-            load_run<kScanItems>(A.u + row_off(A, c, vec), r0, n, fv);
-            load_run<kScanItems>(A.v + row_off(A, c, vec), r0, n, bv);
-        } else {
-            load_run<kScanItems>(A.xs + row_off(A, c, vec), r0, n, fv);
-#pragma unroll
-            for (int i = 0; i < kScanItems; ++i) bv[i] = fv[i];
-        }
         Aff<double> f = aff_identity<double>();
 #pragma unroll
-        for (int i = 0; i < kScanItems; ++i) f = compose(f, Aff<double>{e[i], (double)fv[i]});
+        for (int i = 0; i < kScanItems; ++i) f = compose(f, Aff<double>{e[i], (double)fv[c][i]});
         Aff<double> b = aff_identity<double>();
 #pragma unroll
-        for (int i = kScanItems - 1; i >= 0; --i) b = compose(b, Aff<double>{e[i + 1], (double)bv[i]});
+        for (int i = kScanItems - 1; i >= 0; --i) b = compose(b, Aff<double>{e[i + 1], (double)bv[c][i]});
         Aff<double> tot;
         const Aff<double> fx = block_exscan_up<double, kScanWaves>(f, sh, tot);
         const Aff<double> bx = block_exscan_down<double, kScanWaves>(b, sh, tot);
@@ -237,14 +280,14 @@ __global__ __launch_bounds__(kScanThreads) void lx_scan_apply(ScanArgs A)
         double Lr[kScanItems];
 #pragma unroll
         for (int i = 0; i < kScanItems; ++i) {
-            L = e[i] * L + (double)fv[i];
+            L = e[i] * L + (double)fv[c][i];
             Lr[i] = L;
         }
         if (MODE == kScanPLPR) {
             float pl[kScanItems], pr[kScanItems];
 #pragma unroll
             for (int i = kScanItems - 1; i >= 0; --i) {
-                U = e[i + 1] * U + (double)bv[i];
+                U = e[i + 1] * U + (double)bv[c][i];
                 pl[i] = (float)Lr[i];
                 pr[i] = (float)U;
             }
@@ -255,32 +298,39 @@ __global__ __launch_bounds__(kScanThreads) void lx_scan_apply(ScanArgs A)
             if (C == 2) load_run<kScanItems>(c == 0 ? A.out_c : A.out_s, r0, n, g);
 #pragma unroll
             for (int i = kScanItems - 1; i >= 0; --i) {
-                U = e[i + 1] * U + (double)bv[i];
-                const double y = (MODE == kScanSym) ? Lr[i] + U - (double)fv[i] : Lr[i] + U;
+                U = e[i + 1] * U + (double)bv[c][i];
+                const double y = (MODE == kScanSym) ? Lr[i] + U - (double)fv[c][i] : Lr[i] + U;
                 out[i] = (C == 2) ? fmaf(g[i], (float)y, out[i]) : (float)y;
             }
         }
     }
     if (MODE != kScanPLPR) {
-        uint32_t idx[kScanItems];
-        load_run<kScanItems>(A.perm, r0, n, idx);
-        float* yv = A.y + vec * n;
+        if (RANDOM) {
+            uint32_t idx[kScanItems];
+            load_run<kScanItems>(A.perm, r0, n, idx);
+            float* yv = A.y + vec * n;
 #pragma unroll
-        for (int i = 0; i < kScanItems; ++i)
-            if (r0 + i < n) yv[idx[i]] = out[i];
+            for (int i = 0; i < kScanItems; ++i)
+                if (r0 + i < n) yv[idx[i]] = out[i];
+        } else {
+            store_run<kScanItems>(A.ys + vec * A.ld, r0, n, out);
+        }
     }
 }
 
-template <int C, int MODE>
+template <int C, int MODE, bool RANDOM>
 static hipError_t scan_launch_t(const ScanArgs& a, hipStream_t s)
 {
     const int64_t blocks = a.tiles * a.batch;
-    LX_LAUNCH(MODE == kScanUV ? "scan_reduce_uv" : "scan_reduce_gather", s,
-              (lx_scan_reduce<C, MODE><<<(unsigned)blocks, kScanThreads, 0, s>>>(a)));
+    LX_LAUNCH(MODE == kScanUV ? "scan_reduce_uv" : (RANDOM ? "scan_reduce_gather" : "scan_reduce"), s,
+              (lx_scan_reduce<C, MODE, RANDOM><<<(unsigned)blocks, kScanThreads, 0, s>>>(a)));
+    const int64_t G = (a.tiles + kCarryGroup - 1) / kCarryGroup;
+    const unsigned cb = (unsigned)(a.channels * a.batch * G);
+    LX_LAUNCH("scan_carry", s, (lx_scan_carry_groups<<<cb, kCarryThreads, 0, s>>>(a.agg, a.gagg, a.tiles, G)));
     LX_LAUNCH("scan_carry", s,
-              (lx_scan_carry<<<(unsigned)(a.channels * a.batch), kCarryThreads, 0, s>>>(a.agg, a.carry, a.tiles)));
-    LX_LAUNCH(MODE == kScanPLPR ? "scan_apply_tables" : "scan_apply_scatter", s,
-              (lx_scan_apply<C, MODE><<<(unsigned)blocks, kScanThreads, 0, s>>>(a)));
+              (lx_scan_carry_tiles<<<cb, kCarryThreads, 0, s>>>(a.agg, a.gagg, a.carry, a.tiles, G)));
+    LX_LAUNCH(MODE == kScanPLPR ? "scan_apply_tables" : (RANDOM ? "scan_apply_scatter" : "scan_apply"), s,
+              (lx_scan_apply<C, MODE, RANDOM><<<(unsigned)blocks, kScanThreads, 0, s>>>(a)));
     return hipSuccess;
 }
 
@@ -289,12 +339,14 @@ hipError_t scan_launch(const ScanArgs& a, hipStream_t s)
     if (a.n <= 0 || a.batch <= 0) return hipSuccess;
     if (a.tiles * a.batch > 0x7FFFFFFFll) return hipErrorInvalidValue;
     const bool two = a.channels == 2;
+#define LX_SCAN(M, R) (two ? scan_launch_t<2, M, R>(a, s) : scan_launch_t<1, M, R>(a, s))
     switch (a.mode) {
-        case kScanSym: return two ? scan_launch_t<2, kScanSym>(a, s) : scan_launch_t<1, kScanSym>(a, s);
-        case kScanUV: return two ? scan_launch_t<2, kScanUV>(a, s) : scan_launch_t<1, kScanUV>(a, s);
-        case kScanPLPR: return two ? scan_launch_t<2, kScanPLPR>(a, s) : scan_launch_t<1, kScanPLPR>(a, s);
+        case kScanSym: return a.random ? LX_SCAN(kScanSym, true) : LX_SCAN(kScanSym, false);
+        case kScanUV: return a.random ? LX_SCAN(kScanUV, true) : LX_SCAN(kScanUV, false);
+        case kScanPLPR: return a.random ? LX_SCAN(kScanPLPR, true) : LX_SCAN(kScanPLPR, false);
         default: return hipErrorInvalidValue;
     }
+#undef LX_SCAN
 }
 
 }  // namespace lx

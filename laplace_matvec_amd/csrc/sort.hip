@@ -14,9 +14,13 @@
 //     ticket, ranks them stably with wave64 ballots, publishes its per-bin
 //     counts, looks back over earlier tiles' published counts (decoupled
 //     look-back) to get its global offsets, reorders the tile in LDS by
-//     digit and writes runs of keys and indices.  The first pass reads the
-//     float anchors directly (keys and the index payload are made on the
-//     fly), the last one writes the sorted floats back in their float form.
+//     digit and writes runs of keys.  The first pass reads the float anchors
+//     directly, the last one writes the sorted floats in their float form.
+//     No index payload travels with the keys: each pass instead records,
+//     per slot, the tile position it came from (16 bits) and, per tile and
+//     bin, where the bin's run starts.  Replaying the records (lx_replay)
+//     moves any array into sorted order or back, and an index ramp replayed
+//     forward is the permutation itself.
 //
 // Look-back state word per (tile, bin): 0 = not yet published;
 // bit31 clear, value c+1 = this tile's own count c; bit31 set = count of
@@ -28,12 +32,22 @@
 
 namespace lx {
 
-constexpr int kSortThreads = 512;
+#ifndef LX_SORT_THREADS
+#define LX_SORT_THREADS 512
+#endif
+#ifndef LX_SORT_ITEMS
+#define LX_SORT_ITEMS 16
+#endif
+constexpr int kSortThreads = LX_SORT_THREADS;
 constexpr int kSortWaves = kSortThreads / kWave;
-constexpr int kSortItems = 16;
+constexpr int kSortItems = LX_SORT_ITEMS;
 constexpr int kSortTile = kSortThreads * kSortItems;  // 8192
 constexpr int kRadix = 256;
 constexpr int kHistThreads = 256;
+#ifndef LX_LOOKBACK
+#define LX_LOOKBACK 8
+#endif
+constexpr int kLookback = LX_LOOKBACK;  // predecessors read per look-back round
 
 static_assert(kSortTile == kSortTileSize, "tile size must match the host planner");
 
@@ -68,7 +82,11 @@ __global__ __launch_bounds__(kHistThreads) void lx_sort_hist(const float* __rest
         atomicAdd(&h[0][k & 0xFF], 1u);
         atomicAdd(&h[1][(k >> 8) & 0xFF], 1u);
         atomicAdd(&h[2][(k >> 16) & 0xFF], 1u);
-        atomicAdd(&h[3][k >> 24], 1u);
+        // The top digit (sign and exponent) takes few values, so many lanes
+        // collide: one add per group of equal lanes.
+        const uint32_t d3 = k >> 24;
+        const uint64_t peers = match_digit8(d3);
+        if (count_below(peers) == 0) atomicAdd(&h[3][d3], (uint32_t)__popcll(peers));
     }
     if (__any(bad) && lane_id() == 0) atomicOr(flag, 1u);
     __syncthreads();
@@ -91,13 +109,12 @@ __global__ __launch_bounds__(kRadix) void lx_sort_scan_hist(const uint32_t* __re
 
 template <bool FIRST, bool LAST>
 __global__ __launch_bounds__(kSortThreads) void lx_sort_pass(
-    const float* __restrict__ a_in, const uint32_t* __restrict__ keys_in,
-    const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
-    float* __restrict__ sorted_out, uint32_t* __restrict__ vals_out,
-    const uint32_t* __restrict__ bin_base, uint32_t* __restrict__ state,
+    const float* __restrict__ a_in, const uint32_t* __restrict__ keys_in, uint32_t* __restrict__ keys_out,
+    float* __restrict__ sorted_out, uint16_t* __restrict__ rec, uint32_t* __restrict__ tab_base,
+    uint16_t* __restrict__ tab_start, const uint32_t* __restrict__ bin_base, uint32_t* __restrict__ state,
     uint32_t* __restrict__ ticket, int shift, int64_t n)
 {
-    __shared__ uint32_t s_hist[kSortWaves][kRadix];  // per-wave counts, then wave offsets
+    __shared__ uint16_t s_hist[kSortWaves][kRadix];  // per-wave counts, then wave offsets (<= tile size)
     __shared__ uint32_t s_start[kRadix];             // tile-local start of each bin
     __shared__ uint32_t s_glob[kRadix];              // global position of each bin's first key
     __shared__ uint32_t s_buf[kSortTile];
@@ -112,23 +129,19 @@ __global__ __launch_bounds__(kSortThreads) void lx_sort_pass(
     for (int i = tid; i < kSortWaves * kRadix; i += kSortThreads) (&s_hist[0][0])[i] = 0;
     __syncthreads();
     const uint32_t tile = s_tile;
-    const int64_t wave0 = (int64_t)tile * kSortTile + (int64_t)w * (kSortItems * kWave);
+    const int64_t tile0 = (int64_t)tile * kSortTile;
+    const int wpos = w * (kSortItems * kWave);  // tile-local position of this wave's first key
 
-    // Keys in wave-striped order: item j of lane l is element wave0 + 64 j + l,
-    // so a wave's items in (j, lane) order are its elements in index order.
-    // Positions past n get the largest key: they rank last, in bin 255.
+    // Keys in wave-striped order: item j of lane l is tile position
+    // wpos + 64 j + l, so a wave's items in (j, lane) order are its keys in
+    // index order.  Positions past n get the largest key: they rank last,
+    // in bin 255, and land past n.
     uint32_t key[kSortItems];
-    uint32_t val[kSortItems];
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
-        const int64_t idx = wave0 + (int64_t)j * kWave + lane;
-        if (idx < n) {
-            key[j] = FIRST ? key_of(a_in[idx]) : keys_in[idx];
-            val[j] = FIRST ? (uint32_t)idx : vals_in[idx];
-        } else {
-            key[j] = 0xFFFFFFFFu;
-            val[j] = 0u;
-        }
+        const int64_t idx = tile0 + wpos + j * kWave + lane;
+        if (idx < n) key[j] = FIRST ? key_of(a_in[idx]) : keys_in[idx];
+        else key[j] = 0xFFFFFFFFu;
     }
 
     // Stable rank inside the wave: peers with the same digit, in lane order,
@@ -141,85 +154,106 @@ __global__ __launch_bounds__(kSortThreads) void lx_sort_pass(
         const uint32_t below = count_below(peers);
         const uint32_t prev = s_hist[w][d];
         pos[j] = prev + below;
-        if (below == 0) s_hist[w][d] = prev + (uint32_t)__popcll(peers);
+        if (below == 0) s_hist[w][d] = (uint16_t)(prev + (uint32_t)__popcll(peers));
     }
     __syncthreads();
 
+    // Per bin: offsets of the waves, the tile's count, published at once so
+    // later tiles can look back past this one.
     uint32_t count = 0;
     if (tid < kRadix) {
-        // counts of earlier waves -> offsets; total -> this tile's bin count
         uint32_t run = 0;
 #pragma unroll
         for (int i = 0; i < kSortWaves; ++i) {
             const uint32_t c = s_hist[i][tid];
-            s_hist[i][tid] = run;
+            s_hist[i][tid] = (uint16_t)run;
             run += c;
         }
         count = run;
-        uint32_t* mine = state + (int64_t)tile * kRadix + tid;
-        uint32_t before = 0;
-        if (tile == 0) {
-            st_agent(mine, 0x80000000u | count);
-        } else {
-            st_agent(mine, count + 1u);
-            int64_t t = (int64_t)tile - 1;
-            while (true) {
-                const uint32_t sv = ld_agent(state + t * kRadix + tid);
-                if (sv == 0u) {
-                    __builtin_amdgcn_s_sleep(1);
-                    continue;
-                }
-                if (sv & 0x80000000u) {
-                    before += sv & 0x7FFFFFFFu;
-                    break;
-                }
-                before += sv - 1u;
-                --t;
-            }
-            st_agent(mine, 0x80000000u | (before + count));
-        }
-        s_glob[tid] = bin_base[tid] + before;
+        st_agent(state + (int64_t)tile * kRadix + tid, tile == 0 ? (0x80000000u | count) : (count + 1u));
     }
     uint32_t tile_total;
     const uint32_t start = block_exsum_u32<kSortWaves>(tid < kRadix ? count : 0u, s_red, tile_total);
     if (tid < kRadix) s_start[tid] = start;
     __syncthreads();
 
-    // Place keys in the tile's digit order.
+    // Place keys in the tile's digit order (slots) while earlier tiles finish.
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
         const uint32_t d = (key[j] >> shift) & 0xFFu;
         pos[j] += s_start[d] + s_hist[w][d];
         s_buf[pos[j]] = key[j];
     }
+
+    // Decoupled look-back, kLookback predecessors per round: sum their own
+    // counts until one has published its inclusive count.
+    if (tid < kRadix) {
+        uint32_t before = 0;
+        if (tile > 0) {
+            int64_t t = (int64_t)tile - 1;
+            while (true) {
+                uint32_t sv[kLookback];
+#pragma unroll
+                for (int k = 0; k < kLookback; ++k)
+                    sv[k] = (t - k >= 0) ? ld_agent(state + (t - k) * kRadix + tid) : 0x80000000u;
+                int k = 0;
+                bool done = false;
+#pragma unroll
+                for (int q = 0; q < kLookback; ++q) {
+                    if (!done && k == q) {
+                        const uint32_t v = sv[q];
+                        if (v == 0u) {
+                            // not published yet: resume here next round
+                        } else if (v & 0x80000000u) {
+                            before += v & 0x7FFFFFFFu;
+                            done = true;
+                        } else {
+                            before += v - 1u;
+                            ++k;
+                        }
+                    }
+                }
+                if (done) break;
+                t -= k;
+                if (k == 0) __builtin_amdgcn_s_sleep(1);
+            }
+            st_agent(state + (int64_t)tile * kRadix + tid, 0x80000000u | (before + count));
+        }
+        const uint32_t base = bin_base[tid] + before;
+        s_glob[tid] = base;
+        // replay table: slot i of bin b goes to global position base_b + i
+        tab_base[(int64_t)tile * kRadix + tid] = base - start;
+        tab_start[(int64_t)tile * kRadix + tid] = (uint16_t)start;
+    }
     __syncthreads();
 
-    // Consecutive LDS slots of one digit go to consecutive global slots.
-    uint32_t dst[kSortItems];
+    // Consecutive slots of one digit go to consecutive global positions.
 #pragma unroll
     for (int q = 0; q < kSortItems; ++q) {
         const uint32_t i = (uint32_t)(q * kSortThreads + tid);
         const uint32_t k = s_buf[i];
         const uint32_t d = (k >> shift) & 0xFFu;
-        dst[q] = s_glob[d] + (i - s_start[d]);
-        if ((int64_t)dst[q] < n) {
-            if (LAST) sorted_out[dst[q]] = float_of_key(k);
-            else keys_out[dst[q]] = k;
+        const uint32_t dst = s_glob[d] + (i - s_start[d]);
+        if ((int64_t)dst < n) {
+            if (LAST) sorted_out[dst] = float_of_key(k);
+            else keys_out[dst] = k;
         }
     }
     __syncthreads();
+    // Replay record: the tile position each slot came from.
 #pragma unroll
-    for (int j = 0; j < kSortItems; ++j) s_buf[pos[j]] = val[j];
+    for (int j = 0; j < kSortItems; ++j) s_buf[pos[j]] = (uint32_t)(wpos + j * kWave + lane);
     __syncthreads();
+    uint32_t* rec2 = reinterpret_cast<uint32_t*>(rec + tile0);
 #pragma unroll
-    for (int q = 0; q < kSortItems; ++q) {
-        const uint32_t i = (uint32_t)(q * kSortThreads + tid);
-        if ((int64_t)dst[q] < n) vals_out[dst[q]] = s_buf[i];
+    for (int q = 0; q < kSortItems / 2; ++q) {
+        const uint32_t i = (uint32_t)(q * kSortThreads + tid);  // pair of slots 2i, 2i+1
+        rec2[i] = s_buf[2 * i] | (s_buf[2 * i + 1] << 16);
     }
 }
 
 // Scratch layout (bytes, each region 256-byte aligned):
-//   keysA, valsA, keysB, valsB : uint32[n] each
+//   keysA, keysB               : uint32[n] each
 //   hist, base                 : uint32[4][256] each
 //   tickets                    : uint32[4] (padded to 64)
 //   state                      : uint32[4][tiles][256]
@@ -229,23 +263,43 @@ size_t sort_scratch_bytes(int64_t n)
 {
     const int64_t tiles = (n + kSortTile - 1) / kSortTile;
     size_t b = 0;
-    b += 4 * align256((size_t)n * 4);
+    b += 2 * align256((size_t)n * 4);
     b += 2 * align256(4 * kRadix * 4);
     b += align256(64 * 4);
     b += align256((size_t)4 * tiles * kRadix * 4);
     return b;
 }
 
-hipError_t sort_launch(const float* a, int64_t n, float* sorted, uint32_t* perm, void* scratch,
+size_t sort_record_bytes(int64_t n)
+{
+    const int64_t tiles = (n + kSortTile - 1) / kSortTile;
+    return 4 * (align256((size_t)tiles * kSortTile * 2) + align256((size_t)tiles * kRadix * 4) +
+                align256((size_t)tiles * kRadix * 2));
+}
+
+SortRecords sort_records_at(void* base, int64_t n)
+{
+    const int64_t tiles = (n + kSortTile - 1) / kSortTile;
+    SortRecords r;
+    r.n = n;
+    r.tiles = tiles;
+    char* p = (char*)base;
+    for (int k = 0; k < 4; ++k) {
+        r.rec[k] = (uint16_t*)p; p += align256((size_t)tiles * kSortTile * 2);
+        r.base[k] = (uint32_t*)p; p += align256((size_t)tiles * kRadix * 4);
+        r.start[k] = (uint16_t*)p; p += align256((size_t)tiles * kRadix * 2);
+    }
+    return r;
+}
+
+hipError_t sort_launch(const float* a, int64_t n, float* sorted, const SortRecords& R, void* scratch,
                        uint32_t* flag, hipStream_t s)
 {
     if (n <= 0) return hipSuccess;
     const int64_t tiles = (n + kSortTile - 1) / kSortTile;
     char* p = (char*)scratch;
     uint32_t* keysA = (uint32_t*)p; p += align256((size_t)n * 4);
-    uint32_t* valsA = (uint32_t*)p; p += align256((size_t)n * 4);
     uint32_t* keysB = (uint32_t*)p; p += align256((size_t)n * 4);
-    uint32_t* valsB = (uint32_t*)p; p += align256((size_t)n * 4);
     uint32_t* hist = (uint32_t*)p; p += align256(4 * kRadix * 4);
     uint32_t* base = (uint32_t*)p; p += align256(4 * kRadix * 4);
     uint32_t* tickets = (uint32_t*)p; p += align256(64 * 4);
@@ -267,20 +321,177 @@ hipError_t sort_launch(const float* a, int64_t n, float* sorted, uint32_t* perm,
     const int64_t st = tiles * kRadix;
     LX_LAUNCH("sort_pass", s,
               (lx_sort_pass<true, false><<<grid, kSortThreads, 0, s>>>(
-                  a, nullptr, nullptr, keysA, nullptr, valsA, base + 0 * kRadix, state + 0 * st,
-                  tickets + 0, 0, n)));
+                  a, nullptr, keysA, nullptr, R.rec[0], R.base[0], R.start[0], base + 0 * kRadix,
+                  state + 0 * st, tickets + 0, 0, n)));
     LX_LAUNCH("sort_pass", s,
               (lx_sort_pass<false, false><<<grid, kSortThreads, 0, s>>>(
-                  nullptr, keysA, valsA, keysB, nullptr, valsB, base + 1 * kRadix, state + 1 * st,
-                  tickets + 1, 8, n)));
+                  nullptr, keysA, keysB, nullptr, R.rec[1], R.base[1], R.start[1], base + 1 * kRadix,
+                  state + 1 * st, tickets + 1, 8, n)));
     LX_LAUNCH("sort_pass", s,
               (lx_sort_pass<false, false><<<grid, kSortThreads, 0, s>>>(
-                  nullptr, keysB, valsB, keysA, nullptr, valsA, base + 2 * kRadix, state + 2 * st,
-                  tickets + 2, 16, n)));
+                  nullptr, keysB, keysA, nullptr, R.rec[2], R.base[2], R.start[2], base + 2 * kRadix,
+                  state + 2 * st, tickets + 2, 16, n)));
     LX_LAUNCH("sort_pass", s,
               (lx_sort_pass<false, true><<<grid, kSortThreads, 0, s>>>(
-                  nullptr, keysA, valsA, nullptr, sorted, perm, base + 3 * kRadix, state + 3 * st,
-                  tickets + 3, 24, n)));
+                  nullptr, keysA, nullptr, sorted, R.rec[3], R.base[3], R.start[3], base + 3 * kRadix,
+                  state + 3 * st, tickets + 3, 24, n)));
+    return hipSuccess;
+}
+
+// -------------------------------------------------------------- replay
+//
+// The four passes above factor the sorting permutation into four tile-local
+// partitions.  Replaying them moves any array into sorted order (forward)
+// or back into original order (backward) with coalesced reads and writes:
+// a workgroup stages one 8192-element tile in LDS and copies slot i of bin
+// b between tile position rec[i] and global position base_b + i.  Slots are
+// dealt to threads in stripes (slot q*512 + tid), so consecutive lanes touch
+// consecutive global positions of a bin's run.  The bin of each slot comes
+// from a prefix maximum over the slots of markers set at each non-empty
+// bin's first slot.
+
+constexpr int kReplayItems = kSortTile / kSortThreads;  // 16
+
+template <typename T, bool FWD, bool IOTA>
+__global__ __launch_bounds__(kSortThreads) void lx_replay(const T* __restrict__ in, int64_t in_ld,
+                                                         T* __restrict__ out, int64_t out_ld,
+                                                         const uint16_t* __restrict__ rec,
+                                                         const uint32_t* __restrict__ tab_base,
+                                                         const uint16_t* __restrict__ tab_start, int64_t n,
+                                                         int64_t batch)
+{
+    __shared__ __align__(16) T buf[kSortTile];
+    uint8_t* sbin = reinterpret_cast<uint8_t*>(buf);  // bin of each slot, used before buf holds data
+    __shared__ uint32_t sbase[kRadix];
+    __shared__ uint32_t sred[kSortWaves];
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int w = tid / kWave;
+    const int64_t tile = blockIdx.x;
+    const int64_t t0 = tile * kSortTile;
+
+    uint32_t src[kReplayItems];
+#pragma unroll
+    for (int q = 0; q < kReplayItems; ++q) src[q] = rec[t0 + q * kSortThreads + tid];
+    constexpr int kVec = kReplayItems / 16;  // uint4 words of slot bins per thread
+    static_assert(kReplayItems % 16 == 0, "slots per thread must be a multiple of 16");
+#pragma unroll
+    for (int k = 0; k < kVec; ++k) reinterpret_cast<uint4*>(sbin)[tid * kVec + k] = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t st = 0, nx = 0;
+    if (tid < kRadix) {
+        sbase[tid] = tab_base[tile * kRadix + tid];
+        st = tab_start[tile * kRadix + tid];
+        nx = tid + 1 < kRadix ? tab_start[tile * kRadix + tid + 1] : (uint32_t)kSortTile;
+    }
+    __syncthreads();
+    if (tid < kRadix && nx > st) sbin[st] = (uint8_t)tid;  // first slot of a non-empty bin
+    __syncthreads();
+    {
+        // inclusive prefix max over slots; thread tid scans its kReplayItems consecutive slots
+        uint32_t word[4 * kVec];
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) {
+            const uint4 raw = reinterpret_cast<const uint4*>(sbin)[tid * kVec + k];
+            word[4 * k] = raw.x;
+            word[4 * k + 1] = raw.y;
+            word[4 * k + 2] = raw.z;
+            word[4 * k + 3] = raw.w;
+        }
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < kReplayItems; ++k) m = max(m, (word[k >> 2] >> (8 * (k & 3))) & 0xFFu);
+        uint32_t inc = m;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const uint32_t o = __shfl_up(inc, d);
+            if (lane >= d) inc = max(inc, o);
+        }
+        if (lane == kWave - 1) sred[w] = inc;
+        uint32_t ex = __shfl_up(inc, 1);
+        if (lane == 0) ex = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kSortWaves; ++i)
+            if (i < w) ex = max(ex, sred[i]);
+        uint32_t run = ex;
+#pragma unroll
+        for (int k = 0; k < kReplayItems; ++k) {
+            const uint32_t sh = 8 * (k & 3);
+            run = max(run, (word[k >> 2] >> sh) & 0xFFu);
+            word[k >> 2] = (word[k >> 2] & ~(0xFFu << sh)) | (run << sh);
+        }
+#pragma unroll
+        for (int k = 0; k < kVec; ++k)
+            reinterpret_cast<uint4*>(sbin)[tid * kVec + k] =
+                make_uint4(word[4 * k], word[4 * k + 1], word[4 * k + 2], word[4 * k + 3]);
+    }
+    __syncthreads();
+    uint32_t dst[kReplayItems];
+#pragma unroll
+    for (int q = 0; q < kReplayItems; ++q) {
+        const uint32_t i = (uint32_t)(q * kSortThreads + tid);
+        dst[q] = sbase[sbin[i]] + i;
+    }
+    __syncthreads();  // the bin map is dead: buf takes over its bytes
+    for (int64_t v = 0; v < batch; ++v) {
+        const T* iv = in + v * in_ld;
+        T* ov = out + v * out_ld;
+        if (FWD) {
+#pragma unroll
+            for (int q = 0; q < kReplayItems; ++q) {
+                const int j = q * kSortThreads + tid;
+                if (IOTA) buf[j] = (T)(t0 + j);
+                else buf[j] = (t0 + j < n) ? iv[t0 + j] : T(0);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < kReplayItems; ++q)
+                if ((int64_t)dst[q] < n) ov[dst[q]] = buf[src[q]];
+        } else {
+#pragma unroll
+            for (int q = 0; q < kReplayItems; ++q)
+                if ((int64_t)dst[q] < n) buf[src[q]] = iv[dst[q]];
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < kReplayItems; ++q) {
+                const int j = q * kSortThreads + tid;
+                if (t0 + j < n) ov[t0 + j] = buf[j];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t replay_launch(const SortRecords& R, int pass, bool forward, const float* in, int64_t in_ld,
+                         float* out, int64_t out_ld, int64_t batch, hipStream_t s)
+{
+    if (R.n <= 0 || batch <= 0) return hipSuccess;
+    const unsigned grid = (unsigned)R.tiles;
+    if (forward)
+        LX_LAUNCH("replay_forward", s,
+                  (lx_replay<float, true, false><<<grid, kSortThreads, 0, s>>>(
+                      in, in_ld, out, out_ld, R.rec[pass], R.base[pass], R.start[pass], R.n, batch)));
+    else
+        LX_LAUNCH("replay_backward", s,
+                  (lx_replay<float, false, false><<<grid, kSortThreads, 0, s>>>(
+                      in, in_ld, out, out_ld, R.rec[pass], R.base[pass], R.start[pass], R.n, batch)));
+    return hipSuccess;
+}
+
+hipError_t perm_from_records(const SortRecords& R, uint32_t* perm, uint32_t* tmp, hipStream_t s)
+{
+    if (R.n <= 0) return hipSuccess;
+    const unsigned grid = (unsigned)R.tiles;
+    // iota -> tmp -> perm -> tmp -> perm: after pass k the array holds, at each
+    // pass-k output position, the original index of the element there.
+    uint32_t* bufs[4] = {tmp, perm, tmp, perm};
+    LX_LAUNCH("perm_replay", s,
+              (lx_replay<uint32_t, true, true><<<grid, kSortThreads, 0, s>>>(
+                  nullptr, 0, bufs[0], 0, R.rec[0], R.base[0], R.start[0], R.n, 1)));
+    for (int k = 1; k < 4; ++k)
+        LX_LAUNCH("perm_replay", s,
+                  (lx_replay<uint32_t, true, false><<<grid, kSortThreads, 0, s>>>(
+                      bufs[k - 1], 0, bufs[k], 0, R.rec[k], R.base[k], R.start[k], R.n, 1)));
     return hipSuccess;
 }
 

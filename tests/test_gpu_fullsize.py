@@ -1,0 +1,143 @@
+"""GPU parity at the benchmark's full sizes, in the launch configuration the
+benchmark times (same entry points, same device-drawn inputs).
+
+Where the oracle cannot finish the whole output in seconds, it computes a
+seeded sample of outputs one by one from the dense definition, and the sort
+is checked through the properties that define a stable ascending sort
+(a permutation whose keys ascend, ties in ascending index) -- properties
+that only the oracle's own permutation satisfies, so the check is bit-exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from laplace_matvec_amd import laplex as lx
+from laplace_matvec_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def flip_keys(a):
+    u = np.asarray(a, dtype=np.float32).view(np.uint32)
+    return np.where(u & np.uint32(0x80000000), ~u, u | np.uint32(0x80000000))
+
+
+def assert_stable_sorted(a, perm):
+    """perm is THE stable ascending argsort of a: a permutation, keys ascending,
+    equal keys in ascending original index."""
+    n = a.size
+    perm = np.asarray(perm, dtype=np.int64)
+    assert perm.size == n
+    seen = np.zeros(n, dtype=bool)
+    seen[perm] = True
+    assert seen.all(), "not a permutation"
+    k = flip_keys(a)[perm]
+    dk = k[1:].astype(np.int64) - k[:-1].astype(np.int64)
+    assert (dk >= 0).all(), "keys not ascending"
+    ties = dk == 0
+    assert (perm[1:][ties] > perm[:-1][ties]).all(), "ties not in index order"
+
+
+def test_stable_sort_property_matches_oracle():
+    """The property check accepts the oracle's permutation and rejects others."""
+    rng = np.random.default_rng(3)
+    a = np.round(rng.standard_normal(20000) * 50).astype(np.float32)
+    p = oracle.argsort(a)
+    assert_stable_sorted(a, p)
+    q = p.copy()
+    i = np.flatnonzero(a[p][1:] == a[p][:-1])[0]
+    q[i], q[i + 1] = q[i + 1], q[i]
+    with pytest.raises(AssertionError):
+        assert_stable_sorted(a, q)
+
+
+def sample(n, m, seed):
+    return np.unique(np.random.default_rng(seed).integers(0, n, m))
+
+
+def test_config2_full_n2p24_batch16(gpu):
+    say("[full] config 2: n=2^24, batch 16, ties")
+    inp = wl.device_config_inputs(2, device=gpu)
+    with lx.laplex_plan_create(inp["a"]) as plan:
+        perm = lx.laplex_plan_perm(plan).cpu().numpy()
+        y = lx.laplex_apply(plan, inp["x"]).cpu().numpy()
+    a = inp["a"].cpu().numpy()
+    x = inp["x"].cpu().numpy()
+    assert np.array_equal(perm, oracle.argsort(a).astype(np.int64))
+    ref = oracle.apply_sweep(a, x)
+    errs = [oracle.rel_l2(y[i], ref[i]) for i in range(x.shape[0])]
+    say(f"  max rel L2 {max(errs):.3e}")
+    assert max(errs) < 1e-5
+
+
+def test_config3_full_general_phased(gpu):
+    say("[full] config 3: n=2^26, k=1024, batch 64, phased, both directions")
+    inp = wl.device_config_inputs(3, device=gpu)
+    with lx.laplex_plan_create(inp["a"], b=inp["b"], phi=inp["phi"], psi=inp["psi"]) as plan:
+        pa = lx.laplex_plan_perm(plan, 0).cpu().numpy()
+        pb = lx.laplex_plan_perm(plan, 1).cpu().numpy()
+        y = lx.laplex_apply(plan, inp["x"])
+        z = lx.laplex_apply(plan, inp["w"], transpose=True).cpu().numpy()
+    h = {k: v.cpu().numpy() for k, v in inp.items() if k != "w"}
+    assert_stable_sorted(h["a"], pa)
+    assert np.array_equal(pb, oracle.argsort(h["b"]).astype(np.int64))
+    rows = sample(h["a"].size, 600, 31)
+    ys = y[:, torch.from_numpy(rows).to(gpu)].cpu().numpy()
+    ref = oracle.apply_dense(h["a"], h["x"], b=h["b"], phi=h["phi"], psi=h["psi"], rows=rows)
+    ey = max(oracle.rel_l2(ys[v], ref[v]) for v in range(ys.shape[0]))
+    del y
+    cols = sample(h["b"].size, 12, 32)
+    ez = 0.0
+    for v in (0, 17, 63):
+        wv = inp["w"][v].cpu().numpy()
+        refz = oracle.apply_dense(h["a"], wv, b=h["b"], phi=h["phi"], psi=h["psi"], transpose=True, rows=cols)
+        ez = max(ez, oracle.rel_l2(z[v][cols], refz))
+    say(f"  sampled rel L2: y {ey:.3e}, z {ez:.3e}")
+    assert ey < 1e-5 and ez < 1e-5
+
+
+def test_config4_full_gram(gpu):
+    say("[full] config 4: Gram n=4096, k=3*2^20")
+    inp = wl.device_config_inputs(4, device=gpu)
+    with lx.laplex_plan_create(inp["a"], b=inp["b"]) as plan:
+        M = lx.laplex_gram(plan, inp["D"]).cpu().numpy()
+    a, b, D = (inp[k].cpu().numpy() for k in ("a", "b", "D"))
+    assert np.array_equal(M, M.T)
+    rows = sample(a.size, 12, 41)
+    cols = sample(a.size, 48, 42)
+    ref = oracle.gram_direct(a, b, D, rows=rows, cols=cols)
+    e = oracle.rel_l2(M[np.ix_(rows, cols)], ref)
+    dg = sample(a.size, 24, 43)
+    refd = np.array([oracle.gram_direct(a, b, D, rows=[i], cols=[i])[0, 0] for i in dg])
+    ed = oracle.rel_l2(M[dg, dg], refd)
+    say(f"  sampled rel Frobenius {e:.3e}, diagonal {ed:.3e}")
+    assert e < 1e-5 and ed < 1e-5
+
+
+@pytest.mark.timeout(900)
+def test_config5_full_n2p30_end_to_end(gpu):
+    say("[full] config 5: n=2^30 symmetric, end to end")
+    inp = wl.device_config_inputs(5, device=gpu)
+    with lx.laplex_plan_create(inp["a"]) as plan:
+        y = lx.laplex_apply(plan, inp["x"])
+        perm = lx.laplex_plan_perm(plan).cpu().numpy()
+    a = inp["a"].cpu().numpy()
+    say("  checking the permutation")
+    assert_stable_sorted(a, perm)
+    del perm
+    x = inp["x"].cpu().numpy().reshape(-1)
+    rows = sample(a.size, 24, 51)
+    ys = y.reshape(-1)[torch.from_numpy(rows).to(gpu)].cpu().numpy()
+    say("  oracle on sampled outputs")
+    ref = oracle.apply_dense(a, x, rows=rows)
+    e = oracle.rel_l2(ys, ref)
+    say(f"  sampled rel L2 {e:.3e}")
+    assert e < 1e-4

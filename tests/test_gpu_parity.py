@@ -101,6 +101,37 @@ def test_symmetric_larger_vs_sweep(gpu):
     assert max_rel(y, oracle.apply_sweep(a, x)) < TOL
 
 
+@pytest.mark.parametrize("n,batch,phased", [(1 << 20, 1, False), (1_500_001, 3, False), (1_234_567, 2, True)])
+def test_symmetric_replay_path(gpu, n, batch, phased):
+    """Sides of 2^20 or more move x into sorted order (and y back) by
+    replaying the radix passes instead of gathering through the permutation."""
+    say(f"[sym replay] n={n} batch={batch} phased={phased}")
+    rng = np.random.default_rng(n)
+    a = anchors_with_ties(n, 300.0, rng)
+    x = rng.standard_normal((batch, n)).astype(np.float32)
+    kw = {}
+    if phased:
+        kw = dict(phi=rng.uniform(0, 6.3, n).astype(np.float32), psi=rng.uniform(0, 6.3, n).astype(np.float32))
+    with lx.laplex_plan_create(dev(a), **{k: dev(v) for k, v in kw.items()}) as plan:
+        y = host(lx.laplex_apply(plan, dev(x)))
+        yt = host(lx.laplex_apply(plan, dev(x), transpose=True)) if phased else None
+        perm = host(lx.laplex_plan_perm(plan))
+    assert np.array_equal(perm, oracle.argsort(a).astype(np.int64))
+    assert max_rel(y, oracle.apply_sweep(a, x, **kw)) < TOL
+    if phased:
+        assert max_rel(yt, oracle.apply_sweep(a, x, transpose=True, **kw)) < TOL
+
+
+def test_replay_zero_temperature_bitwise(gpu):
+    """Replayed permutation moves every value exactly (K = I at zero temperature)."""
+    n = (1 << 21) + 77
+    a = (128.0 * np.random.default_rng(5).permutation(n) - 1.0e8).astype(np.float32)
+    x = np.random.default_rng(6).standard_normal((2, n)).astype(np.float32)
+    with lx.laplex_plan_create(dev(a)) as plan:
+        y = host(lx.laplex_apply(plan, dev(x)))
+    assert np.array_equal(y, x)
+
+
 def test_zero_temperature_identity_bitwise(gpu):
     n = 20000
     a = (128.0 * RNG.permutation(n) - 1.0e6).astype(np.float32)
