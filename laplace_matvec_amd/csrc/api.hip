@@ -173,6 +173,11 @@ struct laplex_plan_s {
     float* sphi = nullptr;
     float* cpsi = nullptr;
     float* spsi = nullptr;
+    // general plans: cos/sin of the phases in original order
+    float* cphi0 = nullptr;
+    float* sphi0 = nullptr;
+    float* cpsi0 = nullptr;
+    float* spsi0 = nullptr;
     // workspace for apply / gram
     void* ws = nullptr;
     size_t ws_bytes = 0;
@@ -440,6 +445,12 @@ laplex_status laplex_plan_create(laplex_plan* out, const float* a, int64_t n, co
             LX_PLAN_TRY(hipMemcpyAsync(p->psi0, psi, (size_t)k * 4, hipMemcpyDeviceToDevice, s), "copy psi");
             LX_PLAN_TRY(lx::phase_factors_launch(phi, p->pa, n, p->cphi, p->sphi, flag, s), "phi factors");
             LX_PLAN_TRY(lx::phase_factors_launch(psi, p->pb, k, p->cpsi, p->spsi, flag, s), "psi factors");
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->cphi0, (size_t)n * 4, s), "alloc phases");
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->sphi0, (size_t)n * 4, s), "alloc phases");
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->cpsi0, (size_t)k * 4, s), "alloc phases");
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->spsi0, (size_t)k * 4, s), "alloc phases");
+            LX_PLAN_TRY(lx::phase_factors_launch(phi, nullptr, n, p->cphi0, p->sphi0, flag, s), "phi factors");
+            LX_PLAN_TRY(lx::phase_factors_launch(psi, nullptr, k, p->cpsi0, p->spsi0, flag, s), "psi factors");
         }
     }
     dev_free(scratch, p->device, s);
@@ -569,8 +580,10 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
     const uint32_t* p_i = out_is_a ? p->pb : p->pa;
     const float* anchor_o = out_is_a ? p->a0 : p->b0;
     const float* anchor_i = out_is_a ? p->b0 : p->a0;
-    const float* phase_o = out_is_a ? p->phi0 : p->psi0;
-    const float* phase_i = out_is_a ? p->psi0 : p->phi0;
+    const float* co0 = out_is_a ? p->cphi0 : p->cpsi0;  // cos/sin of phases, original order
+    const float* so0 = out_is_a ? p->sphi0 : p->spsi0;
+    const float* ci0 = out_is_a ? p->cpsi0 : p->cphi0;
+    const float* si0 = out_is_a ? p->spsi0 : p->sphi0;
     const float* c_o = out_is_a ? p->cphi : p->cpsi;
     const float* sn_o = out_is_a ? p->sphi : p->spsi;
     const float* c_i = out_is_a ? p->cpsi : p->cphi;
@@ -602,7 +615,10 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
         E.n_in = ni;
         E.batch = batch;
         E.out_anchor = anchor_o;
-        E.out_phase = p->phased ? phase_o : nullptr;
+        if (p->phased) {
+            E.out_cos = co0;
+            E.out_sin = so0;
+        }
         E.s_in = s_i;
         E.ld = A.ld;
         E.pl = A.pl;
@@ -621,7 +637,10 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
     Bk.batch = batch;
     Bk.s_out = s_o;
     Bk.in_anchor = anchor_i;
-    Bk.in_phase = p->phased ? phase_i : nullptr;
+    if (p->phased) {
+        Bk.in_cos = ci0;
+        Bk.in_sin = si0;
+    }
     Bk.x = x;
     Bk.ld = pad64(no);
     Bk.lds_bytes = p->lds_bytes;

@@ -10,9 +10,11 @@
 // so each output receives the input exactly once, including ties q = s_r.
 //
 // Kernels here:
-//   lx_bucket_lds    + lx_bucket_reduce : u, v when the sorted output side
-//                      fits in LDS (one private bin set per workgroup,
-//                      per-workgroup partials summed in a fixed order);
+//   lx_bucket_sorted + lx_bucket_reduce : u, v when the sorted output side
+//                      is small (up to 1024 anchors): per workgroup, stable
+//                      counting sort of input sub-chunks by interval and
+//                      register accumulation by an owner thread per anchor;
+//                      per-workgroup partials summed in a fixed order;
 //   lx_bucket_global : u, v with device-wide float atomics, any size;
 //   lx_eval          : the transposed reading of the same identity: with
 //                      the scan run over the sorted INPUT side (PL = prefix,
@@ -45,64 +47,187 @@ __device__ __forceinline__ int64_t lower_bound_f(const float* __restrict__ s, in
 
 __device__ __forceinline__ float decay_f(float lo, float hi) { return expf(lo - hi); }
 
-__device__ __forceinline__ void phase_cs(const float* __restrict__ ph, int64_t j, float& c, float& s)
-{
-    double sd, cd;
-    sincos((double)ph[j], &sd, &cd);
-    c = (float)cd;
-    s = (float)sd;
-}
-
 __host__ __device__ inline int64_t pad64(int64_t x) { return (x + 63) & ~(int64_t)63; }
 
 // ------------------------------------------------------------- bucketing
 
+// Sorted bucketing for a small sorted output side (n_out <= 1024).  A
+// workgroup owns up to 8 vectors and a contiguous chunk of inputs, processed
+// in sub-chunks of 2048: each input's interval t and factors are computed
+// once, the sub-chunk is counting-sorted by t (stable: wave ballots give the
+// rank among equal t in index order, integer LDS counters the offsets), and
+// the factors and the values of all the workgroup's vectors are laid out in
+// interval order in LDS.  Thread j then owns u_j and v_j of every vector in
+// registers: it adds the alpha parts of interval j and the beta parts of
+// interval j+1, slot by slot.  No float atomics, and a fixed summation
+// order, so the results are deterministic.
+constexpr int kSub = 2048;                      // inputs per sub-chunk
+constexpr int kSubItems = kSub / kGenThreads;   // 2 per thread
+constexpr int kGenWaves = kGenThreads / kWave;  // 16
+constexpr int kBucketVG = 8;                    // vectors per workgroup (max)
+
+// Active lanes of this wave whose 11-bit value equals ours.
+__device__ __forceinline__ uint64_t match_bits11(uint32_t d)
+{
+    uint64_t peers = __ballot(1);
+#pragma unroll
+    for (int b = 0; b < 11; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const uint64_t bal = __ballot(bit);
+        peers &= bit ? bal : ~bal;
+    }
+    return peers;
+}
+
 template <int C>
-__global__ __launch_bounds__(kGenThreads) void lx_bucket_lds(BucketArgs A, int VG, int groups,
-                                                            int64_t chunk_len)
+__global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, int VG, int groups,
+                                                               int64_t chunk_len)
 {
     extern __shared__ float lds[];
-    const int64_t no = A.n_out;
-    float* so = lds;
-    float* bins = lds + pad64(no);  // [VG][C][2][no]
+    const int no = (int)A.n_out;  // <= kGenThreads
+    const int nbins = no + 1;     // intervals t = 0..no
+    float* so = lds;                                                                   // [no]
+    uint16_t* wcnt = reinterpret_cast<uint16_t*>(lds + pad64(no));                     // [16][nbins]
+    uint32_t* start = reinterpret_cast<uint32_t*>(wcnt + pad64(kGenWaves * nbins));    // [nbins+1]
+    float4* coef = reinterpret_cast<float4*>(start + pad64(nbins + 1));                // [kSub]: (au0, au1, bv0, bv1)
+    float4* xs = coef + kSub;                                                          // [kSub][2]: 8 vectors
+    __shared__ uint32_t sred[kGenWaves];
+
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
     const int g = (int)(blockIdx.x % groups);
     const int64_t chunk = blockIdx.x / groups;
     const int64_t v0 = (int64_t)g * VG;
     const int nv = (int)((A.batch - v0) < VG ? (A.batch - v0) : VG);
+    for (int i = tid; i < no; i += kGenThreads) so[i] = A.s_out[i];
 
-    for (int64_t i = threadIdx.x; i < no; i += kGenThreads) so[i] = A.s_out[i];
-    for (int64_t i = threadIdx.x; i < (int64_t)VG * C * 2 * no; i += kGenThreads) bins[i] = 0.f;
-    __syncthreads();
+    float au[kBucketVG][C], av[kBucketVG][C];  // u_tid and v_tid of each vector
+#pragma unroll
+    for (int vi = 0; vi < kBucketVG; ++vi)
+#pragma unroll
+        for (int c = 0; c < C; ++c) au[vi][c] = av[vi][c] = 0.f;
 
     const int64_t j0 = chunk * chunk_len;
     int64_t j1 = j0 + chunk_len;
     if (j1 > A.n_in) j1 = A.n_in;
-    for (int64_t j = j0 + threadIdx.x; j < j1; j += kGenThreads) {
-        const float q = A.in_anchor[j];
-        const int64_t t = lower_bound_f(so, no, q);
-        const float al = t < no ? decay_f(q, so[t]) : 0.f;
-        const float be = t > 0 ? decay_f(so[t - 1], q) : 0.f;
-        float f[C];
-        if (C == 2) phase_cs(A.in_phase, j, f[0], f[C - 1]);
-        else f[0] = 1.f;
-        for (int vi = 0; vi < nv; ++vi) {
-            const float xv = A.x[(v0 + vi) * A.n_in + j];
+    for (int64_t sub0 = j0; sub0 < j1; sub0 += kSub) {
+        for (int i = tid; i < kGenWaves * nbins; i += kGenThreads) wcnt[i] = 0;
+        __syncthreads();
+        // this thread's items: element sub0 + 128 w + 64 j + lane (wave-striped)
+        int64_t idx[kSubItems];
+        uint32_t tt[kSubItems], slot[kSubItems];
+        float4 cf[kSubItems];
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
-                const float val = f[c] * xv;
-                float* b = bins + ((int64_t)(vi * C + c) * 2) * no;
-                if (t < no) atomicAdd(b + t, al * val);
-                if (t > 0) atomicAdd(b + no + (t - 1), be * val);
+        for (int j = 0; j < kSubItems; ++j) {
+            idx[j] = sub0 + w * (kSubItems * kWave) + j * kWave + lane;
+            float al = 0.f, be = 0.f, f0 = 1.f, f1 = 0.f;
+            uint32_t t = (uint32_t)no;  // past the end: weight 0 in the last interval
+            if (idx[j] < j1) {
+                const float q = A.in_anchor[idx[j]];
+                t = (uint32_t)lower_bound_f(so, no, q);
+                al = t < (uint32_t)no ? decay_f(q, so[t]) : 0.f;
+                be = t > 0 ? decay_f(so[t - 1], q) : 0.f;
+                if (C == 2) {
+                    f0 = A.in_cos[idx[j]];
+                    f1 = A.in_sin[idx[j]];
+                }
+            }
+            tt[j] = t;
+            cf[j] = make_float4(al * f0, al * f1, be * f0, be * f1);
+        }
+        // stable rank among equal intervals: per wave, items in (j, lane) order
+#pragma unroll
+        for (int j = 0; j < kSubItems; ++j) {
+            const uint64_t peers = match_bits11(tt[j]);
+            const uint32_t below = count_below(peers);
+            const uint32_t prev = wcnt[w * nbins + tt[j]];
+            slot[j] = prev + below;
+            if (below == 0) wcnt[w * nbins + tt[j]] = (uint16_t)(prev + (uint32_t)__popcll(peers));
+        }
+        __syncthreads();
+        // per interval: offsets of the waves and the sub-chunk count; then starts
+        uint32_t cnt0 = 0, cnt1 = 0;
+        if (tid < nbins) {
+            uint32_t run = 0;
+            for (int ww = 0; ww < kGenWaves; ++ww) {
+                const uint32_t c = wcnt[ww * nbins + tid];
+                wcnt[ww * nbins + tid] = (uint16_t)run;
+                run += c;
+            }
+            cnt0 = run;
+        }
+        if (tid + kGenThreads < nbins) {  // interval 1024 when no == 1024
+            uint32_t run = 0;
+            for (int ww = 0; ww < kGenWaves; ++ww) {
+                const uint32_t c = wcnt[ww * nbins + tid + kGenThreads];
+                wcnt[ww * nbins + tid + kGenThreads] = (uint16_t)run;
+                run += c;
+            }
+            cnt1 = run;
+        }
+        (void)cnt1;
+        uint32_t tot0;
+        const uint32_t ex0 = block_exsum_u32<kGenWaves>(cnt0, sred, tot0);
+        if (tid < nbins) start[tid] = ex0;
+        if (tid + kGenThreads < nbins) start[tid + kGenThreads] = tot0;
+        if (tid == 0) start[nbins] = kSub;
+        __syncthreads();
+        // lay out factors and the values of every vector in interval order
+#pragma unroll
+        for (int j = 0; j < kSubItems; ++j) {
+            const uint32_t sl = slot[j] + start[tt[j]] + wcnt[w * nbins + tt[j]];
+            coef[sl] = cf[j];
+            float xv[kBucketVG];
+#pragma unroll
+            for (int vi = 0; vi < kBucketVG; ++vi)
+                xv[vi] = (vi < nv && idx[j] < j1) ? A.x[(v0 + vi) * A.n_in + idx[j]] : 0.f;
+            xs[2 * sl] = make_float4(xv[0], xv[1], xv[2], xv[3]);
+            xs[2 * sl + 1] = make_float4(xv[4], xv[5], xv[6], xv[7]);
+        }
+        __syncthreads();
+        if (tid < no) {
+            const uint32_t s0 = start[tid], s1 = start[tid + 1], s2 = start[tid + 2];
+            for (uint32_t sl = s0; sl < s1; ++sl) {  // interval tid: alpha parts -> u_tid
+                const float4 f = coef[sl];
+                const float4 xa = xs[2 * sl], xb = xs[2 * sl + 1];
+                const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+                for (int vi = 0; vi < kBucketVG; ++vi) {
+                    au[vi][0] = fmaf(f.x, xv[vi], au[vi][0]);
+                    if (C == 2) au[vi][C - 1] = fmaf(f.y, xv[vi], au[vi][C - 1]);
+                }
+            }
+            for (uint32_t sl = s1; sl < s2; ++sl) {  // interval tid+1: beta parts -> v_tid
+                const float4 f = coef[sl];
+                const float4 xa = xs[2 * sl], xb = xs[2 * sl + 1];
+                const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+                for (int vi = 0; vi < kBucketVG; ++vi) {
+                    av[vi][0] = fmaf(f.z, xv[vi], av[vi][0]);
+                    if (C == 2) av[vi][C - 1] = fmaf(f.w, xv[vi], av[vi][C - 1]);
+                }
             }
         }
+        __syncthreads();
     }
-    __syncthreads();
     // partial layout [chunk][batch][C][2][no]
-    for (int64_t i = threadIdx.x; i < (int64_t)nv * C * 2 * no; i += kGenThreads) {
-        const int64_t vi = i / (C * 2 * no);
-        const int64_t rest = i - vi * (C * 2 * no);
-        A.partial[((chunk * A.batch + v0 + vi) * C * 2) * no + rest] = bins[i];
+    if (tid < no) {
+#pragma unroll
+        for (int vi = 0; vi < kBucketVG; ++vi)
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                if (vi >= nv) continue;
+                float* pp = A.partial + ((chunk * A.batch + v0 + vi) * C + c) * 2 * no;
+                pp[tid] = au[vi][c];
+                pp[no + tid] = av[vi][c];
+            }
     }
+}
+
+static size_t bucket_sorted_lds(int64_t no, int C)
+{
+    (void)C;
+    const int64_t nbins = no + 1;
+    return (size_t)(pad64(no) + pad64(kGenWaves * nbins) / 2 + pad64(nbins + 1)) * 4 + (size_t)kSub * 16 * 3;
 }
 
 __global__ __launch_bounds__(256) void lx_bucket_reduce(const float* __restrict__ partial, int64_t chunks,
@@ -135,8 +260,8 @@ __global__ __launch_bounds__(256) void lx_bucket_global(BucketArgs A)
         const float al = t < no ? decay_f(q, A.s_out[t]) : 0.f;
         const float be = t > 0 ? decay_f(A.s_out[t - 1], q) : 0.f;
         float f[C];
-        if (C == 2) phase_cs(A.in_phase, j, f[0], f[C - 1]);
-        else f[0] = 1.f;
+        f[0] = C == 2 ? A.in_cos[j] : 1.f;
+        if (C == 2) f[C - 1] = A.in_sin[j];
         for (int64_t vv = 0; vv < A.batch; ++vv) {
             const float xv = A.x[vv * A.n_in + j];
 #pragma unroll
@@ -152,25 +277,26 @@ __global__ __launch_bounds__(256) void lx_bucket_global(BucketArgs A)
 
 static void bucket_shape(const BucketArgs& a, int* vg, int* groups, int* chunks, int64_t* chunk_len)
 {
-    const int64_t lds_floats = a.lds_bytes / 4;
-    const int64_t per_vec = (int64_t)a.channels * 2 * a.n_out;
-    int64_t v = (lds_floats - pad64(a.n_out)) / (per_vec > 0 ? per_vec : 1);
-    if (v > 16) v = 16;
-    if (v > a.batch) v = a.batch;
-    if (a.lds_bytes <= 0 || v < 1) {
+    const bool fits = a.n_out <= kGenThreads && a.lds_bytes > 0 &&
+                      (int64_t)bucket_sorted_lds(a.n_out, a.channels) <= a.lds_bytes;
+    if (!fits) {
         *vg = 0;
         *groups = *chunks = 0;
         *chunk_len = 0;
         return;
     }
+    int64_t v = kBucketVG;
+    if (v > a.batch) v = a.batch;
     *vg = (int)v;
     *groups = (int)((a.batch + v - 1) / v);
-    int64_t c = (a.n_in + 16383) / 16384;
-    int64_t cap = (1024 + *groups - 1) / *groups;
-    if (c > cap) c = cap;
+    // chunks of whole sub-chunks, about 512 workgroups in all
+    int64_t subs = (a.n_in + kSub - 1) / kSub;
+    if (subs < 1) subs = 1;
+    int64_t c = (512 + *groups - 1) / *groups;
+    if (c > subs) c = subs;
     if (c < 1) c = 1;
-    *chunk_len = (a.n_in + c - 1) / c;
-    if (*chunk_len < 1) *chunk_len = 1;
+    const int64_t per = (subs + c - 1) / c;
+    *chunk_len = per * kSub;
     *chunks = (int)((a.n_in + *chunk_len - 1) / *chunk_len);
     if (*chunks < 1) *chunks = 1;
 }
@@ -194,14 +320,14 @@ hipError_t bucket_launch(BucketArgs& a, hipStream_t s)
     bucket_shape(a, &vg, &groups, &chunks, &chunk_len);
     const bool two = a.channels == 2;
     if (vg > 0 && a.partial && a.n_in > 0) {
-        const size_t shmem = (size_t)(pad64(a.n_out) + (int64_t)vg * a.channels * 2 * a.n_out) * 4;
+        const size_t shmem = bucket_sorted_lds(a.n_out, a.channels);
         const unsigned blocks = (unsigned)((int64_t)chunks * groups);
         if (two) {
-            (void)hipFuncSetAttribute((const void*)lx_bucket_lds<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-            LX_LAUNCH("bucket_lds", s, (lx_bucket_lds<2><<<blocks, kGenThreads, shmem, s>>>(a, vg, groups, chunk_len)));
+            (void)hipFuncSetAttribute((const void*)lx_bucket_sorted<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+            LX_LAUNCH("bucket_sorted", s, (lx_bucket_sorted<2><<<blocks, kGenThreads, shmem, s>>>(a, vg, groups, chunk_len)));
         } else {
-            (void)hipFuncSetAttribute((const void*)lx_bucket_lds<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-            LX_LAUNCH("bucket_lds", s, (lx_bucket_lds<1><<<blocks, kGenThreads, shmem, s>>>(a, vg, groups, chunk_len)));
+            (void)hipFuncSetAttribute((const void*)lx_bucket_sorted<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+            LX_LAUNCH("bucket_sorted", s, (lx_bucket_sorted<1><<<blocks, kGenThreads, shmem, s>>>(a, vg, groups, chunk_len)));
         }
         const int64_t total = a.batch * a.channels * 2 * a.n_out;
         int64_t rb = (total + 255) / 256;
@@ -265,8 +391,8 @@ __global__ __launch_bounds__(kGenThreads) void lx_eval(EvalArgs A, int VG, int g
         const float al = t > 0 ? decay_f(si[t - 1], o) : 0.f;
         const float be = t < ni ? decay_f(o, si[t]) : 0.f;
         float gc[C];
-        if (C == 2) phase_cs(A.out_phase, i, gc[0], gc[C - 1]);
-        else gc[0] = 1.f;
+        gc[0] = C == 2 ? A.out_cos[i] : 1.f;
+        if (C == 2) gc[C - 1] = A.out_sin[i];
         for (int vi = 0; vi < nv; ++vi) {
             float acc = 0.f;
 #pragma unroll

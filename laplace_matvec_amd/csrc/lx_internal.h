@@ -111,7 +111,8 @@ struct BucketArgs {
     int64_t batch = 0;
     const float* s_out = nullptr;    // sorted output anchors [n_out]
     const float* in_anchor = nullptr;  // [n_in], original order
-    const float* in_phase = nullptr;   // [n_in] or null
+    const float* in_cos = nullptr;     // cos / sin of the input phases, original order, or null
+    const float* in_sin = nullptr;
     const float* x = nullptr;        // [batch][n_in]
     int64_t ld = 0;                  // row stride of u, v
     float* u = nullptr;              // [channels][batch][ld] (overwritten)
@@ -131,7 +132,8 @@ struct EvalArgs {
     int64_t n_in = 0;                  // sorted input side
     int64_t batch = 0;
     const float* out_anchor = nullptr;  // [n_out]
-    const float* out_phase = nullptr;   // [n_out] or null
+    const float* out_cos = nullptr;     // cos / sin of the output phases, original order, or null
+    const float* out_sin = nullptr;
     const float* s_in = nullptr;        // sorted input anchors [n_in]
     int64_t ld = 0;                     // row stride of pl, pr
     const float* pl = nullptr;          // [channels][batch][ld]

@@ -45,7 +45,7 @@ constexpr int kSortTile = kSortThreads * kSortItems;  // 8192
 constexpr int kRadix = 256;
 constexpr int kHistThreads = 256;
 #ifndef LX_LOOKBACK
-#define LX_LOOKBACK 8
+#define LX_LOOKBACK 4
 #endif
 constexpr int kLookback = LX_LOOKBACK;  // predecessors read per look-back round
 
