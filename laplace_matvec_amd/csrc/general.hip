@@ -66,18 +66,7 @@ constexpr int kSubItems = kSub / kGenThreads;   // 2 per thread
 constexpr int kGenWaves = kGenThreads / kWave;  // 16
 constexpr int kBucketVG = 8;                    // vectors per workgroup (max)
 
-// Active lanes of this wave whose 11-bit value equals ours.
-__device__ __forceinline__ uint64_t match_bits11(uint32_t d)
-{
-    uint64_t peers = __ballot(1);
-#pragma unroll
-    for (int b = 0; b < 11; ++b) {
-        const bool bit = (d >> b) & 1u;
-        const uint64_t bal = __ballot(bit);
-        peers &= bit ? bal : ~bal;
-    }
-    return peers;
-}
+__device__ __forceinline__ uint64_t match_bits11(uint32_t d) { return match_bits<11>(d); }
 
 template <int C>
 __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, int VG, int groups,

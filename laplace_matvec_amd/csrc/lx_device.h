@@ -48,18 +48,25 @@ __device__ __forceinline__ uint32_t count_below(uint64_t mask)
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Active lanes of this wave whose 8-bit digit equals ours.
-__device__ __forceinline__ uint64_t match_digit8(uint32_t d)
+// Active lanes of this wave whose BITS-bit value equals ours: for each bit,
+// keep the lanes whose ballot bit agrees with ours, i.e. AND with
+// ~(ballot ^ m) where m is our bit spread over the word (0 or all ones).
+template <int BITS>
+__device__ __forceinline__ uint64_t match_bits(uint32_t d)
 {
-    uint64_t peers = __ballot(1);
+    const uint64_t act = __ballot(1);
+    uint32_t lo = (uint32_t)act, hi = (uint32_t)(act >> 32);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const bool bit = (d >> b) & 1u;
-        const uint64_t bal = __ballot(bit);
-        peers &= bit ? bal : ~bal;
+    for (int b = 0; b < BITS; ++b) {
+        const uint32_t m = (uint32_t)((int32_t)(d << (31 - b)) >> 31);  // bit b spread: 0 or ~0
+        const uint64_t bal = __ballot(m != 0u);
+        // v_bitop3 truth table indexed (S0 << 2 | S1 << 1 | S2): S0 & ~(S1 ^ S2) -> 0x90
+        lo = __builtin_amdgcn_bitop3_b32(lo, (uint32_t)bal, m, 0x90);
+        hi = __builtin_amdgcn_bitop3_b32(hi, (uint32_t)(bal >> 32), m, 0x90);
     }
-    return peers;
+    return ((uint64_t)hi << 32) | lo;
 }
+__device__ __forceinline__ uint64_t match_digit8(uint32_t d) { return match_bits<8>(d); }
 
 template <class T>
 struct Aff {

@@ -73,21 +73,28 @@ __global__ __launch_bounds__(kHistThreads) void lx_sort_hist(const float* __rest
     __shared__ uint32_t h[4][kRadix];
     for (int i = threadIdx.x; i < 4 * kRadix; i += kHistThreads) (&h[0][0])[i] = 0;
     __syncthreads();
-    bool bad = false;
-    const int64_t stride = (int64_t)gridDim.x * kHistThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kHistThreads + threadIdx.x; i < n; i += stride) {
-        const float f = a[i];
-        bad |= !finite_bits(f);
-        const uint32_t k = key_of(f);
+    uint32_t bad = 0;
+    auto count = [&](float f) {
+        const uint32_t u = __float_as_uint(f);
+        bad |= (~u & 0x7F800000u) == 0u;  // exponent all ones: NaN or Inf
+        const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
         atomicAdd(&h[0][k & 0xFF], 1u);
         atomicAdd(&h[1][(k >> 8) & 0xFF], 1u);
         atomicAdd(&h[2][(k >> 16) & 0xFF], 1u);
-        // The top digit (sign and exponent) takes few values, so many lanes
-        // collide: one add per group of equal lanes.
-        const uint32_t d3 = k >> 24;
-        const uint64_t peers = match_digit8(d3);
-        if (count_below(peers) == 0) atomicAdd(&h[3][d3], (uint32_t)__popcll(peers));
+        atomicAdd(&h[3][k >> 24], 1u);
+    };
+    // four anchors per thread per step (16-byte loads), then the ragged tail
+    const int64_t n4 = n / 4;
+    const float4* a4 = reinterpret_cast<const float4*>(a);
+    const int64_t stride = (int64_t)gridDim.x * kHistThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kHistThreads + threadIdx.x; i < n4; i += stride) {
+        const float4 v = a4[i];
+        count(v.x);
+        count(v.y);
+        count(v.z);
+        count(v.w);
     }
+    for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * kHistThreads + threadIdx.x; i < n; i += stride) count(a[i]);
     if (__any(bad) && lane_id() == 0) atomicOr(flag, 1u);
     __syncthreads();
     for (int i = threadIdx.x; i < 4 * kRadix; i += kHistThreads) {
@@ -137,11 +144,18 @@ __global__ __launch_bounds__(kSortThreads) void lx_sort_pass(
     // index order.  Positions past n get the largest key: they rank last,
     // in bin 255, and land past n.
     uint32_t key[kSortItems];
+    {
+        const int64_t wbase = tile0 + wpos;  // uniform
+        const uint32_t room = (uint32_t)(n - wbase < (int64_t)(kSortItems * kWave) ? (n > wbase ? n - wbase : 0)
+                                                                                   : (int64_t)(kSortItems * kWave));
+        const float* ain = a_in + wbase;
+        const uint32_t* kin = keys_in + wbase;
 #pragma unroll
-    for (int j = 0; j < kSortItems; ++j) {
-        const int64_t idx = tile0 + wpos + j * kWave + lane;
-        if (idx < n) key[j] = FIRST ? key_of(a_in[idx]) : keys_in[idx];
-        else key[j] = 0xFFFFFFFFu;
+        for (int j = 0; j < kSortItems; ++j) {
+            const uint32_t off = (uint32_t)(j * kWave + lane);
+            if (off < room) key[j] = FIRST ? key_of(ain[off]) : kin[off];
+            else key[j] = 0xFFFFFFFFu;
+        }
     }
 
     // Stable rank inside the wave: peers with the same digit, in lane order,
@@ -234,7 +248,7 @@ __global__ __launch_bounds__(kSortThreads) void lx_sort_pass(
         const uint32_t k = s_buf[i];
         const uint32_t d = (k >> shift) & 0xFFu;
         const uint32_t dst = s_glob[d] + (i - s_start[d]);
-        if ((int64_t)dst < n) {
+        if (dst < (uint32_t)n) {
             if (LAST) sorted_out[dst] = float_of_key(k);
             else keys_out[dst] = k;
         }
@@ -311,7 +325,7 @@ hipError_t sort_launch(const float* a, int64_t n, float* sorted, const SortRecor
     if (e != hipSuccess) return e;
 
     {
-        int64_t blocks = (n + kHistThreads * 16 - 1) / (kHistThreads * 16);
+        int64_t blocks = (n + kHistThreads * 64 - 1) / (kHistThreads * 64);
         if (blocks > 2048) blocks = 2048;
         LX_LAUNCH("sort_hist", s, (lx_sort_hist<<<(int)blocks, kHistThreads, 0, s>>>(a, n, hist, flag)));
     }
@@ -446,11 +460,11 @@ __global__ __launch_bounds__(kSortThreads) void lx_replay(const T* __restrict__ 
             __syncthreads();
 #pragma unroll
             for (int q = 0; q < kReplayItems; ++q)
-                if ((int64_t)dst[q] < n) ov[dst[q]] = buf[src[q]];
+                if (dst[q] < (uint32_t)n) ov[dst[q]] = buf[src[q]];
         } else {
 #pragma unroll
             for (int q = 0; q < kReplayItems; ++q)
-                if ((int64_t)dst[q] < n) buf[src[q]] = iv[dst[q]];
+                if (dst[q] < (uint32_t)n) buf[src[q]] = iv[dst[q]];
             __syncthreads();
 #pragma unroll
             for (int q = 0; q < kReplayItems; ++q) {
