@@ -57,7 +57,7 @@ def _load():
     lib.lo_dense_matrix.argtypes = [vp, vp, i64, vp, vp, i64, vp]
     lib.lo_apply_sym_sweep.argtypes = [vp, vp, vp, i64, vp, i64, vp]
     lib.lo_apply_general_sweep.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, vp]
-    lib.lo_gram_direct.argtypes = [vp, i64, vp, i64, vp, vp, i64, vp, i64, vp]
+    lib.lo_gram_direct.argtypes = [vp, vp, i64, vp, vp, i64, vp, vp, i64, vp, i64, vp]
     for f in (lib.lo_argsort, lib.lo_apply_dense, lib.lo_dense_matrix, lib.lo_apply_sym_sweep,
               lib.lo_apply_general_sweep, lib.lo_gram_direct, lib.lo_num_threads):
         f.restype = ctypes.c_int
@@ -168,10 +168,12 @@ def apply_sweep(a, x, b=None, phi=None, psi=None, transpose=False) -> np.ndarray
     return y[0] if one else y
 
 
-def gram_direct(a, b, D, rows=None, cols=None) -> np.ndarray:
-    """M = A diag(D) A^T with A = K(a, b), entry by entry in O(k) (summary
-    §2.2, Gram operators).  rows/cols select original indices of a."""
-    a, b, D = _f32(a), _f32(b), _f32(D)
+def gram_direct(a, b, D, rows=None, cols=None, phi=None, psi=None) -> np.ndarray:
+    """M = A diag(D) A^T with A = K(a, phi; b, psi), entry by entry in O(k)
+    (summary §2.2, Gram operators).  rows/cols select original indices of a."""
+    a, b, D, phi, psi = _f32(a), _f32(b), _f32(D), _f32(phi), _f32(psi)
+    if (phi is None) != (psi is None):
+        raise ValueError("phases: give both phi and psi or neither")
     if D.size != b.size:
         raise ValueError("D must have one weight per b anchor")
     r = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
@@ -179,7 +181,7 @@ def gram_direct(a, b, D, rows=None, cols=None) -> np.ndarray:
     mr = a.size if r is None else r.size
     mc = a.size if c is None else c.size
     M = np.empty((mr, mc), dtype=np.float64)
-    rc = _load().lo_gram_direct(_ptr(a), a.size, _ptr(b), b.size, _ptr(D), _ptr(r),
+    rc = _load().lo_gram_direct(_ptr(a), _ptr(phi), a.size, _ptr(b), _ptr(psi), b.size, _ptr(D), _ptr(r),
                                 0 if r is None else r.size, _ptr(c), 0 if c is None else c.size,
                                 _ptr(M))
     _check(rc, "gram_direct")

@@ -42,7 +42,9 @@
  *   lo_apply_sym_sweep     pinned (dense definition, KMS, Toeplitz FFT)
  *   lo_apply_general_sweep pinned (dense definition, zero temperature)
  *   lo_gram_direct         pinned (KMS inverse on both sides, zero-temperature
- *                          diagonal, Gram-apply consistency)
+ *                          diagonal, Gram-apply consistency; phased: reduces
+ *                          to the unphased Gram at zero phases, zero-temperature
+ *                          signed diagonal, Gram-apply consistency)
  */
 #include <math.h>
 #include <stdint.h>
@@ -297,14 +299,17 @@ out:
 /* ------------------------------------------------------------------- Gram */
 
 /* Weighted Gram matrix of summary §2.2, by its definition M = A diag(D) A^T
- * with A = K(a,b) (n x k), evaluated directly in O(k) per entry:
+ * with A = K(a, phi; b, psi) (n x k, phases optional: both NULL or both given),
+ * evaluated directly in O(k) per entry:
  *   M[r][c] = sum_l A[rows_r][l] * D_l * A[cols_c][l].
  * rows/cols == NULL mean all n.  Output is n_rows x n_cols row-major. */
-int lo_gram_direct(const float* a, int64_t n, const float* b, int64_t k, const float* D,
-                   const int64_t* rows, int64_t n_rows, const int64_t* cols, int64_t n_cols,
-                   double* M)
+int lo_gram_direct(const float* a, const float* phi, int64_t n, const float* b, const float* psi,
+                   int64_t k, const float* D, const int64_t* rows, int64_t n_rows, const int64_t* cols,
+                   int64_t n_cols, double* M)
 {
     if (n < 0 || k < 0 || !a || !M || (k > 0 && (!b || !D))) return LO_BADARG;
+    if ((phi == NULL) != (psi == NULL)) return LO_BADARG;
+    const int phased = phi != NULL;
     const int64_t mr = rows ? n_rows : n, mc = cols ? n_cols : n;
     for (int64_t r = 0; r < mr; ++r)
         if (rows && (rows[r] < 0 || rows[r] >= n)) return LO_BADARG;
@@ -313,12 +318,12 @@ int lo_gram_direct(const float* a, int64_t n, const float* b, int64_t k, const f
 #pragma omp parallel for schedule(dynamic, 1) collapse(2)
     for (int64_t r = 0; r < mr; ++r) {
         for (int64_t c = 0; c < mc; ++c) {
-            const double ai = a[rows ? rows[r] : r];
-            const double aj = a[cols ? cols[c] : c];
+            const int64_t i = rows ? rows[r] : r, j = cols ? cols[c] : c;
+            const double pi = phased ? phi[i] : 0.0, pj = phased ? phi[j] : 0.0;
             double acc = 0.0;
             for (int64_t l = 0; l < k; ++l) {
-                const double bl = b[l];
-                acc += exp(-fabs(ai - bl)) * (double)D[l] * exp(-fabs(aj - bl));
+                const double ql = phased ? psi[l] : 0.0;
+                acc += entry(a[i], pi, b[l], ql, phased) * (double)D[l] * entry(a[j], pj, b[l], ql, phased);
             }
             M[r * mc + c] = acc;
         }

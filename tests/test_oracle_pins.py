@@ -376,3 +376,43 @@ def test_gram_subset_matches_full():
     full = oracle.gram_direct(a, b, D)
     rows, cols = np.array([3, 0, 39]), np.array([7, 3])
     assert np.array_equal(oracle.gram_direct(a, b, D, rows=rows, cols=cols), full[np.ix_(rows, cols)])
+
+
+def test_phased_gram_zero_phases_is_unphased():
+    n, k = 30, 400
+    a = (RNG.standard_normal(n) * 3).astype(np.float32)
+    b = (RNG.standard_normal(k) * 3).astype(np.float32)
+    D = RNG.uniform(-1, 1, k).astype(np.float32)
+    z_n, z_k = np.zeros(n, np.float32), np.zeros(k, np.float32)
+    assert np.array_equal(oracle.gram_direct(a, b, D, phi=z_n, psi=z_k), oracle.gram_direct(a, b, D))
+
+
+def test_phased_gram_zero_temperature_signed_diagonal():
+    """A = K(a, phi; b, psi) with b = a[sigma] far apart: A[sigma_j, j] = cos(phi - psi),
+    so M is diagonal with D_j cos^2(phi_sigma_j - psi_j) (float64 cos of float32 phases)."""
+    n = 40
+    a = (1024.0 * RNG.permutation(n)).astype(np.float32)
+    sigma = RNG.permutation(n)
+    phi = RNG.uniform(0, 6.28, n).astype(np.float32)
+    psi = RNG.uniform(0, 6.28, n).astype(np.float32)
+    D = RNG.uniform(0, 1, n).astype(np.float32)
+    M = oracle.gram_direct(a, a[sigma], D, phi=phi, psi=psi)
+    ref = np.zeros((n, n))
+    ref[sigma, sigma] = D * np.cos(phi[sigma].astype(np.float64) - psi.astype(np.float64)) ** 2
+    np.testing.assert_allclose(M, ref, rtol=1e-15, atol=1e-300)
+
+
+def test_phased_gram_matches_apply_composition():
+    n, k = 50, 700
+    a = (RNG.standard_normal(n) * 5).astype(np.float32)
+    b = (RNG.standard_normal(k) * 5).astype(np.float32)
+    phi = RNG.uniform(0, 6.28, n).astype(np.float32)
+    psi = RNG.uniform(0, 6.28, k).astype(np.float32)
+    D = RNG.uniform(0, 1, k).astype(np.float32)
+    M = oracle.gram_direct(a, b, D, phi=phi, psi=psi)
+    A = oracle.dense_matrix(a, b=b, phi=phi, psi=psi)
+    for j in (0, 7, 49):
+        e = np.zeros(n, dtype=np.float32)
+        e[j] = 1
+        col_in = oracle.apply_dense(a, e, b=b, phi=phi, psi=psi, transpose=True) * D
+        np.testing.assert_allclose(M[:, j], A @ col_in, rtol=1e-12, atol=1e-14)
