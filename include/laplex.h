@@ -103,7 +103,10 @@ laplex_status laplex_apply(laplex_plan plan, const float* x, float* y, int64_t b
  *          real values.
  *   M      device float32[n][n], row-major, rows and columns in the original
  *          order of a.  Needs n * n <= 2^40 (else INVALID_ARGUMENT).
- *   Phased plans return LAPLEX_ERR_UNSUPPORTED.  Asynchronous on `stream`.
+ *   For a phased plan A carries the phases too (A_il = exp(-|a_i - b_l|)
+ *   cos(phi_i - psi_l)); the product of two cosines splits into three
+ *   unphased Grams with weights D cos^2 psi, D cos psi sin psi, D sin^2 psi.
+ *   Asynchronous on `stream`.
  */
 laplex_status laplex_gram(laplex_plan plan, const float* D, float* M, void* stream);
 

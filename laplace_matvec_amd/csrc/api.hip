@@ -676,7 +676,6 @@ laplex_status laplex_gram(laplex_plan p, const float* D, float* M, void* stream)
 {
     if (!p) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "plan is NULL");
     if (!D || !M) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "D or M is NULL");
-    if (p->phased) return fail(LAPLEX_ERR_UNSUPPORTED, "Gram of a phased operator");
     if ((double)p->n * (double)p->n > (double)((int64_t)1 << 40))
         return fail(LAPLEX_ERR_INVALID_ARGUMENT, "n * n too large for a dense Gram matrix");
     if (ranges_overlap(D, (size_t)p->k * 4, M, (size_t)(p->n * p->n) * 4))
@@ -685,7 +684,7 @@ laplex_status laplex_gram(laplex_plan p, const float* D, float* M, void* stream)
     hipStream_t s = (hipStream_t)stream;
     LX_TRY(ensure_perm(p, 0, s), "permutation of a");
     LX_TRY(ensure_perm(p, 1, s), "permutation of b");
-    LX_TRY(ensure_ws(p, lx::gram_scratch_bytes(p->n), s), "workspace");
+    LX_TRY(ensure_ws(p, lx::gram_scratch_bytes(p->n, p->phased ? 3 : 1), s), "workspace");
     lx::GramArgs G;
     G.n = p->n;
     G.k = p->k;
@@ -694,6 +693,12 @@ laplex_status laplex_gram(laplex_plan p, const float* D, float* M, void* stream)
     G.sb = p->sb;
     G.pb = p->pb;
     G.D = D;
+    if (p->phased) {
+        G.cphi_r = p->cphi;
+        G.sphi_r = p->sphi;
+        G.cpsi_r = p->cpsi;
+        G.spsi_r = p->spsi;
+    }
     G.stats = (double*)p->ws;
     G.M = M;
     LX_TRY(lx::gram_launch(G, s), "gram");

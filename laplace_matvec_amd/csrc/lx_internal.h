@@ -151,10 +151,14 @@ struct GramArgs {
     const float* sb = nullptr;      // sorted b [k]
     const uint32_t* pb = nullptr;   // perm of b
     const float* D = nullptr;       // [k], original order of b
+    const float* cphi_r = nullptr;  // phased: cos/sin of phi by rank of a, of psi by rank of b
+    const float* sphi_r = nullptr;
+    const float* cpsi_r = nullptr;
+    const float* spsi_r = nullptr;
     double* stats = nullptr;        // scratch: see gram.hip
     float* M = nullptr;             // [n][n]
 };
-size_t gram_scratch_bytes(int64_t n);
+size_t gram_scratch_bytes(int64_t n, int weight_sets);
 hipError_t gram_launch(const GramArgs& a, hipStream_t s);
 
 }  // namespace lx

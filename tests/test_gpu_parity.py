@@ -275,12 +275,54 @@ def test_gram_symmetric_plan(gpu):
     assert oracle.rel_l2(M, oracle.gram_direct(a, a, D)) < TOL
 
 
-def test_gram_phased_unsupported(gpu):
-    a = dev(RNG.standard_normal(10))
-    with lx.laplex_plan_create(a, phi=a.clone(), psi=a.clone()) as plan:
-        with pytest.raises(lx.LaplexError) as e:
-            lx.laplex_gram(plan, dev(np.ones(10)))
-        assert e.value.status == lx.ERR_UNSUPPORTED
+@pytest.mark.parametrize("n,k", [(1, 1), (7, 3), (300, 5000), (400, 40000)])
+def test_gram_phased_general(gpu, n, k):
+    say(f"[gram phased] n={n} k={k}")
+    rng = np.random.default_rng(7 * n + k)
+    a = (rng.standard_normal(n) * 20).astype(np.float32)
+    b = (rng.standard_normal(k) * 20).astype(np.float32)
+    m = min(n, k) // 5
+    if m:
+        b[rng.integers(0, k, m)] = a[rng.integers(0, n, m)]
+    phi = rng.uniform(-np.pi, np.pi, n).astype(np.float32)
+    psi = rng.uniform(-np.pi, np.pi, k).astype(np.float32)
+    D = rng.uniform(-1, 1, k).astype(np.float32)
+    with lx.laplex_plan_create(dev(a), b=dev(b), phi=dev(phi), psi=dev(psi)) as plan:
+        M = host(lx.laplex_gram(plan, dev(D)))
+    ref = oracle.gram_direct(a, b, D, phi=phi, psi=psi)
+    assert oracle.rel_l2(M, ref) < TOL
+
+
+def test_gram_phased_symmetric_plan(gpu):
+    n = 2000
+    a = anchors_with_ties(n, 10.0)
+    phi = RNG.uniform(-np.pi, np.pi, n).astype(np.float32)
+    psi = RNG.uniform(-np.pi, np.pi, n).astype(np.float32)
+    D = RNG.uniform(0, 1, n).astype(np.float32)
+    with lx.laplex_plan_create(dev(a), phi=dev(phi), psi=dev(psi)) as plan:
+        M = host(lx.laplex_gram(plan, dev(D)))
+    ref = oracle.gram_direct(a, a, D, phi=phi, psi=psi)
+    assert oracle.rel_l2(M, ref) < TOL
+    # a phased symmetric plan is still a real Gram: M = M^T
+    assert np.allclose(M, M.T, rtol=1e-5, atol=1e-6 * np.abs(M).max())
+
+
+def test_gram_phased_zero_temperature_diagonal(gpu):
+    # anchors 1024 apart: A is a signed permutation, M diagonal with
+    # M_ii = D_l cos^2(phi_i - psi_l) for the partner l of i
+    n = 3000
+    a = (1024.0 * RNG.permutation(n)).astype(np.float32)
+    sigma = RNG.permutation(n)
+    phi = RNG.uniform(-np.pi, np.pi, n).astype(np.float32)
+    psi = RNG.uniform(-np.pi, np.pi, n).astype(np.float32)
+    D = RNG.uniform(0, 1, n).astype(np.float32)
+    with lx.laplex_plan_create(dev(a), b=dev(a[sigma]), phi=dev(phi), psi=dev(psi)) as plan:
+        M = host(lx.laplex_gram(plan, dev(D)))
+    inv = np.argsort(sigma)  # b_l = a_{sigma_l}: partner of row i is l = inv[i]
+    diag = D[inv].astype(np.float64) * np.cos(phi.astype(np.float64) - psi[inv].astype(np.float64)) ** 2
+    off = M - np.diag(np.diag(M))
+    assert np.all(off == 0)
+    assert np.allclose(np.diag(M), diag, rtol=1e-5, atol=1e-7)
 
 
 def test_gram_zero_temperature_diagonal(gpu):
