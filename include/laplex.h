@@ -9,8 +9,9 @@
  *   operator (summary §2.1):  K = LAPLEX(a, phi; b, psi),
  *       K_ij = exp(-|a_i - b_j|) * cos(phi_i - psi_j),   a in R^n, b in R^k.
  *   Without phases the cosine factor is 1.  A symmetric plan has b = a.
- *   The temperature of the pages is fixed to 1 (scale the anchors by 1/t for
- *   another temperature).
+ *   A plan's temperature t (laplex_plan_set_temperature, default 1) divides
+ *   the exponent: exp(-|a_i - b_j| / t); t = 0 is the zero-temperature limit
+ *   of summary §2.1 and §2.3, the equality-routing matrix [a_i == b_j].
  *
  *   algorithm (summary §2.2): sort the anchors; apply the lower and upper
  *   triangular parts by a prefix and a suffix scan of the recurrence
@@ -110,6 +111,34 @@ laplex_status laplex_apply(laplex_plan plan, const float* x, float* y, int64_t b
  */
 laplex_status laplex_gram(laplex_plan plan, const float* D, float* M, void* stream);
 
+/*
+ * laplex_backward -- gradients of a training step through y = K x
+ *   (transpose = 0) or y = K^T x (transpose = 1), K at the plan's temperature.
+ *   (summary §2.1: a LAPLEX layer is trained through its anchors and phases;
+ *   the derivatives are those of the definition, entry by entry)
+ *
+ *   x      device float32 [batch][in]: the forward input ((in, out) as in
+ *          laplex_apply).
+ *   g      device float32 [batch][out]: the upstream gradient dL/dy.
+ *   dx     [batch][in]: dL/dx = K^T g (transpose = 0) or K g (transpose = 1).
+ *   da     [n]: dL/da summed over the batch.  For y = K x,
+ *            dL/da_i = -(1/t) sum_v g_vi sum_j sgn(a_i - b_j) K_ij x_vj;
+ *          a symmetric plan (b = a) adds the column-side term, so da is the
+ *          full gradient of its one anchor vector.
+ *   db     [k]: dL/db (general plans only; must be NULL for a symmetric plan).
+ *   dphi   [n], dpsi [k] (symmetric: [n]): phase gradients, phased plans only
+ *          (must be NULL otherwise).  dL/dphi_i = -sum_v g_vi sum_j
+ *          exp(-|a_i - b_j| / t) sin(phi_i - psi_j) x_vj for transpose = 0.
+ *   Each output may be NULL to skip it; outputs are overwritten and must not
+ *   overlap each other, x or g.  sgn(0) = 0: equal anchors exert no force on
+ *   each other (the mean of the two one-sided derivatives).  At t = 0 the
+ *   anchor gradients are 0 (the routing matrix is piecewise constant).
+ *   Asynchronous on `stream`; shares the plan's workspace with apply/gram.
+ */
+laplex_status laplex_backward(laplex_plan plan, const float* x, const float* g, int64_t batch,
+                              int transpose, float* dx, float* da, float* db, float* dphi,
+                              float* dpsi, void* stream);
+
 /* Releases all device memory of the plan (synchronizes the device first).
  * NULL is accepted. */
 laplex_status laplex_plan_destroy(laplex_plan plan);
@@ -141,6 +170,21 @@ laplex_status laplex_plan_info(laplex_plan plan, int64_t* n, int64_t* k, int* fl
 #define LAPLEX_ALGO_BUCKET 1
 #define LAPLEX_ALGO_EVALUATE 2
 laplex_status laplex_plan_set_option(laplex_plan plan, int option, int64_t value);
+
+/*
+ * laplex_plan_set_temperature -- entries exp(-|a_i - b_j| / t) cos(phi_i - psi_j)
+ *   for every later apply / gram / backward of the plan.
+ *   (summary §2.1: the temperature t -> 0 regime; §2.3: zero-temperature
+ *   limit, equality routing that recovers permutations and CountSketch)
+ *
+ *   t      1 is the operator as printed (the default).  t = 0 selects the
+ *          limit: 1 where a_i == b_j (-0.0 == +0.0), else 0, so y routes x by
+ *          exact equality of anchors.  Otherwise FLT_MIN <= t <= FLT_MAX;
+ *          anything else (negative, NaN, Inf, subnormal) is INVALID_ARGUMENT.
+ *   The sort order does not depend on t, so the plan is reused as is.  Not
+ *   ordered with in-flight work: call it between applies on the same thread.
+ */
+laplex_status laplex_plan_set_temperature(laplex_plan plan, double t);
 
 /* Kernel timing: while enabled, every kernel the library launches is
  * bracketed by HIP events on its stream.  laplex_profile_collect waits for

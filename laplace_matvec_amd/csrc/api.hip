@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
+#include <cfloat>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -155,6 +157,8 @@ struct laplex_plan_s {
     int64_t n = 0, k = 0;
     bool sym = true, phased = false;
     int algo = LAPLEX_ALGO_AUTO;
+    double temperature = 1.0;
+    double inv_t = 1.0;  // 1 / temperature, +inf at temperature 0
     int lds_bytes = 0;
     // sorted sides and the replay records of their sorts
     float* sa = nullptr;
@@ -508,6 +512,16 @@ laplex_status laplex_plan_set_option(laplex_plan p, int option, int64_t value)
     return LAPLEX_OK;
 }
 
+laplex_status laplex_plan_set_temperature(laplex_plan p, double t)
+{
+    if (!p) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (!(t == 0.0 || (t >= (double)FLT_MIN && t <= (double)FLT_MAX)))
+        return fail(LAPLEX_ERR_INVALID_ARGUMENT, "temperature must be 0 or in [FLT_MIN, FLT_MAX]");
+    p->temperature = t;
+    p->inv_t = t > 0.0 ? 1.0 / t : HUGE_VAL;
+    return LAPLEX_OK;
+}
+
 laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batch, int transpose, void* stream)
 {
     if (!p) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "plan is NULL");
@@ -533,6 +547,7 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
         lx::ScanArgs A;
         A.mode = lx::kScanSym;
         scan_common(A, cv, n, batch, ch);
+        A.inv_t = p->inv_t;
         A.s = p->sa;
         A.perm = p->pa;
         if (p->phased) {
@@ -598,6 +613,7 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
         A.mode = lx::kScanPLPR;
         A.random = true;
         scan_common(A, cv, ni, batch, ch);
+        A.inv_t = p->inv_t;
         A.s = s_i;
         A.perm = p_i;
         A.x = x;
@@ -614,6 +630,7 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
         E.n_out = no;
         E.n_in = ni;
         E.batch = batch;
+        E.inv_t = (float)p->inv_t;
         E.out_anchor = anchor_o;
         if (p->phased) {
             E.out_cos = co0;
@@ -635,6 +652,7 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
     Bk.n_out = no;
     Bk.n_in = ni;
     Bk.batch = batch;
+    Bk.inv_t = (float)p->inv_t;
     Bk.s_out = s_o;
     Bk.in_anchor = anchor_i;
     if (p->phased) {
@@ -652,6 +670,7 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
     A.mode = lx::kScanUV;
     A.random = true;
     scan_common(A, cv, no, batch, ch);
+    A.inv_t = p->inv_t;
     A.s = s_o;
     A.perm = p_o;
     float* u = cv.take<float>((size_t)ch * batch * A.ld);
@@ -672,6 +691,202 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
     return LAPLEX_OK;
 }
 
+namespace {
+
+// One side of a general plan's gradient: outputs on side "o" (original
+// order) from the prefix/suffix tables of the sorted side "i" of input V.
+struct GradSide {
+    int64_t no, ni;
+    const float* s_i;
+    const uint32_t* p_i;
+    const float* c_i;   // cos/sin of side i's phases by rank (phased)
+    const float* sn_i;
+    const float* anchor_o;
+    const float* c_o0;  // cos/sin of side o's phases, original order (phased)
+    const float* s_o0;
+};
+
+laplex_status grad_general_side(laplex_plan p, const GradSide& G, const float* V, const float* W, int64_t batch,
+                                float* y, float* d_anchor, float* d_phase, hipStream_t s)
+{
+    if (!y && !d_anchor && !d_phase) return LAPLEX_OK;
+    const int ch = p->phased ? 2 : 1;
+    LX_TRY(ensure_ws(p, scan_ws_bytes(G.ni, batch, ch, 1, 2), s), "workspace");
+    Carve cv(p->ws);
+    lx::ScanArgs A;
+    A.mode = lx::kScanPLPR;
+    A.random = true;
+    scan_common(A, cv, G.ni, batch, ch);
+    A.inv_t = p->inv_t;
+    A.s = G.s_i;
+    A.perm = G.p_i;
+    A.x = V;
+    A.xs = cv.take<float>((size_t)batch * A.ld);
+    A.pl = cv.take<float>((size_t)ch * batch * A.ld);
+    A.pr = cv.take<float>((size_t)ch * batch * A.ld);
+    if (p->phased) {
+        A.in_c = G.c_i;
+        A.in_s = G.sn_i;
+    }
+    LX_TRY(lx::scan_launch(A, s), "scan over the input side");
+    lx::EvalGradArgs E;
+    E.channels = ch;
+    E.n_out = G.no;
+    E.n_in = G.ni;
+    E.batch = batch;
+    E.ld = A.ld;
+    E.inv_t = (float)p->inv_t;
+    E.anchor_scale = p->temperature > 0.0 ? (float)(-1.0 / p->temperature) : 0.f;
+    E.out_anchor = G.anchor_o;
+    if (p->phased) {
+        E.out_cos = G.c_o0;
+        E.out_sin = G.s_o0;
+    }
+    E.s_in = G.s_i;
+    E.pl = A.pl;
+    E.pr = A.pr;
+    E.w = W;
+    E.y = y;
+    E.d_anchor = d_anchor;
+    E.d_phase = d_phase;
+    E.lds_bytes = p->lds_bytes;
+    LX_TRY(lx::eval_grad_launch(E, s), "evaluate gradients");
+    return LAPLEX_OK;
+}
+
+}  // namespace
+
+laplex_status laplex_backward(laplex_plan p, const float* x, const float* g, int64_t batch, int transpose,
+                              float* dx, float* da, float* db, float* dphi, float* dpsi, void* stream)
+{
+    if (!p) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (!x || !g) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "x or g is NULL");
+    if (batch < 1) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "batch must be >= 1");
+    if (transpose != 0 && transpose != 1) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "transpose must be 0 or 1");
+    if (p->sym && db) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "symmetric plan: the gradient of b = a is in da");
+    if (!p->phased && (dphi || dpsi)) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "unphased plan has no phase gradients");
+    const int64_t len_in = transpose ? p->n : p->k;
+    const int64_t len_out = transpose ? p->k : p->n;
+    if (batch > (int64_t)1 << 40 || (double)batch * (double)(len_in > len_out ? len_in : len_out) > 4.0e18 / 4)
+        return fail(LAPLEX_ERR_INVALID_ARGUMENT, "batch too large");
+    struct Range {
+        const void* p;
+        size_t bytes;
+    };
+    const Range outs[5] = {{dx, (size_t)(batch * len_in) * 4}, {da, (size_t)p->n * 4}, {db, (size_t)p->k * 4},
+                           {dphi, (size_t)p->n * 4}, {dpsi, (size_t)p->k * 4}};
+    const Range ins[2] = {{x, (size_t)(batch * len_in) * 4}, {g, (size_t)(batch * len_out) * 4}};
+    for (int i = 0; i < 5; ++i) {
+        if (!outs[i].p) continue;
+        for (int j = 0; j < 2; ++j)
+            if (ranges_overlap(outs[i].p, outs[i].bytes, ins[j].p, ins[j].bytes))
+                return fail(LAPLEX_ERR_INVALID_ARGUMENT, "an output overlaps x or g");
+        for (int j = i + 1; j < 5; ++j)
+            if (outs[j].p && ranges_overlap(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes))
+                return fail(LAPLEX_ERR_INVALID_ARGUMENT, "two outputs overlap");
+    }
+    if (!dx && !da && !db && !dphi && !dpsi) return LAPLEX_OK;
+    DeviceGuard guard(p->device);
+    hipStream_t s = (hipStream_t)stream;
+    const int ch = p->phased ? 2 : 1;
+    // row side u, column side w of F = sum <u, K w>
+    const float* u = transpose ? x : g;
+    const float* w = transpose ? g : x;
+    const float anchor_scale = p->temperature > 0.0 ? (float)(-1.0 / p->temperature) : 0.f;
+
+    if (p->sym) {
+        const int64_t n = p->n;
+        const bool replay = n >= replay_min();
+        if (!replay) LX_TRY(ensure_perm(p, 0, s), "permutation");
+        const int64_t ld = pad64(n);
+        const int64_t tiles = (n + lx::kScanTile - 1) / lx::kScanTile;
+        const int64_t groups = (tiles + lx::kCarryGroup - 1) / lx::kCarryGroup;
+        const int64_t rows = 4 * (int64_t)ch * batch;
+        const int64_t nout = (dx ? batch : 0) + (da ? 1 : 0) + (dphi ? 1 : 0) + (dpsi ? 1 : 0);
+        const int64_t tmp_rows = replay ? (2 * batch > nout ? 2 * batch : nout) : batch;
+        const size_t need = align256((size_t)rows * tiles * 4 * 8) + align256((size_t)rows * groups * 4 * 8) +
+                            align256((size_t)rows * tiles * 2 * 8) + 2 * align256((size_t)tmp_rows * ld * 4);
+        LX_TRY(ensure_ws(p, need, s), "workspace");
+        Carve cv(p->ws);
+        lx::GradSymArgs A;
+        A.channels = ch;
+        A.n = n;
+        A.tiles = tiles;
+        A.batch = batch;
+        A.ld = ld;
+        A.out_ld = ld;
+        A.inv_t = p->inv_t;
+        A.anchor_scale = anchor_scale;
+        A.dx_half = transpose ? 0 : 1;
+        A.s = p->sa;
+        A.perm = p->pa;
+        if (p->phased) {
+            A.cphi = p->cphi;
+            A.sphi = p->sphi;
+            A.cpsi = p->cpsi;
+            A.spsi = p->spsi;
+        }
+        A.agg = cv.take<double>((size_t)rows * tiles * 4);
+        A.gagg = cv.take<double>((size_t)rows * groups * 4);
+        A.carry = cv.take<double>((size_t)rows * tiles * 2);
+        float* t1 = cv.take<float>((size_t)tmp_rows * ld);
+        float* t2 = cv.take<float>((size_t)tmp_rows * ld);
+        if (!replay) {
+            A.random = true;
+            A.u = u;
+            A.w = w;
+            A.us = t1;
+            A.ws = t2;
+            A.dx = dx;
+            A.da = da;
+            A.dphi = dphi;
+            A.dpsi = dpsi;
+            LX_TRY(lx::grad_sym_launch(A, s), "symmetric gradient");
+            return LAPLEX_OK;
+        }
+        // u, w -> sorted order (rows [0, B) and [B, 2B)), gradient by rank into
+        // t1, then the wanted rows back to original order.
+        const lx::SortRecords& R = p->ra;
+        LX_TRY(lx::replay_launch(R, 0, true, u, n, t1, ld, batch, s), "replay");
+        LX_TRY(lx::replay_launch(R, 0, true, w, n, t1 + batch * ld, ld, batch, s), "replay");
+        LX_TRY(lx::replay_launch(R, 1, true, t1, ld, t2, ld, 2 * batch, s), "replay");
+        LX_TRY(lx::replay_launch(R, 2, true, t2, ld, t1, ld, 2 * batch, s), "replay");
+        LX_TRY(lx::replay_launch(R, 3, true, t1, ld, t2, ld, 2 * batch, s), "replay");
+        A.random = false;
+        A.us = t2;
+        A.ws = t2 + batch * ld;
+        int64_t row = 0;
+        float* user[4] = {dx, da, dphi, dpsi};
+        int64_t first[4], count[4];
+        for (int o = 0; o < 4; ++o) {
+            count[o] = user[o] ? (o == 0 ? batch : 1) : 0;
+            first[o] = row;
+            row += count[o];
+        }
+        A.dx = dx ? t1 + first[0] * ld : nullptr;
+        A.da = da ? t1 + first[1] * ld : nullptr;
+        A.dphi = dphi ? t1 + first[2] * ld : nullptr;
+        A.dpsi = dpsi ? t1 + first[3] * ld : nullptr;
+        LX_TRY(lx::grad_sym_launch(A, s), "symmetric gradient");
+        LX_TRY(lx::replay_launch(R, 3, false, t1, ld, t2, ld, nout, s), "replay");
+        LX_TRY(lx::replay_launch(R, 2, false, t2, ld, t1, ld, nout, s), "replay");
+        LX_TRY(lx::replay_launch(R, 1, false, t1, ld, t2, ld, nout, s), "replay");
+        for (int o = 0; o < 4; ++o)
+            if (count[o])
+                LX_TRY(lx::replay_launch(R, 0, false, t2 + first[o] * ld, ld, user[o], n, count[o], s), "replay");
+        return LAPLEX_OK;
+    }
+
+    // General plan: outputs on a from the tables of b, outputs on b from those of a.
+    LX_TRY(ensure_perm(p, 0, s), "permutation of a");
+    LX_TRY(ensure_perm(p, 1, s), "permutation of b");
+    GradSide on_a{p->n, p->k, p->sb, p->pb, p->cpsi, p->spsi, p->a0, p->cphi0, p->sphi0};
+    GradSide on_b{p->k, p->n, p->sa, p->pa, p->cphi, p->sphi, p->b0, p->cpsi0, p->spsi0};
+    laplex_status st = grad_general_side(p, on_a, w, u, batch, transpose ? dx : nullptr, da, dphi, s);
+    if (st != LAPLEX_OK) return st;
+    return grad_general_side(p, on_b, u, w, batch, transpose ? nullptr : dx, db, dpsi, s);
+}
+
 laplex_status laplex_gram(laplex_plan p, const float* D, float* M, void* stream)
 {
     if (!p) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "plan is NULL");
@@ -688,6 +903,7 @@ laplex_status laplex_gram(laplex_plan p, const float* D, float* M, void* stream)
     lx::GramArgs G;
     G.n = p->n;
     G.k = p->k;
+    G.inv_t = p->inv_t;
     G.sa = p->sa;
     G.pa = p->pa;
     G.sb = p->sb;

@@ -33,22 +33,6 @@ namespace lx {
 
 constexpr int kGenThreads = 1024;
 
-// #{r : s[r] < q} by bisection.
-__device__ __forceinline__ int64_t lower_bound_f(const float* __restrict__ s, int64_t n, float q)
-{
-    int64_t lo = 0, hi = n;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (s[mid] < q) lo = mid + 1;
-        else hi = mid;
-    }
-    return lo;
-}
-
-__device__ __forceinline__ float decay_f(float lo, float hi) { return expf(lo - hi); }
-
-__host__ __device__ inline int64_t pad64(int64_t x) { return (x + 63) & ~(int64_t)63; }
-
 // ------------------------------------------------------------- bucketing
 
 // Sorted bucketing for a small sorted output side (n_out <= 1024).  A
@@ -113,8 +97,8 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, in
             if (idx[j] < j1) {
                 const float q = A.in_anchor[idx[j]];
                 t = (uint32_t)lower_bound_f(so, no, q);
-                al = t < (uint32_t)no ? decay_f(q, so[t]) : 0.f;
-                be = t > 0 ? decay_f(so[t - 1], q) : 0.f;
+                al = t < (uint32_t)no ? decay_f(q, so[t], A.inv_t) : 0.f;
+                be = t > 0 ? decay_f(so[t - 1], q, A.inv_t) : 0.f;
                 if (C == 2) {
                     f0 = A.in_cos[idx[j]];
                     f1 = A.in_sin[idx[j]];
@@ -246,8 +230,8 @@ __global__ __launch_bounds__(256) void lx_bucket_global(BucketArgs A)
     for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < A.n_in; j += stride) {
         const float q = A.in_anchor[j];
         const int64_t t = lower_bound_f(A.s_out, no, q);
-        const float al = t < no ? decay_f(q, A.s_out[t]) : 0.f;
-        const float be = t > 0 ? decay_f(A.s_out[t - 1], q) : 0.f;
+        const float al = t < no ? decay_f(q, A.s_out[t], A.inv_t) : 0.f;
+        const float be = t > 0 ? decay_f(A.s_out[t - 1], q, A.inv_t) : 0.f;
         float f[C];
         f[0] = C == 2 ? A.in_cos[j] : 1.f;
         if (C == 2) f[C - 1] = A.in_sin[j];
@@ -377,8 +361,8 @@ __global__ __launch_bounds__(kGenThreads) void lx_eval(EvalArgs A, int VG, int g
     for (int64_t i = i0 + threadIdx.x; i < i1; i += kGenThreads) {
         const float o = A.out_anchor[i];
         const int64_t t = lower_bound_f(si, ni, o);
-        const float al = t > 0 ? decay_f(si[t - 1], o) : 0.f;
-        const float be = t < ni ? decay_f(o, si[t]) : 0.f;
+        const float al = t > 0 ? decay_f(si[t - 1], o, A.inv_t) : 0.f;
+        const float be = t < ni ? decay_f(o, si[t], A.inv_t) : 0.f;
         float gc[C];
         gc[0] = C == 2 ? A.out_cos[i] : 1.f;
         if (C == 2) gc[C - 1] = A.out_sin[i];

@@ -1,0 +1,449 @@
+// Gradients of a LAPLEX product: with respect to the input vector, the
+// anchors and the phases (gfx950).
+//
+// "LAPLEX: The FFT of Learnable Laplace Kernels", technical summary §2.1: the
+// operator is a trainable layer whose parameters are its anchors (and
+// phases).  For the bilinear form F = sum_v <u_v, K w_v> (u on the row side,
+// w on the column side; a training step through y = K x has u = dL/dy,
+// w = x, and through y = K^T x has u = x, w = dL/dy) the entrywise
+// derivatives of K_ij = exp(-|a_i - b_j| / t) cos(phi_i - psi_j) give
+//   dF/da_i   = -(1/t) sum_v u_vi (S w_v)_i,   S_ij = sgn(a_i - b_j) K_ij,
+//   dF/dphi_i = -sum_v u_vi (Q w_v)_i,          Q_ij = e_ij sin(phi_i - psi_j),
+// and for the column side the same with the roles of the sides swapped
+// (sgn(b_j - a_i), sin(psi_j - phi_i), weights w, inputs u).  sgn(0) = 0:
+// equal anchors contribute nothing (the mean of the one-sided slopes).
+// With the cos/sin split both products are sums of the unphased plain and
+// signed products of the two channels (inputs times cos, sin of the input
+// phases):
+//   S w = c_out S0(c_in w) + s_out S0(s_in w),  Q w = s_out K0(c_in w) - c_out K0(s_in w),
+// and the plain product c_out K0(c_in w) + s_out K0(s_in w) is the input
+// gradient of the other side.
+//
+// Symmetric plans work by rank along the sorted anchors.  With L, U the
+// inclusive prefix/suffix recurrences of the forward product and Tp, Ts the
+// inclusive prefix/suffix sums inside runs of equal anchors (a recurrence
+// whose multiplier is 1 between equal neighbours and 0 otherwise),
+//   K0 = L + U - x,   S0 = (L - Tp) - (U - Ts),
+// since L - Tp keeps exactly the strictly smaller anchors.  Two halves: half
+// 0 takes w with the column phases as input and u as weight (row side: da,
+// dphi, and the plain product K w); half 1 takes u with the row phases and w
+// as weight (column side of the same anchors: da again, dpsi, K^T u).  Same
+// reduce / carry / apply structure as the forward scans; the apply loops
+// over the vectors of a tile so the batch sums stay in registers.
+//
+// General plans (a != b) evaluate each side's outputs in their original
+// order from the inclusive prefix/suffix tables of the other side (the
+// "evaluate" form of the forward product): with t< = #{s < o} and
+// t<= = #{s <= o} in the sorted input side,
+//   K0 = e(o - s_{t<-1}) PL_{t<-1} + e(s_{t<} - o) PR_{t<},
+//   S0 = e(o - s_{t<-1}) PL_{t<-1} - e(s_{t<=} - o) PR_{t<=}.
+#include "lx_device.h"
+#include "lx_internal.h"
+#include "lx_tile.h"
+
+namespace lx {
+
+// ------------------------------------------------------------ symmetric
+
+// Tiles of kScanTile ranks like the forward scans, 8 ranks per thread (the
+// gradient keeps four running sums per channel per rank).
+constexpr int kGradThreads = 512;
+constexpr int kGradItems = 8;
+constexpr int kGradWaves = kGradThreads / kWave;
+static_assert(kGradThreads * kGradItems == kScanTile, "gradient tile size");
+
+__device__ __forceinline__ int64_t grad_row(int C, int h, int c, int kind, int64_t batch, int64_t vec)
+{
+    return ((int64_t)((h * C + c) * 2 + kind)) * batch + vec;
+}
+
+// Values of both inputs for this thread's ranks: u (row side) and w (column
+// side) by rank; in random mode gathered through perm and stored by rank.
+template <bool RANDOM>
+__device__ __forceinline__ void grad_load_uw(const GradSymArgs& A, int64_t vec, int64_t r0, float (&uu)[kGradItems],
+                                             float (&ww)[kGradItems])
+{
+    const int64_t n = A.n;
+    if (RANDOM) {
+        uint32_t idx[kGradItems];
+        load_run<kGradItems>(A.perm, r0, n, idx);
+        const float* up = A.u + vec * n;
+        const float* wp = A.w + vec * n;
+#pragma unroll
+        for (int i = 0; i < kGradItems; ++i) {
+            uu[i] = (r0 + i < n) ? up[idx[i]] : 0.f;
+            ww[i] = (r0 + i < n) ? wp[idx[i]] : 0.f;
+        }
+    } else {
+        load_run<kGradItems>(A.us + vec * A.ld, r0, n, uu);
+        load_run<kGradItems>(A.ws + vec * A.ld, r0, n, ww);
+    }
+}
+
+template <int C, bool RANDOM>
+__global__ __launch_bounds__(kGradThreads) void lx_grad_sym_reduce(GradSymArgs A)
+{
+    __shared__ Aff<double> sh[kGradWaves];
+    const int64_t vec = blockIdx.x / A.tiles;
+    const int64_t tile = blockIdx.x - vec * A.tiles;
+    const int64_t n = A.n;
+    const int64_t r0 = tile * kScanTile + (int64_t)threadIdx.x * kGradItems;
+
+    double e[kGradItems + 1];
+    uint32_t ties;
+    load_decays_ties<kGradItems>(A.s, r0, n, A.inv_t, e, ties);
+    float uu[kGradItems], ww[kGradItems];
+    grad_load_uw<RANDOM>(A, vec, r0, uu, ww);
+    if (RANDOM) {
+        store_run<kGradItems>(A.us + vec * A.ld, r0, n, uu);
+        store_run<kGradItems>(A.ws + vec * A.ld, r0, n, ww);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float fc[kGradItems], fs[kGradItems];
+        if (C == 2) {
+            load_run<kGradItems>(h == 0 ? A.cpsi : A.cphi, r0, n, fc);
+            load_run<kGradItems>(h == 0 ? A.spsi : A.sphi, r0, n, fs);
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            float val[kGradItems];
+#pragma unroll
+            for (int i = 0; i < kGradItems; ++i) {
+                const float in = h == 0 ? ww[i] : uu[i];
+                val[i] = C == 2 ? (c == 0 ? fc[i] : fs[i]) * in : in;
+            }
+#pragma unroll
+            for (int kind = 0; kind < 2; ++kind) {
+                Aff<double> f = aff_identity<double>(), b = aff_identity<double>();
+#pragma unroll
+                for (int i = 0; i < kGradItems; ++i)
+                    f = compose(f, Aff<double>{kind == 0 ? e[i] : tie_mult(ties, i), (double)val[i]});
+#pragma unroll
+                for (int i = kGradItems - 1; i >= 0; --i)
+                    b = compose(b, Aff<double>{kind == 0 ? e[i + 1] : tie_mult(ties, i + 1), (double)val[i]});
+                Aff<double> ft, bt;
+                (void)block_exscan_up<double, kGradWaves>(f, sh, ft);
+                (void)block_exscan_down<double, kGradWaves>(b, sh, bt);
+                if (threadIdx.x == 0) {
+                    double* ag = A.agg + (grad_row(C, h, c, kind, A.batch, vec) * A.tiles + tile) * 4;
+                    ag[0] = ft.m;
+                    ag[1] = ft.v;
+                    ag[2] = bt.m;
+                    ag[3] = bt.v;
+                }
+            }
+        }
+    }
+}
+
+// One half of the symmetric gradient for one vector: for each channel the
+// decay scan (L forward, U backward) and the tie scan (Tp, Ts) over this
+// thread's ranks, entered from the carries, combined on the way back into
+//   K0 = L + U - x  and  S0 = (L - Tp) - (U - Ts),
+// and folded into the batch sums (anchor, phase) and the plain product.
+// One per-anchor result: through perm into original order, or by rank;
+// ADD accumulates into what is there (the second half of the anchor sum).
+template <bool RANDOM, bool ADD>
+__device__ __forceinline__ void grad_store_out(const GradSymArgs& A, float* dst, int64_t r0,
+                                               const float (&val)[kGradItems])
+{
+    if (!dst) return;
+    const int64_t n = A.n;
+    if (RANDOM) {
+        uint32_t idx[kGradItems];
+        load_run<kGradItems>(A.perm, r0, n, idx);
+#pragma unroll
+        for (int i = 0; i < kGradItems; ++i)
+            if (r0 + i < n) dst[idx[i]] = ADD ? dst[idx[i]] + val[i] : val[i];
+    } else {
+        float v[kGradItems];
+        if (ADD) {
+            load_run<kGradItems>(dst, r0, n, v);
+#pragma unroll
+            for (int i = 0; i < kGradItems; ++i) v[i] += val[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < kGradItems; ++i) v[i] = val[i];
+        }
+        store_run<kGradItems>(dst, r0, n, v);
+    }
+}
+
+// Half H of the symmetric gradient over one tile (one launch per half; the
+// second adds its anchor part to the first's).  For every vector and channel:
+// the decay scan (L forward, U backward) and the tie scan (Tp, Ts) over this
+// thread's ranks, entered from the carries, combined on the way back into
+//   K0 = L + U - x  and  S0 = (L - Tp) - (U - Ts),
+// and folded into the batch sums (anchor, phase) and the plain product.
+// Vectors and channels run in a loop that is not unrolled, and the decays
+// and tie masks are re-read from LDS in it, which keeps one step's state
+// live at a time.
+template <int C, bool RANDOM, int H>
+__global__ __launch_bounds__(kGradThreads) void lx_grad_sym_apply(GradSymArgs A)
+{
+    __shared__ Aff<double> sh[kGradWaves];
+    __shared__ double se[kScanTile + 1];
+    __shared__ uint32_t st[kGradThreads];
+    const int64_t tile = blockIdx.x;
+    const int64_t n = A.n;
+    const int64_t r0 = tile * kScanTile + (int64_t)threadIdx.x * kGradItems;
+    {
+        double e[kGradItems + 1];
+        uint32_t ties;
+        load_decays_ties<kGradItems>(A.s, r0, n, A.inv_t, e, ties);
+#pragma unroll
+        for (int i = 0; i < kGradItems; ++i) se[threadIdx.x * kGradItems + i] = e[i];
+        if (threadIdx.x == kGradThreads - 1) se[kScanTile] = e[kGradItems];
+        st[threadIdx.x] = ties;
+    }
+    __syncthreads();
+    // half 0: input w with the column phases, weight u, output phases phi;
+    // half 1: input u with the row phases, weight w, output phases psi
+    const float* in_v = H == 0 ? A.ws : A.us;
+    const float* wt_v = H == 0 ? A.us : A.ws;
+    const float* icos = H == 0 ? A.cpsi : A.cphi;
+    const float* isin = H == 0 ? A.spsi : A.sphi;
+    const float* ocos = H == 0 ? A.cphi : A.cpsi;
+    const float* osin = H == 0 ? A.sphi : A.spsi;
+    const bool want_dx = A.dx != nullptr && A.dx_half == H;
+    float g_a[kGradItems], g_p[kGradItems];
+#pragma unroll
+    for (int i = 0; i < kGradItems; ++i) g_a[i] = g_p[i] = 0.f;
+
+#pragma unroll 1
+    for (int64_t vec = 0; vec < A.batch; ++vec) {
+        float dxo[kGradItems];
+#pragma unroll
+        for (int i = 0; i < kGradItems; ++i) dxo[i] = 0.f;
+#pragma unroll 1
+        for (int c = 0; c < C; ++c) {
+            double e[kGradItems + 1];
+#pragma unroll
+            for (int i = 0; i <= kGradItems; ++i) e[i] = se[threadIdx.x * kGradItems + i];
+            const uint32_t ties = st[threadIdx.x];
+            float val[kGradItems], wt[kGradItems], fo[kGradItems], fk[kGradItems];
+            load_run<kGradItems>(in_v + vec * A.ld, r0, n, val);
+            load_run<kGradItems>(wt_v + vec * A.ld, r0, n, wt);
+            if (C == 2) {
+                float fi[kGradItems];
+                load_run<kGradItems>(c == 0 ? icos : isin, r0, n, fi);
+                load_run<kGradItems>(c == 0 ? ocos : osin, r0, n, fo);
+                load_run<kGradItems>(c == 0 ? osin : ocos, r0, n, fk);
+                const float sg = c == 0 ? 1.f : -1.f;  // sine product: s_out K0_c - c_out K0_s
+#pragma unroll
+                for (int i = 0; i < kGradItems; ++i) {
+                    val[i] *= fi[i];
+                    fk[i] *= sg;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kGradItems; ++i) fo[i] = fk[i] = 1.f;
+            }
+            Aff<double> fd = aff_identity<double>(), bd = aff_identity<double>();
+            Aff<double> ft = aff_identity<double>(), bt = aff_identity<double>();
+#pragma unroll
+            for (int i = 0; i < kGradItems; ++i) {
+                fd = compose(fd, Aff<double>{e[i], (double)val[i]});
+                ft = compose(ft, Aff<double>{tie_mult(ties, i), (double)val[i]});
+            }
+#pragma unroll
+            for (int i = kGradItems - 1; i >= 0; --i) {
+                bd = compose(bd, Aff<double>{e[i + 1], (double)val[i]});
+                bt = compose(bt, Aff<double>{tie_mult(ties, i + 1), (double)val[i]});
+            }
+            Aff<double> tot;
+            const Aff<double> fxd = block_exscan_up<double, kGradWaves>(fd, sh, tot);
+            const Aff<double> bxd = block_exscan_down<double, kGradWaves>(bd, sh, tot);
+            const Aff<double> fxt = block_exscan_up<double, kGradWaves>(ft, sh, tot);
+            const Aff<double> bxt = block_exscan_down<double, kGradWaves>(bt, sh, tot);
+            const double* cd = A.carry + (grad_row(C, H, c, 0, A.batch, vec) * A.tiles + tile) * 2;
+            const double* ct = A.carry + (grad_row(C, H, c, 1, A.batch, vec) * A.tiles + tile) * 2;
+            double L = fxd.m * cd[0] + fxd.v;
+            double T = fxt.m * ct[0] + fxt.v;
+            double Lr[kGradItems], Sr[kGradItems];  // L and L - Tp by rank
+#pragma unroll
+            for (int i = 0; i < kGradItems; ++i) {
+                L = e[i] * L + (double)val[i];
+                T = tie_mult(ties, i) * T + (double)val[i];
+                Lr[i] = L;
+                Sr[i] = L - T;
+            }
+            double U = bxd.m * cd[1] + bxd.v;
+            double Tb = bxt.m * ct[1] + bxt.v;
+#pragma unroll
+            for (int i = kGradItems - 1; i >= 0; --i) {
+                U = e[i + 1] * U + (double)val[i];
+                Tb = tie_mult(ties, i + 1) * Tb + (double)val[i];
+                const float k0 = (float)(Lr[i] + U - (double)val[i]);
+                const float s0 = (float)(Sr[i] - (U - Tb));
+                g_a[i] = fmaf(A.anchor_scale * wt[i] * fo[i], s0, g_a[i]);
+                if (C == 2) g_p[i] = fmaf(-wt[i] * fk[i], k0, g_p[i]);
+                dxo[i] = fmaf(fo[i], k0, dxo[i]);
+            }
+        }
+        if (want_dx) {
+            if (RANDOM) {
+                uint32_t idx[kGradItems];
+                load_run<kGradItems>(A.perm, r0, n, idx);
+                float* dv = A.dx + vec * n;
+#pragma unroll
+                for (int i = 0; i < kGradItems; ++i)
+                    if (r0 + i < n) dv[idx[i]] = dxo[i];
+            } else {
+                store_run<kGradItems>(A.dx + vec * A.out_ld, r0, n, dxo);
+            }
+        }
+    }
+    grad_store_out<RANDOM, H == 1>(A, A.da, r0, g_a);
+    if (C == 2) grad_store_out<RANDOM, false>(A, H == 0 ? A.dphi : A.dpsi, r0, g_p);
+}
+
+size_t grad_sym_scratch_doubles(int64_t n, int64_t batch, int channels)
+{
+    const int64_t tiles = (n + kScanTile - 1) / kScanTile;
+    const int64_t groups = (tiles + kCarryGroup - 1) / kCarryGroup;
+    const int64_t rows = 4 * (int64_t)channels * batch;
+    return (size_t)(rows * (tiles * 4 + groups * 4 + tiles * 2));
+}
+
+template <int C, bool RANDOM>
+static hipError_t grad_sym_launch_t(const GradSymArgs& a, hipStream_t s)
+{
+    LX_LAUNCH("grad_reduce", s, (lx_grad_sym_reduce<C, RANDOM><<<(unsigned)(a.tiles * a.batch), kGradThreads, 0, s>>>(a)));
+    const hipError_t e = scan_carry_launch(a.agg, a.gagg, a.carry, a.tiles, 4 * (int64_t)C * a.batch, s);
+    if (e != hipSuccess) return e;
+    LX_LAUNCH("grad_apply", s, (lx_grad_sym_apply<C, RANDOM, 0><<<(unsigned)a.tiles, kGradThreads, 0, s>>>(a)));
+    LX_LAUNCH("grad_apply", s, (lx_grad_sym_apply<C, RANDOM, 1><<<(unsigned)a.tiles, kGradThreads, 0, s>>>(a)));
+    return hipSuccess;
+}
+
+hipError_t grad_sym_launch(const GradSymArgs& a, hipStream_t s)
+{
+    if (a.n <= 0 || a.batch <= 0) return hipSuccess;
+    if (a.tiles * a.batch > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    if (a.channels == 2) return a.random ? grad_sym_launch_t<2, true>(a, s) : grad_sym_launch_t<2, false>(a, s);
+    return a.random ? grad_sym_launch_t<1, true>(a, s) : grad_sym_launch_t<1, false>(a, s);
+}
+
+// -------------------------------------------------------------- general
+
+constexpr int kEvalThreads = 1024;
+
+template <int C, bool USE_LDS>
+__global__ __launch_bounds__(kEvalThreads) void lx_eval_grad(EvalGradArgs A, int VG, int64_t chunk_len)
+{
+    extern __shared__ float lds[];
+    const int64_t ni = A.n_in;
+    const int64_t i0 = blockIdx.x * chunk_len;
+    int64_t i1 = i0 + chunk_len;
+    if (i1 > A.n_out) i1 = A.n_out;
+    const float* si = A.s_in;
+    float* tl = nullptr;  // [ni][VG][C]
+    float* tr = nullptr;
+    if (USE_LDS) {
+        float* s_l = lds;
+        tl = lds + pad64(ni);
+        tr = tl + ni * VG * C;
+        for (int64_t i = threadIdx.x; i < ni; i += kEvalThreads) s_l[i] = A.s_in[i];
+        si = s_l;
+    }
+    const int groups = (int)((A.batch + VG - 1) / VG);
+    for (int g = 0; g < groups; ++g) {
+        const int64_t v0 = (int64_t)g * VG;
+        const int nv = (int)((A.batch - v0) < VG ? (A.batch - v0) : VG);
+        if (USE_LDS) {
+            __syncthreads();  // previous group's readers are done
+            for (int64_t i = threadIdx.x; i < ni * VG * C; i += kEvalThreads) {
+                const int64_t t = i / (VG * C);
+                const int64_t rem = i - t * (VG * C);
+                const int64_t vi = rem / C;
+                const int64_t c = rem - vi * C;
+                const int64_t src = (c * A.batch + v0 + vi) * A.ld + t;
+                tl[i] = vi < nv ? A.pl[src] : 0.f;
+                tr[i] = vi < nv ? A.pr[src] : 0.f;
+            }
+            __syncthreads();
+        }
+        for (int64_t i = i0 + threadIdx.x; i < i1; i += kEvalThreads) {
+            const float o = A.out_anchor[i];
+            const int64_t tlt = lower_bound_f(si, ni, o);
+            const int64_t tle = upper_bound_f(si, ni, o, tlt);
+            const float al = tlt > 0 ? decay_f(si[tlt - 1], o, A.inv_t) : 0.f;
+            const float be = tlt < ni ? decay_f(o, si[tlt], A.inv_t) : 0.f;
+            const float be2 = tle < ni ? decay_f(o, si[tle], A.inv_t) : 0.f;
+            float oc = 1.f, os = 0.f;
+            if (C == 2) {
+                oc = A.out_cos[i];
+                os = A.out_sin[i];
+            }
+            float acc_a = 0.f, acc_p = 0.f;
+            for (int vi = 0; vi < nv; ++vi) {
+                float sig = 0.f, kin = 0.f, pla = 0.f;
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    float lv = 0.f, rv = 0.f, rv2 = 0.f;
+                    if (USE_LDS) {
+                        if (tlt > 0) lv = tl[((tlt - 1) * VG + vi) * C + c];
+                        if (tlt < ni) rv = tr[(tlt * VG + vi) * C + c];
+                        if (tle < ni) rv2 = tr[(tle * VG + vi) * C + c];
+                    } else {
+                        const int64_t row = ((int64_t)c * A.batch + v0 + vi) * A.ld;
+                        if (tlt > 0) lv = A.pl[row + tlt - 1];
+                        if (tlt < ni) rv = A.pr[row + tlt];
+                        if (tle < ni) rv2 = A.pr[row + tle];
+                    }
+                    const float k0 = fmaf(al, lv, be * rv);
+                    const float s0 = fmaf(al, lv, -be2 * rv2);
+                    const float fo = c == 0 ? oc : os;
+                    sig = fmaf(fo, s0, sig);
+                    pla = fmaf(fo, k0, pla);
+                    if (C == 2) kin = fmaf(c == 0 ? os : -oc, k0, kin);
+                }
+                const float wt = A.w[(v0 + vi) * A.n_out + i];
+                acc_a = fmaf(wt, sig, acc_a);
+                acc_p = fmaf(-wt, kin, acc_p);
+                if (A.y) A.y[(v0 + vi) * A.n_out + i] = pla;
+            }
+            // this thread owns output i in every group: accumulate in place
+            if (A.d_anchor) A.d_anchor[i] = (g == 0 ? 0.f : A.d_anchor[i]) + A.anchor_scale * acc_a;
+            if (C == 2 && A.d_phase) A.d_phase[i] = (g == 0 ? 0.f : A.d_phase[i]) + acc_p;
+        }
+    }
+}
+
+hipError_t eval_grad_launch(const EvalGradArgs& a, hipStream_t s)
+{
+    if (a.n_out <= 0 || a.batch <= 0) return hipSuccess;
+    const int64_t lds_floats = a.lds_bytes / 4;
+    int64_t vg = (lds_floats - pad64(a.n_in)) / (2 * (int64_t)a.channels * (a.n_in > 0 ? a.n_in : 1));
+    if (vg > 16) vg = 16;
+    if (vg > a.batch) vg = a.batch;
+    const bool use_lds = a.lds_bytes > 0 && vg >= 1;
+    if (!use_lds) vg = a.batch < 16 ? a.batch : 16;
+    int64_t chunks = (a.n_out + 16383) / 16384;
+    if (chunks > 4096) chunks = 4096;
+    if (chunks < 1) chunks = 1;
+    const int64_t chunk_len = (a.n_out + chunks - 1) / chunks;
+    chunks = (a.n_out + chunk_len - 1) / chunk_len;
+    const size_t shmem = use_lds ? (size_t)(pad64(a.n_in) + 2 * vg * a.channels * a.n_in) * 4 : 0;
+    const int v = (int)vg;
+#define LX_EVG(CC, LL)                                                                                   \
+    do {                                                                                                 \
+        if (LL) (void)hipFuncSetAttribute((const void*)lx_eval_grad<CC, LL>,                             \
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);       \
+        LX_LAUNCH("eval_grad", s,                                                                        \
+                  (lx_eval_grad<CC, LL><<<(unsigned)chunks, kEvalThreads, shmem, s>>>(a, v, chunk_len))); \
+    } while (0)
+    if (a.channels == 2) {
+        if (use_lds) LX_EVG(2, true);
+        else LX_EVG(2, false);
+    } else {
+        if (use_lds) LX_EVG(1, true);
+        else LX_EVG(1, false);
+    }
+#undef LX_EVG
+    return hipSuccess;
+}
+
+}  // namespace lx

@@ -7,7 +7,8 @@
 //   b <= s_r       : D e^{-(s_r-b)} e^{-(s_c-b)} = e^{-(s_c-s_r)} D e^{-2(s_r-b)}
 //   s_r < b <= s_c : D e^{-(b-s_r)} e^{-(s_c-b)} = e^{-(s_c-s_r)} D
 //   b > s_c        : D e^{-(b-s_r)} e^{-(b-s_c)} = e^{-(s_c-s_r)} D e^{-2(b-s_c)}
-// so M_rc = e^{-(s_c - s_r)} (P_r + (S_c - S_r) + Q_c) with
+// so M_rc = e^{-(s_c - s_r)} (P_r + (S_c - S_r) + Q_c) with (at temperature t
+// every exponent divided by t)
 //   S_r = sum of D over b <= s_r,
 //   P_r = sum over b <= s_r of D e^{-2(s_r - b)},
 //   Q_c = sum over b >  s_c of D e^{-2(b - s_c)}.
@@ -35,18 +36,6 @@ namespace lx {
 constexpr int kBinThreads = 256;
 constexpr int kGramScanThreads = 1024;
 constexpr int kGT = 64;  // tile edge
-
-// #{j : s[j] <= q}
-__device__ __forceinline__ int64_t upper_bound_f(const float* __restrict__ s, int64_t n, float q)
-{
-    int64_t lo = 0, hi = n;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (s[mid] <= q) lo = mid + 1;
-        else hi = mid;
-    }
-    return lo;
-}
 
 __device__ __forceinline__ double block_sum_d(double x, double* sh)
 {
@@ -97,8 +86,8 @@ __global__ __launch_bounds__(kBinThreads) void lx_gram_bins(GramArgs A, double* 
             wt[0] = d;
         }
         const double b = (double)A.sb[j];
-        const double er = r < n ? exp(-2.0 * (right - b)) : 0.0;
-        const double el = r > 0 ? exp(-2.0 * (b - left)) : 0.0;
+        const double er = r < n ? decay_dist(2.0 * (right - b), A.inv_t) : 0.0;
+        const double el = r > 0 ? decay_dist(2.0 * (b - left), A.inv_t) : 0.0;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             sg[w] += wt[w];
@@ -150,7 +139,7 @@ __global__ __launch_bounds__(kGramScanThreads) void lx_gram_scan(GramArgs A, con
         // forward: S (multiplier 1) and P (multiplier e^{-2 gap}); rank 0 starts both
         Aff<double> S = aff_identity<double>(), P = aff_identity<double>();
         for (int64_t r = r0; r < r1; ++r) {
-            const double m = r > 0 ? exp(-2.0 * ((double)s[r] - (double)s[r - 1])) : 0.0;
+            const double m = r > 0 ? decay_dist(2.0 * ((double)s[r] - (double)s[r - 1]), A.inv_t) : 0.0;
             S = compose(S, Aff<double>{1.0, sg[r]});
             P = compose(P, Aff<double>{m, pw[r]});
         }
@@ -158,7 +147,7 @@ __global__ __launch_bounds__(kGramScanThreads) void lx_gram_scan(GramArgs A, con
         double runS = block_exscan_up<double, kGramScanThreads / kWave>(S, sh, tot).v;
         double runP = block_exscan_up<double, kGramScanThreads / kWave>(P, sh, tot).v;
         for (int64_t r = r0; r < r1; ++r) {
-            const double m = r > 0 ? exp(-2.0 * ((double)s[r] - (double)s[r - 1])) : 0.0;
+            const double m = r > 0 ? decay_dist(2.0 * ((double)s[r] - (double)s[r - 1]), A.inv_t) : 0.0;
             runS += sg[r];
             runP = m * runP + pw[r];
             double* o = st + (int64_t)A.pa[r] * SW + 1 + 3 * w;
@@ -167,12 +156,12 @@ __global__ __launch_bounds__(kGramScanThreads) void lx_gram_scan(GramArgs A, con
         }
         Aff<double> Q = aff_identity<double>();
         for (int64_t r = r1 - 1; r >= r0; --r) {
-            const double m = r + 1 < n ? exp(-2.0 * ((double)s[r + 1] - (double)s[r])) : 0.0;
+            const double m = r + 1 < n ? decay_dist(2.0 * ((double)s[r + 1] - (double)s[r]), A.inv_t) : 0.0;
             Q = compose(Q, Aff<double>{m, qw[r]});
         }
         double runQ = block_exscan_down<double, kGramScanThreads / kWave>(Q, sh, tot).v;
         for (int64_t r = r1 - 1; r >= r0; --r) {
-            const double m = r + 1 < n ? exp(-2.0 * ((double)s[r + 1] - (double)s[r])) : 0.0;
+            const double m = r + 1 < n ? decay_dist(2.0 * ((double)s[r + 1] - (double)s[r]), A.inv_t) : 0.0;
             runQ = m * runQ + qw[r];
             st[(int64_t)A.pa[r] * SW + 3 + 3 * w] = runQ;
         }
@@ -180,7 +169,7 @@ __global__ __launch_bounds__(kGramScanThreads) void lx_gram_scan(GramArgs A, con
 }
 
 template <int NW>
-__global__ __launch_bounds__(256) void lx_gram_tile(const double* __restrict__ st, int64_t n,
+__global__ __launch_bounds__(256) void lx_gram_tile(const double* __restrict__ st, int64_t n, double inv_t,
                                                    float* __restrict__ M)
 {
     constexpr int SW = gram_stride<NW>();
@@ -213,7 +202,7 @@ __global__ __launch_bounds__(256) void lx_gram_tile(const double* __restrict__ s
             } else {
                 val = g[0];
             }
-            M[i * n + j] = (float)(exp(lo[0] - hi[0]) * val);
+            M[i * n + j] = (float)(decay_dist(hi[0] - lo[0], inv_t) * val);
         }
     }
 }
@@ -235,7 +224,7 @@ static hipError_t gram_launch_t(const GramArgs& a, hipStream_t s)
     LX_LAUNCH("gram_bins", s, (lx_gram_bins<NW><<<(unsigned)(n + 1), kBinThreads, 0, s>>>(a, sigma, p, q)));
     LX_LAUNCH("gram_scan", s, (lx_gram_scan<NW><<<1, kGramScanThreads, 0, s>>>(a, sigma, p, q, st)));
     const unsigned nb = (unsigned)((n + kGT - 1) / kGT);
-    LX_LAUNCH("gram_tile", s, (lx_gram_tile<NW><<<dim3(nb, nb), 256, 0, s>>>(st, n, a.M)));
+    LX_LAUNCH("gram_tile", s, (lx_gram_tile<NW><<<dim3(nb, nb), 256, 0, s>>>(st, n, a.inv_t, a.M)));
     return hipSuccess;
 }
 

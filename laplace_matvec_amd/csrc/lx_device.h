@@ -187,14 +187,53 @@ __device__ __forceinline__ uint32_t block_exsum_u32(uint32_t x, uint32_t* sh, ui
     return pre + inc - x;
 }
 
-// Decay factor exp(-(hi - lo)) between two float32 anchors, in float64.
-// The difference of two float32 values is exact in float64, and float64
-// factors keep long chains of equal gaps (common where many anchors sit on
-// one float32 grid) free of the bias a repeated float32 rounding of
-// exp(-gap) would accumulate.
-__device__ __forceinline__ double decay(float lo, float hi)
+// Decay factor exp(-(hi - lo) / t) between two float32 anchors lo <= hi, in
+// float64, with inv_t = 1 / t (+inf at temperature 0, where equal anchors
+// give 1 and all others 0).  The difference of two float32 values is exact
+// in float64, and float64 factors keep long chains of equal gaps (common
+// where many anchors sit on one float32 grid) free of the bias a repeated
+// float32 rounding of exp(-gap) would accumulate.
+__device__ __forceinline__ double decay(float lo, float hi, double inv_t)
 {
-    return exp((double)lo - (double)hi);
+    return lo == hi ? 1.0 : exp(((double)lo - (double)hi) * inv_t);
+}
+
+// exp(-(hi - lo) / t) in float32 for anchors lo <= hi, it = 1 / t.
+__device__ __forceinline__ float decay_f(float lo, float hi, float it)
+{
+    return lo == hi ? 1.f : expf((lo - hi) * it);
+}
+
+// #{r : s[r] < q} by bisection.
+__device__ __forceinline__ int64_t lower_bound_f(const float* __restrict__ s, int64_t n, float q)
+{
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (s[mid] < q) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// #{r : s[r] <= q} by bisection, searching [lo, n) only (s[0..lo) <= q known).
+__device__ __forceinline__ int64_t upper_bound_f(const float* __restrict__ s, int64_t n, float q, int64_t lo = 0)
+{
+    int64_t hi = n;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (s[mid] <= q) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+__host__ __device__ inline int64_t pad64(int64_t x) { return (x + 63) & ~(int64_t)63; }
+
+// exp(-d / t) for a distance d >= 0 (1 at d == 0, also at t = 0).
+__device__ __forceinline__ double decay_dist(double d, double inv_t)
+{
+    return d == 0.0 ? 1.0 : exp(-d * inv_t);
 }
 
 }  // namespace lx

@@ -82,6 +82,7 @@ struct ScanArgs {
     int64_t tiles = 0;         // ceil(n / kScanTile)
     int64_t batch = 0;         // vectors
     int64_t ld = 0;            // row stride of the internal [channels][batch][ld] buffers
+    double inv_t = 1.0;        // 1 / temperature (+inf: equality routing)
     const float* s = nullptr;  // sorted anchors [n]
     const uint32_t* perm = nullptr;  // rank -> original index [n]
     const float* x = nullptr;        // random Sym/PLPR: [batch][n], original order
@@ -102,6 +103,11 @@ struct ScanArgs {
 };
 constexpr int kCarryGroup = 4096;    // tiles per carry group
 hipError_t scan_launch(const ScanArgs& a, hipStream_t s);
+// Carries of `rows` independent scan rows from their tile composites:
+// agg [rows][tiles][4] (fwd m, v, bwd m, v) -> carry [rows][tiles][2];
+// gagg: [rows][ceil(tiles / kCarryGroup)][4] scratch.
+hipError_t scan_carry_launch(const double* agg, double* gagg, double* carry, int64_t tiles, int64_t rows,
+                             hipStream_t s);
 
 // ---- general case a != b (general.hip) ----
 struct BucketArgs {
@@ -109,6 +115,7 @@ struct BucketArgs {
     int64_t n_out = 0;               // sorted output side
     int64_t n_in = 0;                // input side, original order
     int64_t batch = 0;
+    float inv_t = 1.f;               // 1 / temperature (+inf: equality routing)
     const float* s_out = nullptr;    // sorted output anchors [n_out]
     const float* in_anchor = nullptr;  // [n_in], original order
     const float* in_cos = nullptr;     // cos / sin of the input phases, original order, or null
@@ -131,6 +138,7 @@ struct EvalArgs {
     int64_t n_out = 0;                 // outputs, original order
     int64_t n_in = 0;                  // sorted input side
     int64_t batch = 0;
+    float inv_t = 1.f;                  // 1 / temperature (+inf: equality routing)
     const float* out_anchor = nullptr;  // [n_out]
     const float* out_cos = nullptr;     // cos / sin of the output phases, original order, or null
     const float* out_sin = nullptr;
@@ -143,9 +151,64 @@ struct EvalArgs {
 };
 hipError_t eval_launch(const EvalArgs& a, hipStream_t s);
 
+// ---- gradients (grad.hip) ----
+// Symmetric plans, by rank.  u: row-side vectors, w: column-side vectors
+// (see grad.hip for which is which in a training step).
+struct GradSymArgs {
+    int channels = 1;
+    bool random = false;             // u, w gathered and outputs scattered through perm
+    int64_t n = 0, tiles = 0, batch = 0;
+    int64_t ld = 0;                  // row stride of us, ws
+    int64_t out_ld = 0;              // row stride of dx when not random
+    double inv_t = 1.0;
+    float anchor_scale = -1.f;       // -1/t (0 at t = 0)
+    int dx_half = 1;                 // 1: dx = K^T u (column side), 0: dx = K w (row side)
+    const float* s = nullptr;
+    const uint32_t* perm = nullptr;
+    const float* u = nullptr;        // random: [batch][n] original order
+    const float* w = nullptr;
+    float* us = nullptr;             // by rank [batch][ld] (written when random)
+    float* ws = nullptr;
+    const float* cphi = nullptr;     // by rank, phased only
+    const float* sphi = nullptr;
+    const float* cpsi = nullptr;
+    const float* spsi = nullptr;
+    double* agg = nullptr;           // [4 C batch][tiles][4]
+    double* gagg = nullptr;          // [4 C batch][groups][4]
+    double* carry = nullptr;         // [4 C batch][tiles][2]
+    float* dx = nullptr;             // outputs (null: not wanted): original order when
+    float* da = nullptr;             // random, else by rank
+    float* dphi = nullptr;
+    float* dpsi = nullptr;
+};
+size_t grad_sym_scratch_doubles(int64_t n, int64_t batch, int channels);
+hipError_t grad_sym_launch(const GradSymArgs& a, hipStream_t s);
+
+// General plans: one side's outputs from the other side's PL/PR tables.
+struct EvalGradArgs {
+    int channels = 1;
+    int64_t n_out = 0, n_in = 0, batch = 0;
+    int64_t ld = 0;                     // row stride of pl, pr
+    float inv_t = 1.f;
+    float anchor_scale = -1.f;          // -1/t (0 at t = 0)
+    const float* out_anchor = nullptr;  // [n_out], original order
+    const float* out_cos = nullptr;     // output phases, original order (phased)
+    const float* out_sin = nullptr;
+    const float* s_in = nullptr;        // sorted input side
+    const float* pl = nullptr;          // [channels][batch][ld]
+    const float* pr = nullptr;
+    const float* w = nullptr;           // output-side weights [batch][n_out]
+    float* y = nullptr;                 // plain product [batch][n_out], or null
+    float* d_anchor = nullptr;          // [n_out], or null
+    float* d_phase = nullptr;           // [n_out], or null
+    int lds_bytes = 0;
+};
+hipError_t eval_grad_launch(const EvalGradArgs& a, hipStream_t s);
+
 // ---- Gram (gram.hip) ----
 struct GramArgs {
     int64_t n = 0, k = 0;
+    double inv_t = 1.0;             // 1 / temperature (+inf: equality routing)
     const float* sa = nullptr;      // sorted a [n]
     const uint32_t* pa = nullptr;   // perm of a
     const float* sb = nullptr;      // sorted b [k]

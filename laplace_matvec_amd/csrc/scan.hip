@@ -3,6 +3,7 @@
 // Technical summary of "LAPLEX: The FFT of Learnable Laplace Kernels", §2.2:
 // after sorting, the lower-triangular product obeys
 //     L_r = x_r + exp(s_{r-1} - s_r) L_{r-1}
+// (at temperature t the exponent is divided by t)
 // and the upper part the mirrored recurrence
 //     U_r = x_r + exp(s_r - s_{r+1}) U_{r+1},
 // each O(n) work and O(log n) depth as a scan of affine maps.  Both parts
@@ -30,65 +31,9 @@
 // cos/sin split of a phased operator) outermost.
 #include "lx_device.h"
 #include "lx_internal.h"
+#include "lx_tile.h"
 
 namespace lx {
-
-constexpr int kScanThreads = 256;
-constexpr int kScanWaves = kScanThreads / kWave;
-constexpr int kScanItems = 16;
-static_assert(kScanThreads * kScanItems == kScanTile, "scan tile size");
-
-// Loads p[r0 .. r0+N) (zero past n) with 16-byte loads when the run is whole.
-template <int N, class T>
-__device__ __forceinline__ void load_run(const T* __restrict__ p, int64_t r0, int64_t n, T (&out)[N])
-{
-    static_assert(sizeof(T) == 4 && N % 4 == 0, "run of 32-bit values");
-    if (r0 + N <= n) {
-        const uint4* q = reinterpret_cast<const uint4*>(p + r0);
-#pragma unroll
-        for (int i = 0; i < N / 4; ++i) {
-            const uint4 t = q[i];
-            out[4 * i + 0] = __builtin_bit_cast(T, t.x);
-            out[4 * i + 1] = __builtin_bit_cast(T, t.y);
-            out[4 * i + 2] = __builtin_bit_cast(T, t.z);
-            out[4 * i + 3] = __builtin_bit_cast(T, t.w);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i) out[i] = (r0 + i < n) ? p[r0 + i] : T(0);
-    }
-}
-
-template <int N>
-__device__ __forceinline__ void store_run(float* __restrict__ p, int64_t r0, int64_t n, const float (&v)[N])
-{
-    if (r0 + N <= n) {
-        float4* q = reinterpret_cast<float4*>(p + r0);
-#pragma unroll
-        for (int i = 0; i < N / 4; ++i) q[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i)
-            if (r0 + i < n) p[r0 + i] = v[i];
-    }
-}
-
-// e[i] = exp(s[r0-1+i] - s[r0+i]), i = 0..N: the decay between consecutive
-// ranks around this thread's run.  e[i] multiplies the forward carry into
-// rank r0+i, e[i+1] the backward carry into rank r0+i.  Missing neighbours
-// (before rank 0, after rank n-1) give 0, which cuts the chain there.
-template <int N>
-__device__ __forceinline__ void load_decays(const float* __restrict__ s, int64_t r0, int64_t n, double (&e)[N + 1])
-{
-    float mid[N];
-    load_run<N>(s, r0, n, mid);
-    const float left = (r0 > 0 && r0 - 1 < n) ? s[r0 - 1] : 0.f;
-    const float right = (r0 + N < n) ? s[r0 + N] : 0.f;
-    e[0] = (r0 > 0 && r0 < n) ? decay(left, mid[0]) : 0.0;
-#pragma unroll
-    for (int i = 1; i < N; ++i) e[i] = (r0 + i < n) ? decay(mid[i - 1], mid[i]) : 0.0;
-    e[N] = (r0 + N < n) ? decay(mid[N - 1], right) : 0.0;
-}
 
 __device__ __forceinline__ int64_t row_off(const ScanArgs& A, int c, int64_t vec)
 {
@@ -146,7 +91,7 @@ __global__ __launch_bounds__(kScanThreads) void lx_scan_reduce(ScanArgs A)
     const int64_t r0 = tile * kScanTile + (int64_t)threadIdx.x * kScanItems;
 
     double e[kScanItems + 1];
-    load_decays<kScanItems>(A.s, r0, A.n, e);
+    load_decays<kScanItems>(A.s, r0, A.n, A.inv_t, e);
     float fv[C][kScanItems], bv[C][kScanItems];
     load_values<C, MODE, RANDOM, true>(A, vec, r0, fv, bv);
 
@@ -254,7 +199,7 @@ __global__ __launch_bounds__(kScanThreads) void lx_scan_apply(ScanArgs A)
     const int64_t r0 = tile * kScanTile + (int64_t)threadIdx.x * kScanItems;
 
     double e[kScanItems + 1];
-    load_decays<kScanItems>(A.s, r0, n, e);
+    load_decays<kScanItems>(A.s, r0, n, A.inv_t, e);
     float fv[C][kScanItems], bv[C][kScanItems];
     // the reduce step already stored x by rank: read it back
     load_values<C, MODE, false, false>(A, vec, r0, fv, bv);
@@ -318,17 +263,24 @@ __global__ __launch_bounds__(kScanThreads) void lx_scan_apply(ScanArgs A)
     }
 }
 
+hipError_t scan_carry_launch(const double* agg, double* gagg, double* carry, int64_t tiles, int64_t rows,
+                             hipStream_t s)
+{
+    const int64_t G = (tiles + kCarryGroup - 1) / kCarryGroup;
+    const unsigned cb = (unsigned)(rows * G);
+    LX_LAUNCH("scan_carry", s, (lx_scan_carry_groups<<<cb, kCarryThreads, 0, s>>>(agg, gagg, tiles, G)));
+    LX_LAUNCH("scan_carry", s, (lx_scan_carry_tiles<<<cb, kCarryThreads, 0, s>>>(agg, gagg, carry, tiles, G)));
+    return hipSuccess;
+}
+
 template <int C, int MODE, bool RANDOM>
 static hipError_t scan_launch_t(const ScanArgs& a, hipStream_t s)
 {
     const int64_t blocks = a.tiles * a.batch;
     LX_LAUNCH(MODE == kScanUV ? "scan_reduce_uv" : (RANDOM ? "scan_reduce_gather" : "scan_reduce"), s,
               (lx_scan_reduce<C, MODE, RANDOM><<<(unsigned)blocks, kScanThreads, 0, s>>>(a)));
-    const int64_t G = (a.tiles + kCarryGroup - 1) / kCarryGroup;
-    const unsigned cb = (unsigned)(a.channels * a.batch * G);
-    LX_LAUNCH("scan_carry", s, (lx_scan_carry_groups<<<cb, kCarryThreads, 0, s>>>(a.agg, a.gagg, a.tiles, G)));
-    LX_LAUNCH("scan_carry", s,
-              (lx_scan_carry_tiles<<<cb, kCarryThreads, 0, s>>>(a.agg, a.gagg, a.carry, a.tiles, G)));
+    const hipError_t e = scan_carry_launch(a.agg, a.gagg, a.carry, a.tiles, (int64_t)a.channels * a.batch, s);
+    if (e != hipSuccess) return e;
     LX_LAUNCH(MODE == kScanPLPR ? "scan_apply_tables" : (RANDOM ? "scan_apply_scatter" : "scan_apply"), s,
               (lx_scan_apply<C, MODE, RANDOM><<<(unsigned)blocks, kScanThreads, 0, s>>>(a)));
     return hipSuccess;

@@ -38,6 +38,8 @@ SIGNATURES = {
     "laplex_plan_sorted": (_I32, [_VP, _I32, ctypes.POINTER(_VP)]),
     "laplex_plan_info": (_I32, [_VP, ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_I32)]),
     "laplex_plan_set_option": (_I32, [_VP, _I32, _I64]),
+    "laplex_plan_set_temperature": (_I32, [_VP, ctypes.c_double]),
+    "laplex_backward": (_I32, [_VP, _VP, _VP, _I64, _I32, _VP, _VP, _VP, _VP, _VP, _VP]),
     "laplex_profile_enable": (_I32, [_I32]),
     "laplex_profile_reset": (_I32, []),
     "laplex_profile_collect": (_I32, []),
@@ -171,6 +173,45 @@ def laplex_gram(plan: Plan, D, M=None, stream=None):
 
 def laplex_plan_set_option(plan: Plan, option: int, value: int):
     _check(load().laplex_plan_set_option(plan.handle, option, value), "laplex_plan_set_option")
+
+
+def laplex_plan_set_temperature(plan: Plan, t: float):
+    """Entries exp(-|a_i - b_j| / t); t = 0 routes by exact anchor equality."""
+    _check(load().laplex_plan_set_temperature(plan.handle, float(t)), "laplex_plan_set_temperature")
+
+
+def laplex_backward(plan: Plan, x, g, transpose: bool = False, want=("dx", "da", "db", "dphi", "dpsi"),
+                    stream=None) -> dict:
+    """Gradients of a step through y = K x (or K^T x): x the forward input,
+    g = dL/dy.  Returns the requested tensors among dx ([batch][in]), da [n],
+    db [k] (general plans), dphi [n], dpsi [k] (phased plans); entries a plan
+    does not have are left out."""
+    x = _dev_f32(x, "x")
+    g = _dev_f32(g, "g")
+    n_in, n_out = (plan.n, plan.k) if transpose else (plan.k, plan.n)
+    one = x.dim() == 1
+    batch = 1 if one else x.shape[0]
+    if x.shape[-1] != n_in or x.dim() > 2:
+        raise ValueError(f"x must have shape [batch][{n_in}]")
+    if g.numel() != batch * n_out or g.shape[-1] != n_out:
+        raise ValueError(f"g must have shape [batch][{n_out}]")
+    dev = x.device
+    out = {}
+    if "dx" in want:
+        out["dx"] = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    if "da" in want:
+        out["da"] = torch.empty(plan.n, dtype=torch.float32, device=dev)
+    if "db" in want and not plan.symmetric:
+        out["db"] = torch.empty(plan.k, dtype=torch.float32, device=dev)
+    if plan.phased:
+        if "dphi" in want:
+            out["dphi"] = torch.empty(plan.n, dtype=torch.float32, device=dev)
+        if "dpsi" in want:
+            out["dpsi"] = torch.empty(plan.k, dtype=torch.float32, device=dev)
+    p = [_ptr(out.get(k)) for k in ("dx", "da", "db", "dphi", "dpsi")]
+    _check(load().laplex_backward(plan.handle, _ptr(x), _ptr(g), batch, int(bool(transpose)), *p,
+                                  _stream(stream)), "laplex_backward")
+    return out
 
 
 def _copy_device(dst: torch.Tensor, src_ptr: int, nbytes: int, stream=None):

@@ -76,6 +76,9 @@ def test_apply_and_gram_reject_bad_arguments():
     assert lib.laplex_plan_destroy(None) == lx.OK
     assert lib.laplex_plan_set_option(None, 1, 0) == lx.ERR_INVALID_ARGUMENT
     assert lib.laplex_plan_info(None, None, None, None) == lx.ERR_INVALID_ARGUMENT
+    assert lib.laplex_plan_set_temperature(None, 1.0) == lx.ERR_INVALID_ARGUMENT
+    assert lib.laplex_backward(None, FAKE, FAKE, 1, 0, FAKE, None, None, None, None, None) == \
+        lx.ERR_INVALID_ARGUMENT
     for s in range(7):
         assert lib.laplex_status_str(s)
 
