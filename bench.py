@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=1 << 25)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--backward", action="store_true",
+                   help="time a training step instead: forward product plus its backward pass "
+                        "(input and anchor gradients, and phase gradients for a phased operator)")
     return p.parse_args()
 
 
@@ -65,6 +68,10 @@ def model_bytes(kernel: str, n: int, batch: int = 1, channels: int = 1) -> float
         "scan_apply": 4.0 + 2 * factors + 8.0 * batch,
         "scan_reduce_gather": 8.0 + factors + 8.0 * batch,
         "scan_apply_scatter": 8.0 + 2 * factors + 8.0 * batch,
+        # gradient by rank: s, u and w read; per half launch also the anchor
+        # row (written, or read and written) and, in one of the two, dx
+        "grad_reduce": 4.0 + 2 * factors + 8.0 * batch,
+        "grad_apply": 4.0 + 2 * factors + 8.0 * batch + 6.0 + 2.0 * batch,
     }.get(kernel)
     return None if per is None else per * n
 
@@ -149,7 +156,29 @@ def main():
     torch.cuda.synchronize()
     batch = W.batch
 
-    if W.kind == "sym":
+    if W.kind == "sym" and args.backward:
+        a, x = inp["a"], inp["x"]
+        g = wl.device_normal(tuple(x.shape), cfg, wl.S_W, device=dev)
+        y = torch.empty_like(x)
+        dx = torch.empty_like(x)
+        da = torch.empty(n, device=dev)
+        lib = lx.load()
+        import ctypes
+
+        def step():
+            plan = lx.laplex_plan_create(a)
+            lx.laplex_apply(plan, x, y)
+            st = lib.laplex_backward(plan.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(g.data_ptr()),
+                                     batch, 0, ctypes.c_void_p(dx.data_ptr()), ctypes.c_void_p(da.data_ptr()),
+                                     None, None, None, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if st != lx.OK:
+                raise lx.LaplexError(st, "laplex_backward")
+            plan.destroy()
+        elements = n * batch
+        desc = {"workload": W.name, "n": n, "batch": batch,
+                "path": "training step: plan_create + apply + backward (dx, da) (end to end)",
+                "anchors": "a ~ 1e4 N(0,1)" if cfg == 5 else W.note}
+    elif W.kind == "sym":
         a, x = inp["a"], inp["x"]
         y = torch.empty_like(x)
 
@@ -160,6 +189,16 @@ def main():
         elements = n * batch
         desc = {"workload": W.name, "n": n, "batch": batch, "path": "plan_create+apply (end to end)",
                 "anchors": "a ~ 1e4 N(0,1)" if cfg == 5 else W.note}
+    elif W.kind == "general" and args.backward:
+        plan = lx.laplex_plan_create(inp["a"], b=inp["b"], phi=inp["phi"], psi=inp["psi"])
+        y = torch.empty((batch, n), device=dev)
+
+        def step():
+            lx.laplex_apply(plan, inp["x"], y)
+            lx.laplex_backward(plan, inp["x"], inp["w"])
+        elements = n * batch
+        desc = {"workload": W.name, "n": n, "k": W.k, "batch": batch,
+                "path": "training step through y=Kx: apply + backward (dx, da, db, dphi, dpsi), plan excluded"}
     elif W.kind == "general":
         plan = lx.laplex_plan_create(inp["a"], b=inp["b"], phi=inp["phi"], psi=inp["psi"])
         y = torch.empty((batch, n), device=dev)
@@ -211,13 +250,14 @@ def main():
                     "algorithmic_bytes_per_launch": ab, "avg_launch_ms": kernels[dominant]["avg_ms"]}
     # whole-step model bandwidth (symmetric end to end: 4 + 60 sort + 32 apply bytes/elem at B=1)
     extra = {}
-    if W.kind == "sym":
+    if W.kind == "sym" and not args.backward:
         model = model_step_bytes(n, batch)
         extra["model_bytes_per_step"] = model
         extra["model_gbps_end_to_end"] = round(model / (ms / 1e3) / 1e9, 1)
         extra["model_frac_end_to_end"] = round(model / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
     out = {
-        "metric": METRIC if cfg == 5 else f"LAPLEX {W.kind} elements/s ({W.name})",
+        "metric": (METRIC if cfg == 5 else f"LAPLEX {W.kind} elements/s ({W.name})") if not args.backward
+        else f"LAPLEX training step (forward + backward) elements/s ({W.name})",
         "value": elements / (ms / 1e3),
         "unit": "elements/s",
         "n_gpus": 1,
@@ -234,7 +274,7 @@ def main():
         "kernels": {k: {kk: round(vv, 5) for kk, vv in v.items()} for k, v in kernels.items()},
         **extra,
     }
-    if cfg == 5 and not args.no_cpu_baseline:
+    if cfg == 5 and not args.no_cpu_baseline and not args.backward:
         out["cpu_baseline"] = cpu_baseline(args.cpu_sample)
     print(json.dumps(out), flush=True)
 
