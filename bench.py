@@ -57,11 +57,12 @@ def parse():
 TILE_TABLE = 6.0 * 256 / 8192
 
 
-def model_bytes(kernel: str, n: int, batch: int = 1, channels: int = 1) -> float | None:
+def model_bytes(kernel: str, n: int, batch: int = 1, channels: int = 1, vals: int = 0) -> float | None:
+    """vals: value rows carried by each radix pass (read and written)."""
     factors = 8.0 if channels == 2 else 0.0
     per = {
         "sort_hist": 4.0,
-        "sort_pass": 10.0 + TILE_TABLE,
+        "sort_pass": 10.0 + TILE_TABLE + 8.0 * vals,
         "replay_forward": 2.0 + TILE_TABLE + 8.0 * batch,
         "replay_backward": 2.0 + TILE_TABLE + 8.0 * batch,
         "scan_reduce": 4.0 + factors + 4.0 * batch,
@@ -77,10 +78,10 @@ def model_bytes(kernel: str, n: int, batch: int = 1, channels: int = 1) -> float
 
 
 def model_step_bytes(n: int, batch: int) -> float:
-    """Whole symmetric step (plan + apply on the replay path)."""
-    launches = {"sort_hist": 1, "sort_pass": 4, "replay_forward": 4, "scan_reduce": 1,
-                "scan_apply": 1, "replay_backward": 4}
-    return sum(c * model_bytes(k, n, batch) for k, c in launches.items())
+    """Whole symmetric step (plan_create_apply on the replay path: the rows
+    of x travel with the keys through the four radix passes)."""
+    launches = {"sort_hist": 1, "sort_pass": 4, "scan_reduce": 1, "scan_apply": 1, "replay_backward": 4}
+    return sum(c * model_bytes(k, n, batch, vals=batch) for k, c in launches.items())
 
 
 def counter_traffic(kernel: str, workload: str):
@@ -166,8 +167,7 @@ def main():
         import ctypes
 
         def step():
-            plan = lx.laplex_plan_create(a)
-            lx.laplex_apply(plan, x, y)
+            plan, _ = lx.laplex_plan_create_apply(a, x, y)
             st = lib.laplex_backward(plan.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(g.data_ptr()),
                                      batch, 0, ctypes.c_void_p(dx.data_ptr()), ctypes.c_void_p(da.data_ptr()),
                                      None, None, None, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
@@ -176,18 +176,18 @@ def main():
             plan.destroy()
         elements = n * batch
         desc = {"workload": W.name, "n": n, "batch": batch,
-                "path": "training step: plan_create + apply + backward (dx, da) (end to end)",
+                "path": "training step: plan_create_apply + backward (dx, da) (end to end)",
                 "anchors": "a ~ 1e4 N(0,1)" if cfg == 5 else W.note}
     elif W.kind == "sym":
         a, x = inp["a"], inp["x"]
         y = torch.empty_like(x)
 
         def step():
-            plan = lx.laplex_plan_create(a)
-            lx.laplex_apply(plan, x, y)
+            plan, _ = lx.laplex_plan_create_apply(a, x, y)
             plan.destroy()
         elements = n * batch
-        desc = {"workload": W.name, "n": n, "batch": batch, "path": "plan_create+apply (end to end)",
+        desc = {"workload": W.name, "n": n, "batch": batch,
+                "path": "plan_create_apply: sort + apply (end to end)",
                 "anchors": "a ~ 1e4 N(0,1)" if cfg == 5 else W.note}
     elif W.kind == "general" and args.backward:
         plan = lx.laplex_plan_create(inp["a"], b=inp["b"], phi=inp["phi"], psi=inp["psi"])
@@ -240,7 +240,7 @@ def main():
     dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"]) if kernels else None
     roof = None
     if dominant:
-        ab = model_bytes(dominant, n, batch)
+        ab = model_bytes(dominant, n, batch, vals=batch if W.kind == "sym" else 0)
         avg_s = kernels[dominant]["avg_ms"] / 1e3
         if ab is not None:
             ach = ab / avg_s / 1e9

@@ -81,6 +81,25 @@ laplex_status laplex_plan_create(laplex_plan* out, const float* a, int64_t n,
                                  const float* phi, const float* psi, void* stream);
 
 /*
+ * laplex_plan_create_apply -- a symmetric plan (b = a) and y = K x at once.
+ *   (summary §2.2: sort the anchors, then the two scans; for a layer whose
+ *   anchors change every training step the sort and the first product
+ *   always come together)
+ *
+ *   Arguments as laplex_plan_create with b = NULL, plus x, y: device float32
+ *   [batch][n], row-major, not overlapping; batch >= 1.  y = K x as
+ *   laplex_apply(plan, x, y, batch, 0) would give, bit for bit.  For long
+ *   anchor sets the rows of x (up to 18 with phases, 20 without) travel
+ *   through the radix passes with the anchors, which saves one pass over
+ *   x per radix digit; otherwise it is plan_create followed by apply.
+ *   Synchronizes `stream` once, like laplex_plan_create; *out receives the
+ *   plan (NULL on error), which stays usable for apply, gram and backward.
+ */
+laplex_status laplex_plan_create_apply(laplex_plan* out, const float* a, int64_t n,
+                                       const float* phi, const float* psi, const float* x,
+                                       float* y, int64_t batch, void* stream);
+
+/*
  * laplex_apply -- y = K x (transpose = 0) or y = K^T x (transpose = 1).
  *   (summary §2.2: prefix/suffix scans; general case via vectors u, v)
  *

@@ -52,52 +52,118 @@ laplex_status from_hip(hipError_t e, const char* where)
 inline int64_t pad64(int64_t x) { return (x + 63) & ~(int64_t)63; }
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// ------------------------------------------------------------ memory pool
-
-struct DevicePool {
-    hipMemPool_t pool = nullptr;
-    bool tried = false;
+// ------------------------------------------------------- caching allocator
+//
+// Device memory for plans, workspaces and sort scratch.  A layer whose
+// anchors change every training step makes and drops a plan per step, tens
+// of GB each time at n = 2^30, so freed blocks are kept per device and
+// handed out again (best fit, at most twice the request) instead of going
+// back to the driver.  A block freed on stream s carries an event recorded
+// on s at the free; whoever takes it next orders its stream after that
+// event, so reuse across streams is safe.  When the driver is out of
+// memory, the cached blocks are released and the allocation is retried.
+struct CachedBlock {
+    void* ptr;
+    size_t bytes;
+    hipEvent_t freed;  // recorded at the free (null: idle already)
 };
-std::mutex g_pool_mu;
-std::vector<DevicePool> g_pools;
+struct DeviceCache {
+    std::mutex mu;
+    std::vector<CachedBlock> idle;
+    std::vector<std::pair<void*, size_t>> live;
+    std::vector<hipEvent_t> events;
+};
+std::mutex g_cache_mu;
+std::vector<DeviceCache*> g_caches;
 
-hipMemPool_t pool_for(int dev)
+DeviceCache& cache_for(int dev)
 {
-    std::lock_guard<std::mutex> lk(g_pool_mu);
-    if ((int)g_pools.size() <= dev) g_pools.resize(dev + 1);
-    DevicePool& p = g_pools[dev];
-    if (!p.tried) {
-        p.tried = true;
-        hipMemPoolProps props = {};
-        props.allocType = hipMemAllocationTypePinned;
-        props.handleTypes = hipMemHandleTypeNone;
-        props.location.type = hipMemLocationTypeDevice;
-        props.location.id = dev;
-        if (hipMemPoolCreate(&p.pool, &props) == hipSuccess) {
-            uint64_t keep = UINT64_MAX;
-            (void)hipMemPoolSetAttribute(p.pool, hipMemPoolAttrReleaseThreshold, &keep);
-        } else {
-            p.pool = nullptr;
-            (void)hipGetLastError();
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    while ((int)g_caches.size() <= dev) g_caches.push_back(new DeviceCache());
+    return *g_caches[dev];
+}
+
+size_t round_block(size_t bytes)
+{
+    const size_t q = bytes >= ((size_t)1 << 24) ? ((size_t)1 << 21) : 256;  // 2 MiB steps for big blocks
+    return (bytes + q - 1) / q * q;
+}
+
+// Caller holds c.mu.  Waits for the idle blocks' frees and returns them.
+void release_idle(DeviceCache& c)
+{
+    for (CachedBlock& b : c.idle) {
+        if (b.freed) {
+            (void)hipEventSynchronize(b.freed);
+            c.events.push_back(b.freed);
         }
+        (void)hipFree(b.ptr);
     }
-    return p.pool;
+    c.idle.clear();
 }
 
 hipError_t dev_alloc(void** ptr, size_t bytes, int dev, hipStream_t s)
 {
     *ptr = nullptr;
-    if (bytes == 0) bytes = 256;
-    hipMemPool_t pool = pool_for(dev);
-    if (pool) return hipMallocFromPoolAsync(ptr, bytes, pool, s);
-    return hipMalloc(ptr, bytes);
+    bytes = round_block(bytes == 0 ? 256 : bytes);
+    DeviceCache& c = cache_for(dev);
+    std::lock_guard<std::mutex> lk(c.mu);
+    int best = -1;
+    for (int i = 0; i < (int)c.idle.size(); ++i) {
+        const size_t have = c.idle[i].bytes;
+        if (have >= bytes && have <= 2 * bytes && (best < 0 || have < c.idle[best].bytes)) best = i;
+    }
+    if (best >= 0) {
+        CachedBlock b = c.idle[best];
+        c.idle.erase(c.idle.begin() + best);
+        if (b.freed) {
+            (void)hipStreamWaitEvent(s, b.freed, 0);
+            c.events.push_back(b.freed);
+        }
+        c.live.emplace_back(b.ptr, b.bytes);
+        *ptr = b.ptr;
+        return hipSuccess;
+    }
+    hipError_t e = hipMalloc(ptr, bytes);
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) {
+        (void)hipGetLastError();
+        release_idle(c);
+        e = hipMalloc(ptr, bytes);
+    }
+    if (e != hipSuccess) {
+        *ptr = nullptr;
+        return e;
+    }
+    c.live.emplace_back(*ptr, bytes);
+    return hipSuccess;
 }
 
 void dev_free(void* ptr, int dev, hipStream_t s)
 {
     if (!ptr) return;
-    if (pool_for(dev)) (void)hipFreeAsync(ptr, s);
-    else (void)hipFree(ptr);
+    DeviceCache& c = cache_for(dev);
+    std::lock_guard<std::mutex> lk(c.mu);
+    for (size_t i = 0; i < c.live.size(); ++i) {
+        if (c.live[i].first != ptr) continue;
+        const size_t bytes = c.live[i].second;
+        c.live[i] = c.live.back();
+        c.live.pop_back();
+        hipEvent_t ev = nullptr;
+        if (!c.events.empty()) {
+            ev = c.events.back();
+            c.events.pop_back();
+        } else if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+            ev = nullptr;
+        }
+        if (ev && hipEventRecord(ev, s) != hipSuccess) {
+            (void)hipGetLastError();
+            (void)hipStreamSynchronize(s);
+            c.events.push_back(ev);
+            ev = nullptr;
+        }
+        c.idle.push_back(CachedBlock{ptr, bytes, ev});
+        return;
+    }
 }
 
 // ------------------------------------------------------------- profiling
@@ -213,10 +279,11 @@ hipError_t plan_alloc(laplex_plan p, void** out, size_t bytes, hipStream_t s)
 void plan_release(laplex_plan p)
 {
     if (!p) return;
-    hipStream_t s = nullptr;
-    for (void* q : p->owned) dev_free(q, p->device, s);
-    if (p->ws) dev_free(p->ws, p->device, s);
-    (void)hipStreamSynchronize(s);
+    // every stream may still use the plan's memory: wait for the device, then
+    // the blocks go back to the cache already idle
+    (void)hipDeviceSynchronize();
+    for (void* q : p->owned) dev_free(q, p->device, nullptr);
+    if (p->ws) dev_free(p->ws, p->device, nullptr);
     delete p;
 }
 
@@ -357,8 +424,13 @@ const char* laplex_status_str(laplex_status s)
 
 const char* laplex_last_error(void) { return g_last_error.c_str(); }
 
-laplex_status laplex_plan_create(laplex_plan* out, const float* a, int64_t n, const float* b, int64_t k,
-                                 const float* phi, const float* psi, void* stream)
+namespace {
+
+// Plan creation; with x != NULL (symmetric plans only) also y = K x, sorting
+// the rows of x along with the anchors when the plan replays its sort.
+laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, const float* b, int64_t k,
+                               const float* phi, const float* psi, const float* x, float* y, int64_t batch,
+                               void* stream)
 {
     if (out) *out = nullptr;
     if (!out) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "out is NULL");
@@ -409,20 +481,74 @@ laplex_status laplex_plan_create(laplex_plan* out, const float* a, int64_t n, co
         p->ra = lx::sort_records_at(rec, n);
     }
     const int64_t big = sym ? n : (n > k ? n : k);
-    LX_PLAN_TRY(dev_alloc(&scratch, lx::sort_scratch_bytes(big), p->device, s), "alloc sort scratch");
-    LX_PLAN_TRY(lx::sort_launch(a, n, p->sa, p->ra, scratch, flag, s), "sort a");
+    // Symmetric plans on the replay path sort value rows with the anchors:
+    // the rows of x (when applying at once) and the phases.
+    const bool replay = sym && n >= replay_min();
+    const int ph_rows = p->phased ? 2 : 0;
+    const bool fuse = x != nullptr && replay && batch + ph_rows <= lx::kMaxSortVals;
+    lx::SortVals V;
+    if (replay) {
+        if (fuse)
+            for (int64_t v = 0; v < batch; ++v) V.in[V.rows++] = x + v * n;
+        if (p->phased) {
+            V.in[V.rows++] = phi;
+            V.in[V.rows++] = psi;
+        }
+        V.ld = pad64(n);
+    }
+    const size_t vbytes = align256((size_t)V.rows * V.ld * 4);
+    LX_PLAN_TRY(dev_alloc(&scratch, lx::sort_scratch_bytes(big) + 2 * vbytes, p->device, s), "alloc sort scratch");
+    if (V.rows) {
+        V.va = (float*)((char*)scratch + lx::sort_scratch_bytes(big));
+        V.vb = (float*)((char*)V.va + vbytes);
+    }
+    LX_PLAN_TRY(lx::sort_launch(a, n, p->sa, p->ra, scratch, flag, s, V.rows ? &V : nullptr), "sort a");
     if (sym) {
         p->sb = p->sa;
         p->rb = p->ra;
-        // short sides gather through the permutation, and phases need it once
-        if (n < replay_min() || p->phased) LX_PLAN_TRY(ensure_perm(p, 0, s), "permutation");
+        // short sides gather through the permutation
+        if (!replay) LX_PLAN_TRY(ensure_perm(p, 0, s), "permutation");
         if (p->phased) {
             LX_PLAN_TRY(plan_alloc(p, (void**)&p->cphi, (size_t)n * 4, s), "alloc phases");
             LX_PLAN_TRY(plan_alloc(p, (void**)&p->sphi, (size_t)n * 4, s), "alloc phases");
             LX_PLAN_TRY(plan_alloc(p, (void**)&p->cpsi, (size_t)n * 4, s), "alloc phases");
             LX_PLAN_TRY(plan_alloc(p, (void**)&p->spsi, (size_t)n * 4, s), "alloc phases");
-            LX_PLAN_TRY(lx::phase_factors_launch(phi, p->pa, n, p->cphi, p->sphi, flag, s), "phi factors");
-            LX_PLAN_TRY(lx::phase_factors_launch(psi, p->pa, n, p->cpsi, p->spsi, flag, s), "psi factors");
+            if (replay) {
+                // the phases came out of the sort in rank order: the last two rows
+                const float* sphi_rank = V.vb + (V.rows - 2) * V.ld;
+                const float* spsi_rank = V.vb + (V.rows - 1) * V.ld;
+                LX_PLAN_TRY(lx::phase_factors_launch(sphi_rank, nullptr, n, p->cphi, p->sphi, flag, s), "phi factors");
+                LX_PLAN_TRY(lx::phase_factors_launch(spsi_rank, nullptr, n, p->cpsi, p->spsi, flag, s), "psi factors");
+            } else {
+                LX_PLAN_TRY(lx::phase_factors_launch(phi, p->pa, n, p->cphi, p->sphi, flag, s), "phi factors");
+                LX_PLAN_TRY(lx::phase_factors_launch(psi, p->pa, n, p->cpsi, p->spsi, flag, s), "psi factors");
+            }
+        }
+        if (fuse) {
+            // y = K x from the sorted rows of x: scan in place, replay back into y
+            const int ch = p->phased ? 2 : 1;
+            LX_PLAN_TRY(ensure_ws(p, scan_ws_bytes(n, batch, ch, 0, 0), s), "workspace");
+            Carve cv(p->ws);
+            lx::ScanArgs A;
+            A.mode = lx::kScanSym;
+            scan_common(A, cv, n, batch, ch);
+            A.inv_t = p->inv_t;
+            A.s = p->sa;
+            A.random = false;
+            A.xs = V.vb;
+            A.ys = V.vb;
+            if (p->phased) {
+                A.in_c = p->cpsi;
+                A.in_s = p->spsi;
+                A.out_c = p->cphi;
+                A.out_s = p->sphi;
+            }
+            LX_PLAN_TRY(lx::scan_launch(A, s), "symmetric apply");
+            const lx::SortRecords& R = p->ra;
+            LX_PLAN_TRY(lx::replay_launch(R, 3, false, V.vb, V.ld, V.va, V.ld, batch, s), "replay");
+            LX_PLAN_TRY(lx::replay_launch(R, 2, false, V.va, V.ld, V.vb, V.ld, batch, s), "replay");
+            LX_PLAN_TRY(lx::replay_launch(R, 1, false, V.vb, V.ld, V.va, V.ld, batch, s), "replay");
+            LX_PLAN_TRY(lx::replay_launch(R, 0, false, V.va, V.ld, y, n, batch, s), "replay");
         }
     } else {
         LX_PLAN_TRY(plan_alloc(p, (void**)&p->sb, (size_t)k * 4, s), "alloc sorted b");
@@ -463,8 +589,38 @@ laplex_status laplex_plan_create(laplex_plan* out, const float* a, int64_t n, co
     LX_PLAN_TRY(hipStreamSynchronize(s), "synchronize");
     if (host_flag & 1u) return bail(fail(LAPLEX_ERR_NONFINITE_ANCHOR, "NaN or Inf among anchors or phases"));
 #undef LX_PLAN_TRY
+    if (x && !fuse) {
+        // not fused (short side or too many rows): the plain apply
+        const laplex_status st2 = laplex_apply(p, x, y, batch, 0, stream);
+        if (st2 != LAPLEX_OK) {
+            plan_release(p);
+            return st2;
+        }
+    }
     *out = p;
     return LAPLEX_OK;
+}
+
+}  // namespace
+
+laplex_status laplex_plan_create(laplex_plan* out, const float* a, int64_t n, const float* b, int64_t k,
+                                 const float* phi, const float* psi, void* stream)
+{
+    return plan_create_impl(out, a, n, b, k, phi, psi, nullptr, nullptr, 0, stream);
+}
+
+laplex_status laplex_plan_create_apply(laplex_plan* out, const float* a, int64_t n, const float* phi,
+                                       const float* psi, const float* x, float* y, int64_t batch, void* stream)
+{
+    if (out) *out = nullptr;
+    if (!out) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "out is NULL");
+    if (!x || !y) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "x or y is NULL");
+    if (batch < 1) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "batch must be >= 1");
+    if (n >= 1 && (batch > (int64_t)1 << 40 || (double)batch * (double)n > 4.0e18 / 4))
+        return fail(LAPLEX_ERR_INVALID_ARGUMENT, "batch too large");
+    if (n >= 1 && ranges_overlap(x, (size_t)(batch * n) * 4, y, (size_t)(batch * n) * 4))
+        return fail(LAPLEX_ERR_INVALID_ARGUMENT, "x and y overlap");
+    return plan_create_impl(out, a, n, nullptr, 0, phi, psi, x, y, batch, stream);
 }
 
 laplex_status laplex_plan_destroy(laplex_plan p)

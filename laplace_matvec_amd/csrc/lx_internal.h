@@ -45,13 +45,29 @@ struct SortRecords {
     uint32_t* base[4] = {};
     uint16_t* start[4] = {};
 };
+// Value rows sorted along with the keys (key-value passes): pass 0 reads
+// in[r] (original order); the passes alternate between va and vb (rows of
+// stride ld), so the sorted rows end in vb.
+constexpr int kMaxSortVals = 20;
+struct SortVals {
+    int rows = 0;
+    const float* in[kMaxSortVals] = {};
+    float* va = nullptr;
+    float* vb = nullptr;
+    int64_t ld = 0;
+};
+struct SortValPass {  // kernel argument: one pass's row pointers
+    int rows = 0;
+    const float* in[kMaxSortVals] = {};
+    float* out[kMaxSortVals] = {};
+};
 size_t sort_scratch_bytes(int64_t n);   // temporary, during the sort
 size_t sort_record_bytes(int64_t n);    // kept by the plan
 SortRecords sort_records_at(void* base, int64_t n);
 // Stable argsort of a[0..n): sorted[r] = a[perm[r]] for the permutation the
 // records describe.  *flag (device) gets bit 0 if any anchor is NaN/Inf.
 hipError_t sort_launch(const float* a, int64_t n, float* sorted, const SortRecords& R, void* scratch,
-                       uint32_t* flag, hipStream_t s);
+                       uint32_t* flag, hipStream_t s, const SortVals* vals = nullptr);
 // One replayed pass: forward moves pass-k input order to pass-k output
 // order, backward the reverse.  Rows of `batch` vectors with strides in_ld,
 // out_ld (elements).

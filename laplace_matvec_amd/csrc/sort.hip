@@ -114,12 +114,12 @@ __global__ __launch_bounds__(kRadix) void lx_sort_scan_hist(const uint32_t* __re
     base[d * kRadix + threadIdx.x] = ex;
 }
 
-template <bool FIRST, bool LAST>
+template <bool FIRST, bool LAST, bool VALS>
 __global__ __launch_bounds__(kSortThreads) void lx_sort_pass(
     const float* __restrict__ a_in, const uint32_t* __restrict__ keys_in, uint32_t* __restrict__ keys_out,
     float* __restrict__ sorted_out, uint16_t* __restrict__ rec, uint32_t* __restrict__ tab_base,
     uint16_t* __restrict__ tab_start, const uint32_t* __restrict__ bin_base, uint32_t* __restrict__ state,
-    uint32_t* __restrict__ ticket, int shift, int64_t n)
+    uint32_t* __restrict__ ticket, int shift, int64_t n, SortValPass vals)
 {
     __shared__ uint16_t s_hist[kSortWaves][kRadix];  // per-wave counts, then wave offsets (<= tile size)
     __shared__ uint32_t s_start[kRadix];             // tile-local start of each bin
@@ -144,10 +144,10 @@ __global__ __launch_bounds__(kSortThreads) void lx_sort_pass(
     // index order.  Positions past n get the largest key: they rank last,
     // in bin 255, and land past n.
     uint32_t key[kSortItems];
+    const int64_t wbase = tile0 + wpos;  // uniform
+    const uint32_t room = (uint32_t)(n - wbase < (int64_t)(kSortItems * kWave) ? (n > wbase ? n - wbase : 0)
+                                                                               : (int64_t)(kSortItems * kWave));
     {
-        const int64_t wbase = tile0 + wpos;  // uniform
-        const uint32_t room = (uint32_t)(n - wbase < (int64_t)(kSortItems * kWave) ? (n > wbase ? n - wbase : 0)
-                                                                                   : (int64_t)(kSortItems * kWave));
         const float* ain = a_in + wbase;
         const uint32_t* kin = keys_in + wbase;
 #pragma unroll
@@ -242,18 +242,42 @@ __global__ __launch_bounds__(kSortThreads) void lx_sort_pass(
     __syncthreads();
 
     // Consecutive slots of one digit go to consecutive global positions.
+    uint32_t dsts[VALS ? kSortItems : 1];
 #pragma unroll
     for (int q = 0; q < kSortItems; ++q) {
         const uint32_t i = (uint32_t)(q * kSortThreads + tid);
         const uint32_t k = s_buf[i];
         const uint32_t d = (k >> shift) & 0xFFu;
         const uint32_t dst = s_glob[d] + (i - s_start[d]);
+        if (VALS) dsts[q] = dst;
         if (dst < (uint32_t)n) {
             if (LAST) sorted_out[dst] = float_of_key(k);
             else keys_out[dst] = k;
         }
     }
     __syncthreads();
+    // Value rows travel with the keys: loaded like the keys, placed in the
+    // same slots, written to the same destinations.
+    if (VALS) {
+        float* fbuf = reinterpret_cast<float*>(s_buf);
+        for (int r = 0; r < vals.rows; ++r) {
+            const float* vin = vals.in[r] + wbase;
+            float v[kSortItems];
+#pragma unroll
+            for (int j = 0; j < kSortItems; ++j) {
+                const uint32_t off = (uint32_t)(j * kWave + lane);
+                v[j] = off < room ? vin[off] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < kSortItems; ++j) fbuf[pos[j]] = v[j];
+            __syncthreads();
+            float* vout = vals.out[r];
+#pragma unroll
+            for (int q = 0; q < kSortItems; ++q)
+                if (dsts[q] < (uint32_t)n) vout[dsts[q]] = fbuf[q * kSortThreads + tid];
+            __syncthreads();
+        }
+    }
     // Replay record: the tile position each slot came from.
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) s_buf[pos[j]] = (uint32_t)(wpos + j * kWave + lane);
@@ -307,7 +331,7 @@ SortRecords sort_records_at(void* base, int64_t n)
 }
 
 hipError_t sort_launch(const float* a, int64_t n, float* sorted, const SortRecords& R, void* scratch,
-                       uint32_t* flag, hipStream_t s)
+                       uint32_t* flag, hipStream_t s, const SortVals* vals)
 {
     if (n <= 0) return hipSuccess;
     const int64_t tiles = (n + kSortTile - 1) / kSortTile;
@@ -331,24 +355,41 @@ hipError_t sort_launch(const float* a, int64_t n, float* sorted, const SortRecor
     }
     LX_LAUNCH("sort_scan_hist", s, (lx_sort_scan_hist<<<4, kRadix, 0, s>>>(hist, base)));
 
+    // value rows: pass 0 reads the caller's rows, then ping-pong va -> vb -> va -> vb
+    const bool hv = vals && vals->rows > 0;
+    if (hv && vals->rows > kMaxSortVals) return hipErrorInvalidValue;
+    SortValPass vp[4];
+    if (hv) {
+        float* const ping[4] = {vals->va, vals->vb, vals->va, vals->vb};
+        for (int k = 0; k < 4; ++k) {
+            vp[k].rows = vals->rows;
+            for (int r = 0; r < vals->rows; ++r) {
+                vp[k].in[r] = k == 0 ? vals->in[r] : ping[k - 1] + (int64_t)r * vals->ld;
+                vp[k].out[r] = ping[k] + (int64_t)r * vals->ld;
+            }
+        }
+    }
     const int grid = (int)tiles;
     const int64_t st = tiles * kRadix;
-    LX_LAUNCH("sort_pass", s,
-              (lx_sort_pass<true, false><<<grid, kSortThreads, 0, s>>>(
-                  a, nullptr, keysA, nullptr, R.rec[0], R.base[0], R.start[0], base + 0 * kRadix,
-                  state + 0 * st, tickets + 0, 0, n)));
-    LX_LAUNCH("sort_pass", s,
-              (lx_sort_pass<false, false><<<grid, kSortThreads, 0, s>>>(
-                  nullptr, keysA, keysB, nullptr, R.rec[1], R.base[1], R.start[1], base + 1 * kRadix,
-                  state + 1 * st, tickets + 1, 8, n)));
-    LX_LAUNCH("sort_pass", s,
-              (lx_sort_pass<false, false><<<grid, kSortThreads, 0, s>>>(
-                  nullptr, keysB, keysA, nullptr, R.rec[2], R.base[2], R.start[2], base + 2 * kRadix,
-                  state + 2 * st, tickets + 2, 16, n)));
-    LX_LAUNCH("sort_pass", s,
-              (lx_sort_pass<false, true><<<grid, kSortThreads, 0, s>>>(
-                  nullptr, keysA, nullptr, sorted, R.rec[3], R.base[3], R.start[3], base + 3 * kRadix,
-                  state + 3 * st, tickets + 3, 24, n)));
+    const uint32_t* kin[4] = {nullptr, keysA, keysB, keysA};
+    uint32_t* kout[4] = {keysA, keysB, keysA, nullptr};
+    for (int k = 0; k < 4; ++k) {
+#define LX_PASS(F, L, V)                                                                                      \
+    LX_LAUNCH("sort_pass", s,                                                                                 \
+              (lx_sort_pass<F, L, V><<<grid, kSortThreads, 0, s>>>(                                          \
+                  k == 0 ? a : nullptr, kin[k], kout[k], k == 3 ? sorted : nullptr, R.rec[k], R.base[k],      \
+                  R.start[k], base + k * kRadix, state + k * st, tickets + k, 8 * k, n, vp[k])))
+        if (hv) {
+            if (k == 0) LX_PASS(true, false, true);
+            else if (k == 3) LX_PASS(false, true, true);
+            else LX_PASS(false, false, true);
+        } else {
+            if (k == 0) LX_PASS(true, false, false);
+            else if (k == 3) LX_PASS(false, true, false);
+            else LX_PASS(false, false, false);
+        }
+#undef LX_PASS
+    }
     return hipSuccess;
 }
 

@@ -31,6 +31,7 @@ PLAN_SYMMETRIC, PLAN_PHASED = 1, 2
 _VP, _I64, _I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 SIGNATURES = {
     "laplex_plan_create": (_I32, [ctypes.POINTER(_VP), _VP, _I64, _VP, _I64, _VP, _VP, _VP]),
+    "laplex_plan_create_apply": (_I32, [ctypes.POINTER(_VP), _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP]),
     "laplex_apply": (_I32, [_VP, _VP, _VP, _I64, _I32, _VP]),
     "laplex_gram": (_I32, [_VP, _VP, _VP, _VP]),
     "laplex_plan_destroy": (_I32, [_VP]),
@@ -140,6 +141,29 @@ def laplex_plan_create(a, b=None, phi=None, psi=None, stream=None) -> Plan:
     _check(st, "laplex_plan_create")
     k = a.numel() if b is None else b.numel()
     return Plan(h, a.numel(), k, b is None, phi is not None, a.device)
+
+
+def laplex_plan_create_apply(a, x, y=None, phi=None, psi=None, stream=None):
+    """Symmetric plan and y = K x in one call; returns (plan, y)."""
+    a = _dev_f32(a, "a")
+    phi = _dev_f32(phi, "phi")
+    psi = _dev_f32(psi, "psi")
+    x = _dev_f32(x, "x")
+    n = a.numel()
+    one = x.dim() == 1
+    batch = 1 if one else x.shape[0]
+    if x.shape[-1] != n or x.dim() > 2:
+        raise ValueError(f"x must have shape [batch][{n}]")
+    if y is None:
+        y = torch.empty_like(x)
+    y = _dev_f32(y, "y")
+    if y.numel() != batch * n:
+        raise ValueError("y has the wrong size")
+    h = ctypes.c_void_p()
+    st = load().laplex_plan_create_apply(ctypes.byref(h), _ptr(a), n, _ptr(phi), _ptr(psi), _ptr(x), _ptr(y),
+                                         batch, _stream(stream))
+    _check(st, "laplex_plan_create_apply")
+    return Plan(h, n, n, True, phi is not None, a.device), y
 
 
 def laplex_apply(plan: Plan, x, y=None, transpose: bool = False, stream=None):

@@ -77,6 +77,13 @@ def test_apply_and_gram_reject_bad_arguments():
     assert lib.laplex_plan_set_option(None, 1, 0) == lx.ERR_INVALID_ARGUMENT
     assert lib.laplex_plan_info(None, None, None, None) == lx.ERR_INVALID_ARGUMENT
     assert lib.laplex_plan_set_temperature(None, 1.0) == lx.ERR_INVALID_ARGUMENT
+    h = ctypes.c_void_p(1)
+    assert lib.laplex_plan_create_apply(ctypes.byref(h), FAKE, 10, None, None, None, FAKE, 1, None) == \
+        lx.ERR_INVALID_ARGUMENT and h.value is None
+    assert lib.laplex_plan_create_apply(ctypes.byref(h), FAKE, 10, None, None, FAKE, FAKE, 1, None) == \
+        lx.ERR_INVALID_ARGUMENT  # x and y overlap
+    assert lib.laplex_plan_create_apply(ctypes.byref(h), FAKE, 10, None, None, FAKE, ctypes.c_void_p(0x9000), 0,
+                                        None) == lx.ERR_INVALID_ARGUMENT
     assert lib.laplex_backward(None, FAKE, FAKE, 1, 0, FAKE, None, None, None, None, None) == \
         lx.ERR_INVALID_ARGUMENT
     for s in range(7):
