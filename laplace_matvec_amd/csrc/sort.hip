@@ -66,22 +66,31 @@ hipError_t fill_u32(uint32_t* p, uint32_t v, int64_t count, hipStream_t s)
     return hipSuccess;
 }
 
+// Digit histograms of all four passes in one read of the anchors.  Each
+// digit has kHistCopies copies in LDS, lane l counting into copy l % 8, rows
+// 257 words apart so that lanes of one wave hitting the same bin of a
+// concentrated digit (the sign and exponent byte of clustered anchors) land
+// on different banks and addresses.
+constexpr int kHistCopies = 8;
+constexpr int kHistRow = kRadix + 1;
+
 __global__ __launch_bounds__(kHistThreads) void lx_sort_hist(const float* __restrict__ a, int64_t n,
                                                             uint32_t* __restrict__ hist,
                                                             uint32_t* __restrict__ flag)
 {
-    __shared__ uint32_t h[4][kRadix];
-    for (int i = threadIdx.x; i < 4 * kRadix; i += kHistThreads) (&h[0][0])[i] = 0;
+    __shared__ uint32_t h[4][kHistCopies * kHistRow];
+    for (int i = threadIdx.x; i < 4 * kHistCopies * kHistRow; i += kHistThreads) (&h[0][0])[i] = 0;
     __syncthreads();
     uint32_t bad = 0;
+    const int copy = (lane_id() % kHistCopies) * kHistRow;
     auto count = [&](float f) {
         const uint32_t u = __float_as_uint(f);
         bad |= (~u & 0x7F800000u) == 0u;  // exponent all ones: NaN or Inf
         const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-        atomicAdd(&h[0][k & 0xFF], 1u);
-        atomicAdd(&h[1][(k >> 8) & 0xFF], 1u);
-        atomicAdd(&h[2][(k >> 16) & 0xFF], 1u);
-        atomicAdd(&h[3][k >> 24], 1u);
+        atomicAdd(&h[0][copy + (k & 0xFF)], 1u);
+        atomicAdd(&h[1][copy + ((k >> 8) & 0xFF)], 1u);
+        atomicAdd(&h[2][copy + ((k >> 16) & 0xFF)], 1u);
+        atomicAdd(&h[3][copy + (k >> 24)], 1u);
     };
     // four anchors per thread per step (16-byte loads), then the ragged tail
     const int64_t n4 = n / 4;
@@ -98,7 +107,10 @@ __global__ __launch_bounds__(kHistThreads) void lx_sort_hist(const float* __rest
     if (__any(bad) && lane_id() == 0) atomicOr(flag, 1u);
     __syncthreads();
     for (int i = threadIdx.x; i < 4 * kRadix; i += kHistThreads) {
-        const uint32_t c = (&h[0][0])[i];
+        const int d = i / kRadix, b = i % kRadix;
+        uint32_t c = 0;
+#pragma unroll
+        for (int q = 0; q < kHistCopies; ++q) c += h[d][q * kHistRow + b];
         if (c) atomicAdd(&hist[i], c);
     }
 }
