@@ -160,13 +160,24 @@ __global__ __launch_bounds__(kSortThreads) void lx_sort_pass(
     const uint32_t room = (uint32_t)(n - wbase < (int64_t)(kSortItems * kWave) ? (n > wbase ? n - wbase : 0)
                                                                                : (int64_t)(kSortItems * kWave));
     {
-        const float* ain = a_in + wbase;
-        const uint32_t* kin = keys_in + wbase;
+        // raw words first (all loads in flight together), keys after: a
+        // conversion next to each load would make every load wait for itself
+        const uint32_t* src = FIRST ? reinterpret_cast<const uint32_t*>(a_in) + wbase : keys_in + wbase;
+        if (room == (uint32_t)(kSortItems * kWave)) {
+#pragma unroll
+            for (int j = 0; j < kSortItems; ++j) key[j] = src[j * kWave + lane];
+        } else {
+#pragma unroll
+            for (int j = 0; j < kSortItems; ++j) {
+                const uint32_t off = (uint32_t)(j * kWave + lane);
+                key[j] = off < room ? src[off] : 0u;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < kSortItems; ++j) {
-            const uint32_t off = (uint32_t)(j * kWave + lane);
-            if (off < room) key[j] = FIRST ? key_of(ain[off]) : kin[off];
-            else key[j] = 0xFFFFFFFFu;
+            const bool valid = (uint32_t)(j * kWave + lane) < room;
+            if (FIRST) key[j] = key_of(__uint_as_float(key[j]));
+            key[j] = valid ? key[j] : 0xFFFFFFFFu;
         }
     }
 
@@ -503,21 +514,38 @@ __global__ __launch_bounds__(kSortThreads) void lx_replay(const T* __restrict__ 
     for (int64_t v = 0; v < batch; ++v) {
         const T* iv = in + v * in_ld;
         T* ov = out + v * out_ld;
+        // Every load of a step is issued before any of its values is used
+        // (whole tiles load unconditionally, gathers through a clamped index):
+        // a use next to a load inside a bounds branch makes each load wait
+        // for itself.
         if (FWD) {
+            T val[kReplayItems];
+            if (IOTA) {
 #pragma unroll
-            for (int q = 0; q < kReplayItems; ++q) {
-                const int j = q * kSortThreads + tid;
-                if (IOTA) buf[j] = (T)(t0 + j);
-                else buf[j] = (t0 + j < n) ? iv[t0 + j] : T(0);
+                for (int q = 0; q < kReplayItems; ++q) val[q] = (T)(t0 + q * kSortThreads + tid);
+            } else if (t0 + kSortTile <= n) {
+#pragma unroll
+                for (int q = 0; q < kReplayItems; ++q) val[q] = iv[t0 + q * kSortThreads + tid];
+            } else {
+#pragma unroll
+                for (int q = 0; q < kReplayItems; ++q) {
+                    const int64_t j = t0 + q * kSortThreads + tid;
+                    val[q] = iv[j < n ? j : n - 1];
+                }
             }
+#pragma unroll
+            for (int q = 0; q < kReplayItems; ++q) buf[q * kSortThreads + tid] = val[q];
             __syncthreads();
 #pragma unroll
             for (int q = 0; q < kReplayItems; ++q)
                 if (dst[q] < (uint32_t)n) ov[dst[q]] = buf[src[q]];
         } else {
+            T val[kReplayItems];
+#pragma unroll
+            for (int q = 0; q < kReplayItems; ++q) val[q] = iv[dst[q] < (uint32_t)n ? dst[q] : (uint32_t)(n - 1)];
 #pragma unroll
             for (int q = 0; q < kReplayItems; ++q)
-                if (dst[q] < (uint32_t)n) buf[src[q]] = iv[dst[q]];
+                if (dst[q] < (uint32_t)n) buf[src[q]] = val[q];
             __syncthreads();
 #pragma unroll
             for (int q = 0; q < kReplayItems; ++q) {
