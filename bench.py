@@ -168,7 +168,8 @@ def main():
 
         def step():
             plan, _ = lx.laplex_plan_create_apply(a, x, y)
-            st = lib.laplex_backward(plan.handle, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(g.data_ptr()),
+            # x = NULL: the plan kept the rows of x it sorted
+            st = lib.laplex_backward(plan.handle, None, ctypes.c_void_p(g.data_ptr()),
                                      batch, 0, ctypes.c_void_p(dx.data_ptr()), ctypes.c_void_p(da.data_ptr()),
                                      None, None, None, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
             if st != lx.OK:

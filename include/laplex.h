@@ -94,6 +94,8 @@ laplex_status laplex_plan_create(laplex_plan* out, const float* a, int64_t n,
  *   x per radix digit; otherwise it is plan_create followed by apply.
  *   Synchronizes `stream` once, like laplex_plan_create; *out receives the
  *   plan (NULL on error), which stays usable for apply, gram and backward.
+ *   The plan keeps its own copy of x (batch * n floats, sorted or as given)
+ *   for laplex_backward with x = NULL; it is released with the plan.
  */
 laplex_status laplex_plan_create_apply(laplex_plan* out, const float* a, int64_t n,
                                        const float* phi, const float* psi, const float* x,
@@ -137,7 +139,10 @@ laplex_status laplex_gram(laplex_plan plan, const float* D, float* M, void* stre
  *   the derivatives are those of the definition, entry by entry)
  *
  *   x      device float32 [batch][in]: the forward input ((in, out) as in
- *          laplex_apply).
+ *          laplex_apply).  NULL for a plan made by laplex_plan_create_apply
+ *          (then transpose = 0 and batch as in that call): the plan kept that
+ *          call's x, by rank when its rows travelled with the sort, so the
+ *          backward does not move x into sorted order again.
  *   g      device float32 [batch][out]: the upstream gradient dL/dy.
  *   dx     [batch][in]: dL/dx = K^T g (transpose = 0) or K g (transpose = 1).
  *   da     [n]: dL/da summed over the batch.  For y = K x,

@@ -248,6 +248,12 @@ struct laplex_plan_s {
     float* sphi0 = nullptr;
     float* cpsi0 = nullptr;
     float* spsi0 = nullptr;
+    // plan_create_apply keeps its input x for a later backward: the rows by
+    // rank (when they travelled with the sort; stride pad64(n)) or a copy in
+    // original order
+    float* kept_x = nullptr;
+    bool kept_by_rank = false;
+    int64_t kept_batch = 0;
     // workspace for apply / gram
     void* ws = nullptr;
     size_t ws_bytes = 0;
@@ -497,10 +503,23 @@ laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, cons
         V.ld = pad64(n);
     }
     const size_t vbytes = align256((size_t)V.rows * V.ld * 4);
-    LX_PLAN_TRY(dev_alloc(&scratch, lx::sort_scratch_bytes(big) + 2 * vbytes, p->device, s), "alloc sort scratch");
+    // value buffers: va and vb for the sort; when applying at once the sorted
+    // rows (vb) stay with the plan for a later backward, and a third buffer
+    // joins the ping-pong of the replay back into y
+    LX_PLAN_TRY(dev_alloc(&scratch, lx::sort_scratch_bytes(big) + 2 * vbytes, p->device, s),
+                "alloc sort scratch");
+    float* vt = nullptr;
     if (V.rows) {
         V.va = (float*)((char*)scratch + lx::sort_scratch_bytes(big));
-        V.vb = (float*)((char*)V.va + vbytes);
+        if (fuse) {
+            LX_PLAN_TRY(plan_alloc(p, (void**)&V.vb, vbytes, s), "alloc kept x");
+            vt = (float*)((char*)V.va + vbytes);
+            p->kept_x = V.vb;
+            p->kept_by_rank = true;
+            p->kept_batch = batch;
+        } else {
+            V.vb = (float*)((char*)V.va + vbytes);
+        }
     }
     LX_PLAN_TRY(lx::sort_launch(a, n, p->sa, p->ra, scratch, flag, s, V.rows ? &V : nullptr), "sort a");
     if (sym) {
@@ -535,8 +554,8 @@ laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, cons
             A.inv_t = p->inv_t;
             A.s = p->sa;
             A.random = false;
-            A.xs = V.vb;
-            A.ys = V.vb;
+            A.xs = V.vb;  // kept: y by rank goes to va
+            A.ys = V.va;
             if (p->phased) {
                 A.in_c = p->cpsi;
                 A.in_s = p->spsi;
@@ -545,10 +564,10 @@ laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, cons
             }
             LX_PLAN_TRY(lx::scan_launch(A, s), "symmetric apply");
             const lx::SortRecords& R = p->ra;
-            LX_PLAN_TRY(lx::replay_launch(R, 3, false, V.vb, V.ld, V.va, V.ld, batch, s), "replay");
-            LX_PLAN_TRY(lx::replay_launch(R, 2, false, V.va, V.ld, V.vb, V.ld, batch, s), "replay");
-            LX_PLAN_TRY(lx::replay_launch(R, 1, false, V.vb, V.ld, V.va, V.ld, batch, s), "replay");
-            LX_PLAN_TRY(lx::replay_launch(R, 0, false, V.va, V.ld, y, n, batch, s), "replay");
+            LX_PLAN_TRY(lx::replay_launch(R, 3, false, V.va, V.ld, vt, V.ld, batch, s), "replay");
+            LX_PLAN_TRY(lx::replay_launch(R, 2, false, vt, V.ld, V.va, V.ld, batch, s), "replay");
+            LX_PLAN_TRY(lx::replay_launch(R, 1, false, V.va, V.ld, vt, V.ld, batch, s), "replay");
+            LX_PLAN_TRY(lx::replay_launch(R, 0, false, vt, V.ld, y, n, batch, s), "replay");
         }
     } else {
         LX_PLAN_TRY(plan_alloc(p, (void**)&p->sb, (size_t)k * 4, s), "alloc sorted b");
@@ -590,8 +609,18 @@ laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, cons
     if (host_flag & 1u) return bail(fail(LAPLEX_ERR_NONFINITE_ANCHOR, "NaN or Inf among anchors or phases"));
 #undef LX_PLAN_TRY
     if (x && !fuse) {
-        // not fused (short side or too many rows): the plain apply
-        const laplex_status st2 = laplex_apply(p, x, y, batch, 0, stream);
+        // not fused (short side or too many rows): the plain apply, and a copy
+        // of x kept for a later backward
+        laplex_status st2 = laplex_apply(p, x, y, batch, 0, stream);
+        if (st2 == LAPLEX_OK) {
+            float* keep = nullptr;
+            st2 = from_hip(plan_alloc(p, (void**)&keep, (size_t)(batch * n) * 4, s), "alloc kept x");
+            if (st2 == LAPLEX_OK)
+                st2 = from_hip(hipMemcpyAsync(keep, x, (size_t)(batch * n) * 4, hipMemcpyDeviceToDevice, s), "copy x");
+            p->kept_x = keep;
+            p->kept_by_rank = false;
+            p->kept_batch = batch;
+        }
         if (st2 != LAPLEX_OK) {
             plan_release(p);
             return st2;
@@ -916,9 +945,16 @@ laplex_status laplex_backward(laplex_plan p, const float* x, const float* g, int
                               float* dx, float* da, float* db, float* dphi, float* dpsi, void* stream)
 {
     if (!p) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "plan is NULL");
-    if (!x || !g) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "x or g is NULL");
+    if (!g) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "g is NULL");
     if (batch < 1) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "batch must be >= 1");
     if (transpose != 0 && transpose != 1) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "transpose must be 0 or 1");
+    // x == NULL: the input kept by laplex_plan_create_apply (y = K x, so transpose 0)
+    const bool use_kept = x == nullptr;
+    if (use_kept && !p->kept_x) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "x is NULL and the plan keeps no input");
+    if (use_kept && (transpose != 0 || batch != p->kept_batch))
+        return fail(LAPLEX_ERR_INVALID_ARGUMENT, "the kept input is for transpose = 0 and its own batch");
+    const bool kept_by_rank = use_kept && p->kept_by_rank;
+    if (use_kept && !kept_by_rank) x = p->kept_x;
     if (p->sym && db) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "symmetric plan: the gradient of b = a is in da");
     if (!p->phased && (dphi || dpsi)) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "unphased plan has no phase gradients");
     const int64_t len_in = transpose ? p->n : p->k;
@@ -935,7 +971,7 @@ laplex_status laplex_backward(laplex_plan p, const float* x, const float* g, int
     for (int i = 0; i < 5; ++i) {
         if (!outs[i].p) continue;
         for (int j = 0; j < 2; ++j)
-            if (ranges_overlap(outs[i].p, outs[i].bytes, ins[j].p, ins[j].bytes))
+            if (ins[j].p && ranges_overlap(outs[i].p, outs[i].bytes, ins[j].p, ins[j].bytes))
                 return fail(LAPLEX_ERR_INVALID_ARGUMENT, "an output overlaps x or g");
         for (int j = i + 1; j < 5; ++j)
             if (outs[j].p && ranges_overlap(outs[i].p, outs[i].bytes, outs[j].p, outs[j].bytes))
@@ -952,7 +988,7 @@ laplex_status laplex_backward(laplex_plan p, const float* x, const float* g, int
 
     if (p->sym) {
         const int64_t n = p->n;
-        const bool replay = n >= replay_min();
+        const bool replay = kept_by_rank || n >= replay_min();
         if (!replay) LX_TRY(ensure_perm(p, 0, s), "permutation");
         const int64_t ld = pad64(n);
         const int64_t tiles = (n + lx::kScanTile - 1) / lx::kScanTile;
@@ -1003,14 +1039,24 @@ laplex_status laplex_backward(laplex_plan p, const float* x, const float* g, int
         // u, w -> sorted order (rows [0, B) and [B, 2B)), gradient by rank into
         // t1, then the wanted rows back to original order.
         const lx::SortRecords& R = p->ra;
-        LX_TRY(lx::replay_launch(R, 0, true, u, n, t1, ld, batch, s), "replay");
-        LX_TRY(lx::replay_launch(R, 0, true, w, n, t1 + batch * ld, ld, batch, s), "replay");
-        LX_TRY(lx::replay_launch(R, 1, true, t1, ld, t2, ld, 2 * batch, s), "replay");
-        LX_TRY(lx::replay_launch(R, 2, true, t2, ld, t1, ld, 2 * batch, s), "replay");
-        LX_TRY(lx::replay_launch(R, 3, true, t1, ld, t2, ld, 2 * batch, s), "replay");
         A.random = false;
-        A.us = t2;
-        A.ws = t2 + batch * ld;
+        if (kept_by_rank) {
+            // w = x is already by rank: only u travels
+            LX_TRY(lx::replay_launch(R, 0, true, u, n, t1, ld, batch, s), "replay");
+            LX_TRY(lx::replay_launch(R, 1, true, t1, ld, t2, ld, batch, s), "replay");
+            LX_TRY(lx::replay_launch(R, 2, true, t2, ld, t1, ld, batch, s), "replay");
+            LX_TRY(lx::replay_launch(R, 3, true, t1, ld, t2, ld, batch, s), "replay");
+            A.us = t2;
+            A.ws = p->kept_x;
+        } else {
+            LX_TRY(lx::replay_launch(R, 0, true, u, n, t1, ld, batch, s), "replay");
+            LX_TRY(lx::replay_launch(R, 0, true, w, n, t1 + batch * ld, ld, batch, s), "replay");
+            LX_TRY(lx::replay_launch(R, 1, true, t1, ld, t2, ld, 2 * batch, s), "replay");
+            LX_TRY(lx::replay_launch(R, 2, true, t2, ld, t1, ld, 2 * batch, s), "replay");
+            LX_TRY(lx::replay_launch(R, 3, true, t1, ld, t2, ld, 2 * batch, s), "replay");
+            A.us = t2;
+            A.ws = t2 + batch * ld;
+        }
         int64_t row = 0;
         float* user[4] = {dx, da, dphi, dpsi};
         int64_t first[4], count[4];

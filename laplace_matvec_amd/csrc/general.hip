@@ -343,14 +343,16 @@ __global__ __launch_bounds__(kGenThreads) void lx_eval(EvalArgs A, int VG, int g
         tl = lds + pad64(ni);
         tr = tl + ni * VG * C;
         for (int64_t i = threadIdx.x; i < ni; i += kGenThreads) s_l[i] = A.s_in[i];
+        // rows of the tables in global memory are read along t (coalesced)
         for (int64_t i = threadIdx.x; i < ni * VG * C; i += kGenThreads) {
-            const int64_t t = i / (VG * C);
-            const int64_t rem = i - t * (VG * C);
-            const int64_t vi = rem / C;
-            const int64_t c = rem - vi * C;
+            const int64_t row = i / ni;  // vi * C + c
+            const int64_t t = i - row * ni;
+            const int64_t vi = row / C;
+            const int64_t c = row - vi * C;
             const int64_t src = (c * A.batch + v0 + vi) * A.ld + t;
-            tl[i] = vi < nv ? A.pl[src] : 0.f;
-            tr[i] = vi < nv ? A.pr[src] : 0.f;
+            const int64_t dst = (t * VG + vi) * C + c;
+            tl[dst] = vi < nv ? A.pl[src] : 0.f;
+            tr[dst] = vi < nv ? A.pr[src] : 0.f;
         }
         __syncthreads();
         si = s_l;

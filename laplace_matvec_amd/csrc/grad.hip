@@ -80,10 +80,78 @@ __device__ __forceinline__ void grad_load_uw(const GradSymArgs& A, int64_t vec, 
     }
 }
 
+// Per-tile totals of several scan rows with one barrier: each wave folds
+// its lanes (in lane order for forward rows, reversed for backward rows),
+// lane 63 / lane 0 leave the wave's composite in LDS, and after the barrier
+// one thread per row folds the waves.
+template <int R>
+__device__ __forceinline__ void wave_totals(const Aff<double> (&f)[R], const Aff<double> (&b)[R], Aff<double>* sh)
+{
+    const int lane = lane_id();
+    const int w = (int)threadIdx.x / kWave;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const Aff<double> fi = wave_scan_up(f[r]);
+        const Aff<double> bi = wave_scan_down(b[r]);
+        if (lane == kWave - 1) sh[(w * R + r) * 2] = fi;
+        if (lane == 0) sh[(w * R + r) * 2 + 1] = bi;
+    }
+}
+
+// Exclusive block scans of two forward rows and two backward rows with one
+// barrier.  `sh` holds two buffers of [waves][4] composites used by turns
+// (`parity`), so the next call needs no second barrier before writing.
+__device__ __forceinline__ void block_exscan4(Aff<double> f0, Aff<double> f1, Aff<double> b0, Aff<double> b1,
+                                              Aff<double>* sh, int parity, Aff<double>& xf0, Aff<double>& xf1,
+                                              Aff<double>& xb0, Aff<double>& xb1)
+{
+    const int lane = lane_id();
+    const int w = (int)threadIdx.x / kWave;
+    Aff<double>* buf = sh + parity * (kGradWaves * 4);
+    const Aff<double> if0 = wave_scan_up(f0), if1 = wave_scan_up(f1);
+    const Aff<double> ib0 = wave_scan_down(b0), ib1 = wave_scan_down(b1);
+    Aff<double> ef0{__shfl_up(if0.m, 1), __shfl_up(if0.v, 1)};
+    Aff<double> ef1{__shfl_up(if1.m, 1), __shfl_up(if1.v, 1)};
+    Aff<double> eb0{__shfl_down(ib0.m, 1), __shfl_down(ib0.v, 1)};
+    Aff<double> eb1{__shfl_down(ib1.m, 1), __shfl_down(ib1.v, 1)};
+    if (lane == 0) ef0 = ef1 = aff_identity<double>();
+    if (lane == kWave - 1) eb0 = eb1 = aff_identity<double>();
+    if (lane == kWave - 1) {
+        buf[w * 4 + 0] = if0;
+        buf[w * 4 + 1] = if1;
+    }
+    if (lane == 0) {
+        buf[w * 4 + 2] = ib0;
+        buf[w * 4 + 3] = ib1;
+    }
+    __syncthreads();
+    Aff<double> pf0 = aff_identity<double>(), pf1 = aff_identity<double>();
+    Aff<double> pb0 = aff_identity<double>(), pb1 = aff_identity<double>();
+#pragma unroll
+    for (int i = 0; i < kGradWaves; ++i) {
+        if (i < w) {
+            pf0 = compose(pf0, buf[i * 4 + 0]);
+            pf1 = compose(pf1, buf[i * 4 + 1]);
+        }
+    }
+#pragma unroll
+    for (int i = kGradWaves - 1; i >= 0; --i) {
+        if (i > w) {
+            pb0 = compose(pb0, buf[i * 4 + 2]);
+            pb1 = compose(pb1, buf[i * 4 + 3]);
+        }
+    }
+    xf0 = compose(pf0, ef0);
+    xf1 = compose(pf1, ef1);
+    xb0 = compose(pb0, eb0);
+    xb1 = compose(pb1, eb1);
+}
+
 template <int C, bool RANDOM>
 __global__ __launch_bounds__(kGradThreads) void lx_grad_sym_reduce(GradSymArgs A)
 {
-    __shared__ Aff<double> sh[kGradWaves];
+    constexpr int R = 4 * C;  // rows: half h, channel c, kind (decay, tie)
+    __shared__ Aff<double> sh[kGradWaves * R * 2];
     const int64_t vec = blockIdx.x / A.tiles;
     const int64_t tile = blockIdx.x - vec * A.tiles;
     const int64_t n = A.n;
@@ -98,6 +166,7 @@ __global__ __launch_bounds__(kGradThreads) void lx_grad_sym_reduce(GradSymArgs A
         store_run<kGradItems>(A.us + vec * A.ld, r0, n, uu);
         store_run<kGradItems>(A.ws + vec * A.ld, r0, n, ww);
     }
+    Aff<double> fr[R], br[R];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         float fc[kGradItems], fs[kGradItems];
@@ -122,18 +191,25 @@ __global__ __launch_bounds__(kGradThreads) void lx_grad_sym_reduce(GradSymArgs A
 #pragma unroll
                 for (int i = kGradItems - 1; i >= 0; --i)
                     b = compose(b, Aff<double>{kind == 0 ? e[i + 1] : tie_mult(ties, i + 1), (double)val[i]});
-                Aff<double> ft, bt;
-                (void)block_exscan_up<double, kGradWaves>(f, sh, ft);
-                (void)block_exscan_down<double, kGradWaves>(b, sh, bt);
-                if (threadIdx.x == 0) {
-                    double* ag = A.agg + (grad_row(C, h, c, kind, A.batch, vec) * A.tiles + tile) * 4;
-                    ag[0] = ft.m;
-                    ag[1] = ft.v;
-                    ag[2] = bt.m;
-                    ag[3] = bt.v;
-                }
+                fr[(h * C + c) * 2 + kind] = f;
+                br[(h * C + c) * 2 + kind] = b;
             }
         }
+    }
+    wave_totals<R>(fr, br, sh);
+    __syncthreads();
+    if (threadIdx.x < 2 * R) {
+        // thread t folds row t / 2 forward (even t) or backward (odd t) over the waves
+        const int row = (int)threadIdx.x / 2, dir = (int)threadIdx.x & 1;
+        Aff<double> acc = aff_identity<double>();
+        if (dir == 0)
+            for (int w = 0; w < kGradWaves; ++w) acc = compose(acc, sh[(w * R + row) * 2]);
+        else
+            for (int w = kGradWaves - 1; w >= 0; --w) acc = compose(acc, sh[(w * R + row) * 2 + 1]);
+        const int h = row / (2 * C), c = (row / 2) % C, kind = row % 2;
+        double* ag = A.agg + (grad_row(C, h, c, kind, A.batch, vec) * A.tiles + tile) * 4;
+        ag[2 * dir] = acc.m;
+        ag[2 * dir + 1] = acc.v;
     }
 }
 
@@ -180,9 +256,10 @@ __device__ __forceinline__ void grad_store_out(const GradSymArgs& A, float* dst,
 // and tie masks are re-read from LDS in it, which keeps one step's state
 // live at a time.
 template <int C, bool RANDOM, int H>
-__global__ __launch_bounds__(kGradThreads) void lx_grad_sym_apply(GradSymArgs A)
+__global__ __launch_bounds__(kGradThreads, 4) void lx_grad_sym_apply(GradSymArgs A)
 {
-    __shared__ Aff<double> sh[kGradWaves];
+    __shared__ Aff<double> sh[2 * kGradWaves * 4];
+    int parity = 0;
     __shared__ double se[kScanTile + 1];
     __shared__ uint32_t st[kGradThreads];
     const int64_t tile = blockIdx.x;
@@ -252,11 +329,9 @@ __global__ __launch_bounds__(kGradThreads) void lx_grad_sym_apply(GradSymArgs A)
                 bd = compose(bd, Aff<double>{e[i + 1], (double)val[i]});
                 bt = compose(bt, Aff<double>{tie_mult(ties, i + 1), (double)val[i]});
             }
-            Aff<double> tot;
-            const Aff<double> fxd = block_exscan_up<double, kGradWaves>(fd, sh, tot);
-            const Aff<double> bxd = block_exscan_down<double, kGradWaves>(bd, sh, tot);
-            const Aff<double> fxt = block_exscan_up<double, kGradWaves>(ft, sh, tot);
-            const Aff<double> bxt = block_exscan_down<double, kGradWaves>(bt, sh, tot);
+            Aff<double> fxd, fxt, bxd, bxt;
+            block_exscan4(fd, ft, bd, bt, sh, parity, fxd, fxt, bxd, bxt);
+            parity ^= 1;
             const double* cd = A.carry + (grad_row(C, H, c, 0, A.batch, vec) * A.tiles + tile) * 2;
             const double* ct = A.carry + (grad_row(C, H, c, 1, A.batch, vec) * A.tiles + tile) * 2;
             double L = fxd.m * cd[0] + fxd.v;

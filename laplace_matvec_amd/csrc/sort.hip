@@ -431,7 +431,7 @@ hipError_t sort_launch(const float* a, int64_t n, float* sorted, const SortRecor
 constexpr int kReplayItems = kSortTile / kSortThreads;  // 16
 
 template <typename T, bool FWD, bool IOTA>
-__global__ __launch_bounds__(kSortThreads) void lx_replay(const T* __restrict__ in, int64_t in_ld,
+__global__ __launch_bounds__(kSortThreads, 6) void lx_replay(const T* __restrict__ in, int64_t in_ld,
                                                          T* __restrict__ out, int64_t out_ld,
                                                          const uint16_t* __restrict__ rec,
                                                          const uint32_t* __restrict__ tab_base,
@@ -519,22 +519,30 @@ __global__ __launch_bounds__(kSortThreads) void lx_replay(const T* __restrict__ 
         // a use next to a load inside a bounds branch makes each load wait
         // for itself.
         if (FWD) {
-            T val[kReplayItems];
-            if (IOTA) {
+            static_assert(sizeof(T) == 4, "32-bit elements");
+            if (!IOTA && t0 + kSortTile <= n && ((uintptr_t)(iv + t0) & 15) == 0) {
+                // whole aligned tile: four 16-byte loads per thread, lanes contiguous
+                const uint4* src4 = reinterpret_cast<const uint4*>(iv + t0);
+                uint4 w4[kReplayItems / 4];
 #pragma unroll
-                for (int q = 0; q < kReplayItems; ++q) val[q] = (T)(t0 + q * kSortThreads + tid);
-            } else if (t0 + kSortTile <= n) {
+                for (int q = 0; q < kReplayItems / 4; ++q) w4[q] = src4[q * kSortThreads + tid];
 #pragma unroll
-                for (int q = 0; q < kReplayItems; ++q) val[q] = iv[t0 + q * kSortThreads + tid];
+                for (int q = 0; q < kReplayItems / 4; ++q) reinterpret_cast<uint4*>(buf)[q * kSortThreads + tid] = w4[q];
             } else {
+                // ragged or unaligned tile: rounds of 8 loads in flight
+                constexpr int kHalf = kReplayItems / 2;
 #pragma unroll
-                for (int q = 0; q < kReplayItems; ++q) {
-                    const int64_t j = t0 + q * kSortThreads + tid;
-                    val[q] = iv[j < n ? j : n - 1];
+                for (int h = 0; h < 2; ++h) {
+                    T val[kHalf];
+#pragma unroll
+                    for (int q = 0; q < kHalf; ++q) {
+                        const int64_t j = t0 + (h * kHalf + q) * kSortThreads + tid;
+                        val[q] = IOTA ? (T)j : iv[j < n ? j : n - 1];
+                    }
+#pragma unroll
+                    for (int q = 0; q < kHalf; ++q) buf[(h * kHalf + q) * kSortThreads + tid] = val[q];
                 }
             }
-#pragma unroll
-            for (int q = 0; q < kReplayItems; ++q) buf[q * kSortThreads + tid] = val[q];
             __syncthreads();
 #pragma unroll
             for (int q = 0; q < kReplayItems; ++q)

@@ -206,23 +206,26 @@ def laplex_plan_set_temperature(plan: Plan, t: float):
 
 def laplex_backward(plan: Plan, x, g, transpose: bool = False, want=("dx", "da", "db", "dphi", "dpsi"),
                     stream=None) -> dict:
-    """Gradients of a step through y = K x (or K^T x): x the forward input,
-    g = dL/dy.  Returns the requested tensors among dx ([batch][in]), da [n],
+    """Gradients of a step through y = K x (or K^T x): x the forward input
+    (None for a plan from laplex_plan_create_apply, which kept it), g = dL/dy.  Returns the requested tensors among dx ([batch][in]), da [n],
     db [k] (general plans), dphi [n], dpsi [k] (phased plans); entries a plan
     does not have are left out."""
-    x = _dev_f32(x, "x")
     g = _dev_f32(g, "g")
     n_in, n_out = (plan.n, plan.k) if transpose else (plan.k, plan.n)
-    one = x.dim() == 1
-    batch = 1 if one else x.shape[0]
-    if x.shape[-1] != n_in or x.dim() > 2:
-        raise ValueError(f"x must have shape [batch][{n_in}]")
+    if x is None:  # the input kept by laplex_plan_create_apply
+        shape = (n_in,) if g.dim() == 1 else (g.shape[0], n_in)
+    else:
+        x = _dev_f32(x, "x")
+        shape = tuple(x.shape)
+        if x.shape[-1] != n_in or x.dim() > 2:
+            raise ValueError(f"x must have shape [batch][{n_in}]")
+    batch = 1 if len(shape) == 1 else shape[0]
     if g.numel() != batch * n_out or g.shape[-1] != n_out:
         raise ValueError(f"g must have shape [batch][{n_out}]")
-    dev = x.device
+    dev = g.device
     out = {}
     if "dx" in want:
-        out["dx"] = torch.empty(x.shape, dtype=torch.float32, device=dev)
+        out["dx"] = torch.empty(shape, dtype=torch.float32, device=dev)
     if "da" in want:
         out["da"] = torch.empty(plan.n, dtype=torch.float32, device=dev)
     if "db" in want and not plan.symmetric:

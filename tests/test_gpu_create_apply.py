@@ -69,3 +69,34 @@ def test_create_apply_rejects_nonfinite(gpu):
     with pytest.raises(lx.LaplexError) as e:
         lx.laplex_plan_create_apply(dev(np.arange(n)), dev(np.ones(n)), phi=dev(phi), psi=dev(np.zeros(n)))
     assert e.value.status == lx.ERR_NONFINITE_ANCHOR
+
+
+@pytest.mark.parametrize("n,batch,phased", [(3000, 2, True), ((1 << 20) + 77, 2, False), ((1 << 20) + 77, 1, True)])
+def test_backward_with_kept_input(gpu, n, batch, phased):
+    # plan_create_apply keeps x: backward(x=None) equals backward(x) bit for bit
+    print(f"[kept x backward] n={n} batch={batch} phased={phased}", flush=True)
+    rng = np.random.default_rng(n + 3 * batch)
+    a = (rng.standard_normal(n) * 30).astype(np.float32)
+    a[rng.integers(0, n, n // 9)] = a[rng.integers(0, n, n // 9)]
+    phi = rng.uniform(-np.pi, np.pi, n).astype(np.float32) if phased else None
+    psi = rng.uniform(-np.pi, np.pi, n).astype(np.float32) if phased else None
+    x = rng.standard_normal((batch, n)).astype(np.float32)
+    g = rng.standard_normal((batch, n)).astype(np.float32)
+    P = None if phi is None else dev(phi)
+    Q = None if psi is None else dev(psi)
+    plan, _ = lx.laplex_plan_create_apply(dev(a), dev(x), phi=P, psi=Q)
+    with plan:
+        kept = {k: host(v) for k, v in lx.laplex_backward(plan, None, dev(g)).items()}
+        given = {k: host(v) for k, v in lx.laplex_backward(plan, dev(x), dev(g)).items()}
+        with pytest.raises(lx.LaplexError) as e:
+            lx.laplex_backward(plan, None, dev(g), transpose=True)
+        assert e.value.status == lx.ERR_INVALID_ARGUMENT
+    assert set(kept) == set(given)
+    for k in kept:
+        assert np.array_equal(kept[k], given[k]), k
+    ref = oracle.grad_dense(a, g, x, phi=phi, psi=psi, rows=np.arange(0, n, max(1, n // 300)))
+    assert oracle.rel_l2(kept["da"][::max(1, n // 300)], ref["da"]) < TOL
+    with lx.laplex_plan_create(dev(a)) as p2:
+        with pytest.raises(lx.LaplexError) as e:
+            lx.laplex_backward(p2, None, dev(g))
+        assert e.value.status == lx.ERR_INVALID_ARGUMENT
