@@ -3,8 +3,9 @@
 
 Default workload (the headline measurement): symmetric apply y = K(a, a) x
 at n = 2^30, float32, one vector, a ~ 1e4 N(0,1) and x ~ N(0,1) drawn on the
-device (Philox4x32-10), timed END TO END: plan creation (radix argsort of
-the anchors) + apply (gather, prefix/suffix scans, scatter) + plan release.
+device (Philox4x32-10), timed END TO END with laplex_plan_create_apply: the
+radix argsort of the anchors (x travelling through its passes), the prefix
+and suffix scans, the replay of y back to original order, plan release.
 
 One step = one pass of the whole path over the resident inputs.  W untimed
 warm-up steps, then K timed steps between device synchronizations; kernel
@@ -12,7 +13,8 @@ durations come from HIP events recorded by the library around each launch
 in the same timed region.  Rank 0 prints one JSON line.
 
 Other workloads (for the record, not the headline line): --workload
-c1 | c2 | c3 | c4 (see laplace_matvec_amd/workloads.py).
+c1 | c2 | c3 | c4 (see laplace_matvec_amd/workloads.py); --backward times a
+training step (forward product plus its backward pass) instead.
 """
 from __future__ import annotations
 
@@ -39,7 +41,7 @@ def parse():
     p.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--n", type=int, default=None, help="override n (testing only)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=1 << 25)
+    p.add_argument("--cpu-sample", type=int, default=1 << 26)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (counter calibration)")
     p.add_argument("--backward", action="store_true",
