@@ -506,11 +506,11 @@ laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, cons
     // value buffers: va and vb for the sort; when applying at once the sorted
     // rows (vb) stay with the plan for a later backward, and a third buffer
     // joins the ping-pong of the replay back into y
-    LX_PLAN_TRY(dev_alloc(&scratch, lx::sort_scratch_bytes(big) + 2 * vbytes, p->device, s),
+    LX_PLAN_TRY(dev_alloc(&scratch, lx::sort_scratch_bytes(big, V.rows > 0) + 2 * vbytes, p->device, s),
                 "alloc sort scratch");
     float* vt = nullptr;
     if (V.rows) {
-        V.va = (float*)((char*)scratch + lx::sort_scratch_bytes(big));
+        V.va = (float*)((char*)scratch + lx::sort_scratch_bytes(big, V.rows > 0));
         if (fuse) {
             LX_PLAN_TRY(plan_alloc(p, (void**)&V.vb, vbytes, s), "alloc kept x");
             vt = (float*)((char*)V.va + vbytes);

@@ -61,7 +61,7 @@ struct SortValPass {  // kernel argument: one pass's row pointers
     const float* in[kMaxSortVals] = {};
     float* out[kMaxSortVals] = {};
 };
-size_t sort_scratch_bytes(int64_t n);   // temporary, during the sort
+size_t sort_scratch_bytes(int64_t n, bool with_vals = false);  // temporary, during the sort
 size_t sort_record_bytes(int64_t n);    // kept by the plan
 SortRecords sort_records_at(void* base, int64_t n);
 // Stable argsort of a[0..n): sorted[r] = a[perm[r]] for the permutation the

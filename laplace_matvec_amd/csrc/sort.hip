@@ -127,16 +127,17 @@ __global__ __launch_bounds__(kRadix) void lx_sort_scan_hist(const uint32_t* __re
 }
 
 template <bool FIRST, bool LAST, bool VALS>
-__global__ __launch_bounds__(kSortThreads) void lx_sort_pass(
+__global__ __launch_bounds__(kSortThreads, 4) void lx_sort_pass(
     const float* __restrict__ a_in, const uint32_t* __restrict__ keys_in, uint32_t* __restrict__ keys_out,
-    float* __restrict__ sorted_out, uint16_t* __restrict__ rec, uint32_t* __restrict__ tab_base,
+    const uint2* __restrict__ kv_in, uint2* __restrict__ kv_out, float* __restrict__ sorted_out, uint16_t* __restrict__ rec, uint32_t* __restrict__ tab_base,
     uint16_t* __restrict__ tab_start, const uint32_t* __restrict__ bin_base, uint32_t* __restrict__ state,
     uint32_t* __restrict__ ticket, int shift, int64_t n, SortValPass vals)
 {
     __shared__ uint16_t s_hist[kSortWaves][kRadix];  // per-wave counts, then wave offsets (<= tile size)
     __shared__ uint32_t s_start[kRadix];             // tile-local start of each bin
-    __shared__ uint32_t s_glob[kRadix];              // global position of each bin's first key
+    __shared__ uint32_t s_off[kRadix];               // global position of slot 0 of each bin's run
     __shared__ uint32_t s_buf[kSortTile];
+    __shared__ float s_val[VALS ? kSortTile : 1];    // one value row in slot order
     __shared__ uint32_t s_red[kSortWaves];
     __shared__ uint32_t s_tile;
 
@@ -154,8 +155,17 @@ __global__ __launch_bounds__(kSortThreads) void lx_sort_pass(
     // Keys in wave-striped order: item j of lane l is tile position
     // wpos + 64 j + l, so a wave's items in (j, lane) order are its keys in
     // index order.  Positions past n get the largest key: they rank last,
-    // in bin 255, and land past n.
+    // in bin 255, and land past n.  The first value row is loaded with the
+    // keys, so its latency overlaps the ranking and the look-back.
+    //
+    // With value rows, the passes between the first and the last move each
+    // key together with the first row's value as one 8-byte pair: a tile's
+    // scattered output is then one run per bin instead of two, half as many
+    // partly written cache lines.
+    constexpr bool PAIR_IN = VALS && !FIRST;
+    constexpr bool PAIR_OUT = VALS && !LAST;
     uint32_t key[kSortItems];
+    float v0[VALS ? kSortItems : 1];
     const int64_t wbase = tile0 + wpos;  // uniform
     const uint32_t room = (uint32_t)(n - wbase < (int64_t)(kSortItems * kWave) ? (n > wbase ? n - wbase : 0)
                                                                                : (int64_t)(kSortItems * kWave));
@@ -163,14 +173,46 @@ __global__ __launch_bounds__(kSortThreads) void lx_sort_pass(
         // raw words first (all loads in flight together), keys after: a
         // conversion next to each load would make every load wait for itself
         const uint32_t* src = FIRST ? reinterpret_cast<const uint32_t*>(a_in) + wbase : keys_in + wbase;
+        const float* vin = VALS && !PAIR_IN ? vals.in[0] + wbase : nullptr;
+        const uint2* pin = PAIR_IN ? kv_in + wbase : nullptr;
         if (room == (uint32_t)(kSortItems * kWave)) {
+            if (PAIR_IN) {
 #pragma unroll
-            for (int j = 0; j < kSortItems; ++j) key[j] = src[j * kWave + lane];
+                for (int j = 0; j < kSortItems; ++j) {
+                    const uint2 kv = pin[j * kWave + lane];
+                    key[j] = kv.x;
+                    v0[j] = __uint_as_float(kv.y);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < kSortItems; ++j) key[j] = src[j * kWave + lane];
+                if (VALS) {
+#pragma unroll
+                    for (int j = 0; j < kSortItems; ++j) v0[j] = vin[j * kWave + lane];
+                }
+            }
         } else {
+            if (PAIR_IN) {
 #pragma unroll
-            for (int j = 0; j < kSortItems; ++j) {
-                const uint32_t off = (uint32_t)(j * kWave + lane);
-                key[j] = off < room ? src[off] : 0u;
+                for (int j = 0; j < kSortItems; ++j) {
+                    const uint32_t off = (uint32_t)(j * kWave + lane);
+                    const uint2 kv = off < room ? pin[off] : make_uint2(0u, 0u);
+                    key[j] = kv.x;
+                    v0[j] = __uint_as_float(kv.y);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < kSortItems; ++j) {
+                    const uint32_t off = (uint32_t)(j * kWave + lane);
+                    key[j] = off < room ? src[off] : 0u;
+                }
+                if (VALS) {
+#pragma unroll
+                    for (int j = 0; j < kSortItems; ++j) {
+                        const uint32_t off = (uint32_t)(j * kWave + lane);
+                        v0[j] = off < room ? vin[off] : 0.f;
+                    }
+                }
             }
         }
 #pragma unroll
@@ -214,12 +256,29 @@ __global__ __launch_bounds__(kSortThreads) void lx_sort_pass(
     if (tid < kRadix) s_start[tid] = start;
     __syncthreads();
 
-    // Place keys in the tile's digit order (slots) while earlier tiles finish.
+    // Slots in the tile's digit order.  The replay record (the tile position
+    // each slot came from) depends on nothing outside the tile: it is
+    // written before the look-back, while earlier tiles finish.
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
         const uint32_t d = (key[j] >> shift) & 0xFFu;
         pos[j] += s_start[d] + s_hist[w][d];
+        s_buf[pos[j]] = (uint32_t)(wpos + j * kWave + lane);
+    }
+    __syncthreads();
+    {
+        uint32_t* rec2 = reinterpret_cast<uint32_t*>(rec + tile0);
+#pragma unroll
+        for (int q = 0; q < kSortItems / 2; ++q) {
+            const uint32_t i = (uint32_t)(q * kSortThreads + tid);  // pair of slots 2i, 2i+1
+            rec2[i] = s_buf[2 * i] | (s_buf[2 * i + 1] << 16);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSortItems; ++j) {
         s_buf[pos[j]] = key[j];
+        if (VALS) s_val[pos[j]] = v0[j];
     }
 
     // Decoupled look-back, kLookback predecessors per round: sum their own
@@ -257,59 +316,59 @@ __global__ __launch_bounds__(kSortThreads) void lx_sort_pass(
             st_agent(state + (int64_t)tile * kRadix + tid, 0x80000000u | (before + count));
         }
         const uint32_t base = bin_base[tid] + before;
-        s_glob[tid] = base;
         // replay table: slot i of bin b goes to global position base_b + i
+        s_off[tid] = base - start;
         tab_base[(int64_t)tile * kRadix + tid] = base - start;
         tab_start[(int64_t)tile * kRadix + tid] = (uint16_t)start;
     }
     __syncthreads();
 
-    // Consecutive slots of one digit go to consecutive global positions.
-    uint32_t dsts[VALS ? kSortItems : 1];
+    // Consecutive slots of one digit go to consecutive global positions;
+    // the first value row goes out with its keys.
+    float* vout0 = VALS && !PAIR_OUT ? vals.out[0] : nullptr;
 #pragma unroll
     for (int q = 0; q < kSortItems; ++q) {
         const uint32_t i = (uint32_t)(q * kSortThreads + tid);
         const uint32_t k = s_buf[i];
-        const uint32_t d = (k >> shift) & 0xFFu;
-        const uint32_t dst = s_glob[d] + (i - s_start[d]);
-        if (VALS) dsts[q] = dst;
+        const uint32_t dst = s_off[(k >> shift) & 0xFFu] + i;
         if (dst < (uint32_t)n) {
-            if (LAST) sorted_out[dst] = float_of_key(k);
-            else keys_out[dst] = k;
+            if (PAIR_OUT) {
+                kv_out[dst] = make_uint2(k, __float_as_uint(s_val[i]));
+            } else {
+                if (LAST) sorted_out[dst] = float_of_key(k);
+                else keys_out[dst] = k;
+                if (VALS) vout0[dst] = s_val[i];
+            }
         }
     }
-    __syncthreads();
-    // Value rows travel with the keys: loaded like the keys, placed in the
-    // same slots, written to the same destinations.
+    // Further value rows: loaded like the keys, placed in the same slots,
+    // written to the destinations of the keys still held in the slots.
     if (VALS) {
-        float* fbuf = reinterpret_cast<float*>(s_buf);
-        for (int r = 0; r < vals.rows; ++r) {
+        for (int r = 1; r < vals.rows; ++r) {
             const float* vin = vals.in[r] + wbase;
             float v[kSortItems];
+            if (room == (uint32_t)(kSortItems * kWave)) {
 #pragma unroll
-            for (int j = 0; j < kSortItems; ++j) {
-                const uint32_t off = (uint32_t)(j * kWave + lane);
-                v[j] = off < room ? vin[off] : 0.f;
+                for (int j = 0; j < kSortItems; ++j) v[j] = vin[j * kWave + lane];
+            } else {
+#pragma unroll
+                for (int j = 0; j < kSortItems; ++j) {
+                    const uint32_t off = (uint32_t)(j * kWave + lane);
+                    v[j] = off < room ? vin[off] : 0.f;
+                }
             }
+            __syncthreads();
 #pragma unroll
-            for (int j = 0; j < kSortItems; ++j) fbuf[pos[j]] = v[j];
+            for (int j = 0; j < kSortItems; ++j) s_val[pos[j]] = v[j];
             __syncthreads();
             float* vout = vals.out[r];
 #pragma unroll
-            for (int q = 0; q < kSortItems; ++q)
-                if (dsts[q] < (uint32_t)n) vout[dsts[q]] = fbuf[q * kSortThreads + tid];
-            __syncthreads();
+            for (int q = 0; q < kSortItems; ++q) {
+                const uint32_t i = (uint32_t)(q * kSortThreads + tid);
+                const uint32_t dst = s_off[(s_buf[i] >> shift) & 0xFFu] + i;
+                if (dst < (uint32_t)n) vout[dst] = s_val[i];
+            }
         }
-    }
-    // Replay record: the tile position each slot came from.
-#pragma unroll
-    for (int j = 0; j < kSortItems; ++j) s_buf[pos[j]] = (uint32_t)(wpos + j * kWave + lane);
-    __syncthreads();
-    uint32_t* rec2 = reinterpret_cast<uint32_t*>(rec + tile0);
-#pragma unroll
-    for (int q = 0; q < kSortItems / 2; ++q) {
-        const uint32_t i = (uint32_t)(q * kSortThreads + tid);  // pair of slots 2i, 2i+1
-        rec2[i] = s_buf[2 * i] | (s_buf[2 * i + 1] << 16);
     }
 }
 
@@ -318,16 +377,17 @@ __global__ __launch_bounds__(kSortThreads) void lx_sort_pass(
 //   hist, base                 : uint32[4][256] each
 //   tickets                    : uint32[4] (padded to 64)
 //   state                      : uint32[4][tiles][256]
+//   pairB (with value rows)    : uint2[n]; pairA overlays keysA + keysB
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-size_t sort_scratch_bytes(int64_t n)
+size_t sort_scratch_bytes(int64_t n, bool with_vals)
 {
     const int64_t tiles = (n + kSortTile - 1) / kSortTile;
-    size_t b = 0;
-    b += 2 * align256((size_t)n * 4);
+    size_t b = 2 * align256((size_t)n * 4);
     b += 2 * align256(4 * kRadix * 4);
     b += align256(64 * 4);
     b += align256((size_t)4 * tiles * kRadix * 4);
+    if (with_vals) b += align256((size_t)n * 8);
     return b;
 }
 
@@ -364,7 +424,11 @@ hipError_t sort_launch(const float* a, int64_t n, float* sorted, const SortRecor
     uint32_t* hist = (uint32_t*)p; p += align256(4 * kRadix * 4);
     uint32_t* base = (uint32_t*)p; p += align256(4 * kRadix * 4);
     uint32_t* tickets = (uint32_t*)p; p += align256(64 * 4);
-    uint32_t* state = (uint32_t*)p;
+    uint32_t* state = (uint32_t*)p; p += align256((size_t)4 * tiles * kRadix * 4);
+    // key-value pairs (with value rows): keysA and keysB together hold one
+    // array of n pairs, the region after the look-back state the other
+    uint2* pairA = reinterpret_cast<uint2*>(keysA);
+    uint2* pairB = reinterpret_cast<uint2*>(p);
 
     // hist, base and tickets are contiguous: clear them and the state together
     const int64_t clear_words = (int64_t)((char*)state - (char*)hist) / 4 + 4 * tiles * kRadix;
@@ -396,11 +460,14 @@ hipError_t sort_launch(const float* a, int64_t n, float* sorted, const SortRecor
     const int64_t st = tiles * kRadix;
     const uint32_t* kin[4] = {nullptr, keysA, keysB, keysA};
     uint32_t* kout[4] = {keysA, keysB, keysA, nullptr};
+    const uint2* pin[4] = {nullptr, pairA, pairB, pairA};
+    uint2* pout[4] = {pairA, pairB, pairA, nullptr};
     for (int k = 0; k < 4; ++k) {
 #define LX_PASS(F, L, V)                                                                                      \
     LX_LAUNCH("sort_pass", s,                                                                                 \
               (lx_sort_pass<F, L, V><<<grid, kSortThreads, 0, s>>>(                                          \
-                  k == 0 ? a : nullptr, kin[k], kout[k], k == 3 ? sorted : nullptr, R.rec[k], R.base[k],      \
+                  k == 0 ? a : nullptr, kin[k], kout[k], hv ? pin[k] : nullptr, hv ? pout[k] : nullptr,       \
+                  k == 3 ? sorted : nullptr, R.rec[k], R.base[k],                                            \
                   R.start[k], base + k * kRadix, state + k * st, tickets + k, 8 * k, n, vp[k])))
         if (hv) {
             if (k == 0) LX_PASS(true, false, true);
