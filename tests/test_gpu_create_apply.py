@@ -100,3 +100,44 @@ def test_backward_with_kept_input(gpu, n, batch, phased):
         with pytest.raises(lx.LaplexError) as e:
             lx.laplex_backward(p2, None, dev(g))
         assert e.value.status == lx.ERR_INVALID_ARGUMENT
+
+
+def _anchors(kind, n, rng):
+    if kind == "one_bin":  # every key in one top-digit bin: the last radix pass keeps tiles whole
+        return (1.0 + rng.random(n)).astype(np.float32)
+    if kind == "wide":  # signs and exponents spread over many top-digit bins
+        return (rng.standard_normal(n) * 10.0 ** rng.uniform(-6, 6, n)).astype(np.float32)
+    if kind == "ties":  # few distinct values: long equal runs, decay 1
+        a = rng.integers(-40, 40, n).astype(np.float32) * 0.25
+        a[rng.integers(0, n, 64)] = -0.0
+        return a
+    if kind == "equal":
+        return np.full(n, 3.5, np.float32)
+    if kind == "gaps":  # far apart clusters: decays underflow between them
+        return (rng.integers(0, 8, n) * 2000.0 + rng.random(n)).astype(np.float32)
+    return (rng.standard_normal(n) * 1e4).astype(np.float32)
+
+
+@pytest.mark.parametrize("kind,n", [
+    ("normal", (1 << 20) + 1), ("normal", (3 << 20) + 12345), ("one_bin", (1 << 20) + 8191),
+    ("wide", (2 << 20) + 4097), ("ties", (1 << 20) + 77), ("equal", 1 << 20), ("gaps", (1 << 21) + 3),
+])
+def test_create_apply_anchor_layouts(gpu, kind, n):
+    # one row at n >= 2^20 (x travels through the radix passes) for anchor
+    # layouts that stress the sort's bins and the scans' decays, against the
+    # fp64 sweep of the oracle
+    print(f"[create_apply layouts] kind={kind} n={n}", flush=True)
+    rng = np.random.default_rng(n)
+    a = _anchors(kind, n, rng)
+    x = rng.standard_normal((1, n)).astype(np.float32)
+    plan, y = lx.laplex_plan_create_apply(dev(a), dev(x))
+    with plan:
+        y = host(y)
+        y_again = host(lx.laplex_apply(plan, dev(x)))
+    ref = oracle.apply_sweep(a, x)
+    assert oracle.rel_l2(y[0], ref[0]) < TOL
+    assert oracle.rel_l2(y_again[0], ref[0]) < TOL
+    # deterministic: a second plan gives the same bits
+    plan2, y2 = lx.laplex_plan_create_apply(dev(a), dev(x))
+    with plan2:
+        assert np.array_equal(host(y2), y)
