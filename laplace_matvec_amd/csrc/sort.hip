@@ -92,11 +92,27 @@ __global__ __launch_bounds__(kHistThreads) void lx_sort_hist(const float* __rest
         atomicAdd(&h[2][copy + ((k >> 16) & 0xFF)], 1u);
         atomicAdd(&h[3][copy + (k >> 24)], 1u);
     };
-    // four anchors per thread per step (16-byte loads), then the ragged tail
+    // sixteen anchors per thread per step: four 16-byte loads issued before
+    // any is counted (counting next to each load would make every load wait
+    // for itself), then single float4s, then the ragged tail
     const int64_t n4 = n / 4;
     const float4* a4 = reinterpret_cast<const float4*>(a);
     const int64_t stride = (int64_t)gridDim.x * kHistThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kHistThreads + threadIdx.x; i < n4; i += stride) {
+    constexpr int kHistBatch = 4;
+    int64_t i = (int64_t)blockIdx.x * kHistThreads + threadIdx.x;
+    for (; i + (kHistBatch - 1) * stride < n4; i += kHistBatch * stride) {
+        float4 v[kHistBatch];
+#pragma unroll
+        for (int q = 0; q < kHistBatch; ++q) v[q] = a4[i + q * stride];
+#pragma unroll
+        for (int q = 0; q < kHistBatch; ++q) {
+            count(v[q].x);
+            count(v[q].y);
+            count(v[q].z);
+            count(v[q].w);
+        }
+    }
+    for (; i < n4; i += stride) {
         const float4 v = a4[i];
         count(v.x);
         count(v.y);
