@@ -68,6 +68,21 @@ __device__ __forceinline__ uint64_t match_bits(uint32_t d)
 }
 __device__ __forceinline__ uint64_t match_digit8(uint32_t d) { return match_bits<8>(d); }
 
+// Workgroups of a launch are dealt to the compute dies (8 XCDs, each with
+// its own L2) in turn: workgroup b runs on die b % 8.  For launches whose
+// workgroups are independent, this bijection of [0, tiles) gives the
+// workgroups of one die a contiguous range of tiles, taken in order, so
+// neighbouring tiles share an L2 (their partly covered cache lines at the
+// seams are fetched or merged once).  Any other dispatch only changes the
+// order in which tiles are done.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t tiles)
+{
+    constexpr int64_t kDies = 8;
+    const int64_t q = tiles / kDies, r = tiles % kDies;
+    const int64_t x = b % kDies, j = b / kDies;
+    return x < r ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
+
 template <class T>
 struct Aff {
     T m, v;

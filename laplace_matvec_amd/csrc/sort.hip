@@ -528,7 +528,7 @@ __global__ __launch_bounds__(kSortThreads, 6) void lx_replay(const T* __restrict
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int w = tid / kWave;
-    const int64_t tile = blockIdx.x;
+    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);  // grid = tiles
     const int64_t t0 = tile * kSortTile;
 
     uint32_t src[kReplayItems];
