@@ -889,12 +889,96 @@ struct GradSide {
     const float* anchor_o;
     const float* c_o0;  // cos/sin of side o's phases, original order (phased)
     const float* s_o0;
+    const float* s_o;       // side o sorted, and its permutation (rank -> original index)
+    const uint32_t* p_o;
+    const float* anchor_i0; // side i's anchors and phase factors, original order
+    const float* c_i0;
+    const float* s_i0;
 };
+
+// Outputs on a small side (at most 1024 anchors) from a large input side:
+// the inputs are bucketed into the intervals of the sorted outputs, in
+// their original order (no gather, no tables over the large side).
+laplex_status grad_small_side(laplex_plan p, const GradSide& G, const float* V, const float* W, int64_t batch,
+                              float* y, float* d_anchor, float* d_phase, hipStream_t s, bool* done)
+{
+    *done = false;
+    const int ch = p->phased ? 2 : 1;
+    lx::BucketArgs Bk;
+    Bk.channels = ch;
+    Bk.n_out = G.no;
+    Bk.n_in = G.ni;
+    Bk.batch = batch;
+    Bk.inv_t = (float)p->inv_t;
+    Bk.s_out = G.s_o;
+    Bk.in_anchor = G.anchor_i0;
+    if (p->phased) {
+        Bk.in_cos = G.c_i0;
+        Bk.in_sin = G.s_i0;
+    }
+    Bk.x = V;
+    Bk.ld = pad64(G.no);
+    Bk.lds_bytes = p->lds_bytes;
+    Bk.ties = true;
+    Bk.partial_floats = lx::bucket_partial_floats(Bk, nullptr, nullptr);
+    if (Bk.partial_floats == 0) return LAPLEX_OK;  // not the LDS-binned shape: the table path instead
+    const size_t rows = (size_t)ch * batch * Bk.ld;
+    const size_t need = scan_ws_bytes(G.no, batch, ch, 0, 2) + 3 * align256(rows * 4) +
+                        align256((size_t)Bk.partial_floats * 4);
+    LX_TRY(ensure_ws(p, need, s), "workspace");
+    Carve cv(p->ws);
+    lx::ScanArgs A;
+    A.mode = lx::kScanUVLR;
+    A.random = false;
+    scan_common(A, cv, G.no, batch, ch);
+    A.inv_t = p->inv_t;
+    A.s = G.s_o;
+    float* u = cv.take<float>(rows);
+    float* v = cv.take<float>(rows);
+    float* tie = cv.take<float>(rows);
+    A.u = u;
+    A.v = v;
+    A.pl = cv.take<float>((size_t)ch * batch * A.ld);
+    A.pr = cv.take<float>((size_t)ch * batch * A.ld);
+    Bk.u = u;
+    Bk.v = v;
+    Bk.tie = tie;
+    Bk.partial = cv.take<float>((size_t)Bk.partial_floats);
+    LX_TRY(lx::bucket_launch(Bk, s), "bucket inputs");
+    LX_TRY(lx::scan_launch(A, s), "scan over the output side");
+    lx::EvalLRArgs E;
+    E.channels = ch;
+    E.n_out = G.no;
+    E.batch = batch;
+    E.ld = A.ld;
+    E.anchor_scale = p->temperature > 0.0 ? (float)(-1.0 / p->temperature) : 0.f;
+    E.s_out = G.s_o;
+    E.perm_out = G.p_o;
+    if (p->phased) {
+        E.out_cos = G.c_o0;
+        E.out_sin = G.s_o0;
+    }
+    E.L = A.pl;
+    E.R = A.pr;
+    E.T = tie;
+    E.w = W;
+    E.y = y;
+    E.d_anchor = d_anchor;
+    E.d_phase = d_phase;
+    LX_TRY(lx::eval_lr_launch(E, s), "evaluate gradients");
+    *done = true;
+    return LAPLEX_OK;
+}
 
 laplex_status grad_general_side(laplex_plan p, const GradSide& G, const float* V, const float* W, int64_t batch,
                                 float* y, float* d_anchor, float* d_phase, hipStream_t s)
 {
     if (!y && !d_anchor && !d_phase) return LAPLEX_OK;
+    if (G.no <= 1024 && G.ni > G.no) {
+        bool done = false;
+        const laplex_status st = grad_small_side(p, G, V, W, batch, y, d_anchor, d_phase, s, &done);
+        if (st != LAPLEX_OK || done) return st;
+    }
     const int ch = p->phased ? 2 : 1;
     LX_TRY(ensure_ws(p, scan_ws_bytes(G.ni, batch, ch, 1, 2), s), "workspace");
     Carve cv(p->ws);
@@ -1082,8 +1166,10 @@ laplex_status laplex_backward(laplex_plan p, const float* x, const float* g, int
     // General plan: outputs on a from the tables of b, outputs on b from those of a.
     LX_TRY(ensure_perm(p, 0, s), "permutation of a");
     LX_TRY(ensure_perm(p, 1, s), "permutation of b");
-    GradSide on_a{p->n, p->k, p->sb, p->pb, p->cpsi, p->spsi, p->a0, p->cphi0, p->sphi0};
-    GradSide on_b{p->k, p->n, p->sa, p->pa, p->cphi, p->sphi, p->b0, p->cpsi0, p->spsi0};
+    GradSide on_a{p->n, p->k, p->sb, p->pb, p->cpsi, p->spsi, p->a0, p->cphi0, p->sphi0,
+                  p->sa, p->pa, p->b0, p->cpsi0, p->spsi0};
+    GradSide on_b{p->k, p->n, p->sa, p->pa, p->cphi, p->sphi, p->b0, p->cpsi0, p->spsi0,
+                  p->sb, p->pb, p->a0, p->cphi0, p->sphi0};
     laplex_status st = grad_general_side(p, on_a, w, u, batch, transpose ? dx : nullptr, da, dphi, s);
     if (st != LAPLEX_OK) return st;
     return grad_general_side(p, on_b, u, w, batch, transpose ? nullptr : dx, db, dpsi, s);

@@ -8,6 +8,8 @@
 //     u_t     += exp(-(s_t - q)) x      reaches every rank >= t via L,
 //     v_{t-1} += exp(-(q - s_{t-1})) x  reaches every rank <= t-1 via R,
 // so each output receives the input exactly once, including ties q = s_r.
+// For gradients the ties are also summed apart (tie_t += x for q = s_t):
+// the signed product leaves them out.
 //
 // Kernels here:
 //   lx_bucket_sorted + lx_bucket_reduce : u, v when the sorted output side
@@ -52,7 +54,7 @@ constexpr int kBucketVG = 8;                    // vectors per workgroup (max)
 
 __device__ __forceinline__ uint64_t match_bits11(uint32_t d) { return match_bits<11>(d); }
 
-template <int C>
+template <int C, bool TIES>
 __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, int VG, int groups,
                                                                int64_t chunk_len)
 {
@@ -64,6 +66,7 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, in
     uint32_t* start = reinterpret_cast<uint32_t*>(wcnt + pad64(kGenWaves * nbins));    // [nbins+1]
     float4* coef = reinterpret_cast<float4*>(start + pad64(nbins + 1));                // [kSub]: (au0, au1, bv0, bv1)
     float4* xs = coef + kSub;                                                          // [kSub][2]: 8 vectors
+    uint8_t* tflag = reinterpret_cast<uint8_t*>(xs + 2 * kSub);                        // [kSub] (TIES): q == s_t
     __shared__ uint32_t sred[kGenWaves];
 
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
@@ -74,10 +77,15 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, in
     for (int i = tid; i < no; i += kGenThreads) so[i] = A.s_out[i];
 
     float au[kBucketVG][C], av[kBucketVG][C];  // u_tid and v_tid of each vector
+    float at[TIES ? kBucketVG : 1][C];         // tie_tid
 #pragma unroll
     for (int vi = 0; vi < kBucketVG; ++vi)
 #pragma unroll
         for (int c = 0; c < C; ++c) au[vi][c] = av[vi][c] = 0.f;
+#pragma unroll
+    for (int vi = 0; vi < (TIES ? kBucketVG : 1); ++vi)
+#pragma unroll
+        for (int c = 0; c < C; ++c) at[vi][c] = 0.f;
 
     const int64_t j0 = chunk * chunk_len;
     int64_t j1 = j0 + chunk_len;
@@ -88,15 +96,18 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, in
         // this thread's items: element sub0 + 128 w + 64 j + lane (wave-striped)
         int64_t idx[kSubItems];
         uint32_t tt[kSubItems], slot[kSubItems];
+        bool tie[kSubItems];
         float4 cf[kSubItems];
 #pragma unroll
         for (int j = 0; j < kSubItems; ++j) {
             idx[j] = sub0 + w * (kSubItems * kWave) + j * kWave + lane;
             float al = 0.f, be = 0.f, f0 = 1.f, f1 = 0.f;
             uint32_t t = (uint32_t)no;  // past the end: weight 0 in the last interval
+            tie[j] = false;
             if (idx[j] < j1) {
                 const float q = A.in_anchor[idx[j]];
                 t = (uint32_t)lower_bound_f(so, no, q);
+                tie[j] = t < (uint32_t)no && so[t] == q;
                 al = t < (uint32_t)no ? decay_f(q, so[t], A.inv_t) : 0.f;
                 be = t > 0 ? decay_f(so[t - 1], q, A.inv_t) : 0.f;
                 if (C == 2) {
@@ -149,6 +160,7 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, in
         for (int j = 0; j < kSubItems; ++j) {
             const uint32_t sl = slot[j] + start[tt[j]] + wcnt[w * nbins + tt[j]];
             coef[sl] = cf[j];
+            if (TIES) tflag[sl] = tie[j] ? 1 : 0;
             float xv[kBucketVG];
 #pragma unroll
             for (int vi = 0; vi < kBucketVG; ++vi)
@@ -168,6 +180,14 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, in
                     au[vi][0] = fmaf(f.x, xv[vi], au[vi][0]);
                     if (C == 2) au[vi][C - 1] = fmaf(f.y, xv[vi], au[vi][C - 1]);
                 }
+                if (TIES) {  // a tie's alpha is exactly 1: its factors are the phase's cos, sin
+                    const float tw = tflag[sl] ? 1.f : 0.f;
+#pragma unroll
+                    for (int vi = 0; vi < (TIES ? kBucketVG : 1); ++vi) {
+                        at[vi][0] = fmaf(tw * f.x, xv[vi], at[vi][0]);
+                        if (C == 2) at[vi][C - 1] = fmaf(tw * f.y, xv[vi], at[vi][C - 1]);
+                    }
+                }
             }
             for (uint32_t sl = s1; sl < s2; ++sl) {  // interval tid+1: beta parts -> v_tid
                 const float4 f = coef[sl];
@@ -182,43 +202,49 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, in
         }
         __syncthreads();
     }
-    // partial layout [chunk][batch][C][2][no]
+    // partial layout [chunk][batch][C][P][no], P = 2 (u, v) or 3 (u, v, tie)
+    constexpr int P = TIES ? 3 : 2;
     if (tid < no) {
 #pragma unroll
         for (int vi = 0; vi < kBucketVG; ++vi)
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 if (vi >= nv) continue;
-                float* pp = A.partial + ((chunk * A.batch + v0 + vi) * C + c) * 2 * no;
+                float* pp = A.partial + ((chunk * A.batch + v0 + vi) * C + c) * P * no;
                 pp[tid] = au[vi][c];
                 pp[no + tid] = av[vi][c];
+                if (TIES) pp[2 * no + tid] = at[TIES ? vi : 0][c];
             }
     }
 }
 
-static size_t bucket_sorted_lds(int64_t no, int C)
+static size_t bucket_sorted_lds(int64_t no, int C, bool ties)
 {
     (void)C;
     const int64_t nbins = no + 1;
-    return (size_t)(pad64(no) + pad64(kGenWaves * nbins) / 2 + pad64(nbins + 1)) * 4 + (size_t)kSub * 16 * 3;
+    return (size_t)(pad64(no) + pad64(kGenWaves * nbins) / 2 + pad64(nbins + 1)) * 4 + (size_t)kSub * 16 * 3 +
+           (ties ? (size_t)kSub : 0);
 }
 
+// Sums the per-workgroup partials in chunk order (float64) into u, v and,
+// with P = 3, the tie sums.
 __global__ __launch_bounds__(256) void lx_bucket_reduce(const float* __restrict__ partial, int64_t chunks,
-                                                       int64_t batch, int C, int64_t no, int64_t ld,
-                                                       float* __restrict__ u, float* __restrict__ v)
+                                                       int64_t batch, int C, int P, int64_t no, int64_t ld,
+                                                       float* __restrict__ u, float* __restrict__ v,
+                                                       float* __restrict__ tie)
 {
-    const int64_t total = batch * C * 2 * no;
+    const int64_t total = batch * C * P * no;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
         double acc = 0.0;
         for (int64_t ch = 0; ch < chunks; ++ch) acc += (double)partial[ch * total + i];
         const int64_t t = i % no;
         int64_t rest = i / no;
-        const int w = (int)(rest % 2);
-        rest /= 2;
+        const int w = (int)(rest % P);
+        rest /= P;
         const int64_t c = rest % C;
         const int64_t vv = rest / C;
-        (w == 0 ? u : v)[(c * batch + vv) * ld + t] = (float)acc;
+        (w == 0 ? u : (w == 1 ? v : tie))[(c * batch + vv) * ld + t] = (float)acc;
     }
 }
 
@@ -243,6 +269,7 @@ __global__ __launch_bounds__(256) void lx_bucket_global(BucketArgs A)
                 const int64_t row = ((int64_t)c * A.batch + vv) * A.ld;
                 if (t < no) atomicAdd(A.u + row + t, al * val);
                 if (t > 0) atomicAdd(A.v + row + t - 1, be * val);
+                if (A.ties && t < no && A.s_out[t] == q) atomicAdd(A.tie + row + t, val);
             }
         }
     }
@@ -251,7 +278,7 @@ __global__ __launch_bounds__(256) void lx_bucket_global(BucketArgs A)
 static void bucket_shape(const BucketArgs& a, int* vg, int* groups, int* chunks, int64_t* chunk_len)
 {
     const bool fits = a.n_out <= kGenThreads && a.lds_bytes > 0 &&
-                      (int64_t)bucket_sorted_lds(a.n_out, a.channels) <= a.lds_bytes;
+                      (int64_t)bucket_sorted_lds(a.n_out, a.channels, a.ties) <= a.lds_bytes;
     if (!fits) {
         *vg = 0;
         *groups = *chunks = 0;
@@ -282,7 +309,7 @@ int64_t bucket_partial_floats(const BucketArgs& a, int* groups, int* chunks)
     if (groups) *groups = g;
     if (chunks) *chunks = c;
     if (vg == 0) return 0;
-    return (int64_t)c * a.batch * a.channels * 2 * a.n_out;
+    return (int64_t)c * a.batch * a.channels * (a.ties ? 3 : 2) * a.n_out;
 }
 
 hipError_t bucket_launch(BucketArgs& a, hipStream_t s)
@@ -292,30 +319,45 @@ hipError_t bucket_launch(BucketArgs& a, hipStream_t s)
     int64_t chunk_len;
     bucket_shape(a, &vg, &groups, &chunks, &chunk_len);
     const bool two = a.channels == 2;
+    const bool ties = a.ties;
+    if (ties && !a.tie) return hipErrorInvalidValue;
     if (vg > 0 && a.partial && a.n_in > 0) {
-        const size_t shmem = bucket_sorted_lds(a.n_out, a.channels);
+        const size_t shmem = bucket_sorted_lds(a.n_out, a.channels, ties);
         const unsigned blocks = (unsigned)((int64_t)chunks * groups);
+#define LX_BKS(CC, TT)                                                                                         \
+    do {                                                                                                       \
+        (void)hipFuncSetAttribute((const void*)lx_bucket_sorted<CC, TT>, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                  (int)shmem);                                                                 \
+        LX_LAUNCH("bucket_sorted", s,                                                                          \
+                  (lx_bucket_sorted<CC, TT><<<blocks, kGenThreads, shmem, s>>>(a, vg, groups, chunk_len)));     \
+    } while (0)
         if (two) {
-            (void)hipFuncSetAttribute((const void*)lx_bucket_sorted<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-            LX_LAUNCH("bucket_sorted", s, (lx_bucket_sorted<2><<<blocks, kGenThreads, shmem, s>>>(a, vg, groups, chunk_len)));
+            if (ties) LX_BKS(2, true);
+            else LX_BKS(2, false);
         } else {
-            (void)hipFuncSetAttribute((const void*)lx_bucket_sorted<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-            LX_LAUNCH("bucket_sorted", s, (lx_bucket_sorted<1><<<blocks, kGenThreads, shmem, s>>>(a, vg, groups, chunk_len)));
+            if (ties) LX_BKS(1, true);
+            else LX_BKS(1, false);
         }
-        const int64_t total = a.batch * a.channels * 2 * a.n_out;
+#undef LX_BKS
+        const int P = ties ? 3 : 2;
+        const int64_t total = a.batch * a.channels * P * a.n_out;
         int64_t rb = (total + 255) / 256;
         if (rb > 8192) rb = 8192;
         LX_LAUNCH("bucket_reduce", s,
-                  (lx_bucket_reduce<<<(unsigned)rb, 256, 0, s>>>(a.partial, chunks, a.batch, a.channels,
-                                                                 a.n_out, a.ld, a.u, a.v)));
+                  (lx_bucket_reduce<<<(unsigned)rb, 256, 0, s>>>(a.partial, chunks, a.batch, a.channels, P,
+                                                                 a.n_out, a.ld, a.u, a.v, a.tie)));
         return hipSuccess;
     }
-    // global path: clear u and v, then accumulate with device atomics
+    // global path: clear u, v (and the tie sums), then accumulate with device atomics
     const int64_t words = (int64_t)a.channels * a.batch * a.ld;
     hipError_t e = fill_u32((uint32_t*)a.u, 0u, words, s);
     if (e != hipSuccess) return e;
     e = fill_u32((uint32_t*)a.v, 0u, words, s);
     if (e != hipSuccess) return e;
+    if (ties) {
+        e = fill_u32((uint32_t*)a.tie, 0u, words, s);
+        if (e != hipSuccess) return e;
+    }
     if (a.n_in <= 0) return hipSuccess;
     int64_t blocks = (a.n_in + 255) / 256;
     if (blocks > 8192) blocks = 8192;

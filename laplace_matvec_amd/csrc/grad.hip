@@ -521,4 +521,53 @@ hipError_t eval_grad_launch(const EvalGradArgs& a, hipStream_t s)
     return hipSuccess;
 }
 
+// A small output side (the sorted bucketing path): one thread per output,
+// in sorted order, over every vector.  With L the left part including ties
+// (ties were bucketed into the left interval), R the strict right part and T
+// the ties: K0 = L + R, S0 = (L - T) - R.
+template <int C>
+__global__ __launch_bounds__(256) void lx_eval_grad_lr(EvalLRArgs A)
+{
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= A.n_out) return;
+    const float o = A.s_out[j];
+    const int64_t first = lower_bound_f(A.s_out, A.n_out, o);  // ties were summed at the run's first rank
+    const int64_t i = A.perm_out[j];
+    float oc = 1.f, os = 0.f;
+    if (C == 2) {
+        oc = A.out_cos[i];
+        os = A.out_sin[i];
+    }
+    float acc_a = 0.f, acc_p = 0.f;
+    for (int64_t v = 0; v < A.batch; ++v) {
+        float sig = 0.f, kin = 0.f, pla = 0.f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int64_t row = ((int64_t)c * A.batch + v) * A.ld;
+            const float lv = A.L[row + j], rv = A.R[row + j], tv = A.T[row + first];
+            const float k0 = lv + rv;
+            const float s0 = (lv - tv) - rv;
+            const float fo = c == 0 ? oc : os;
+            sig = fmaf(fo, s0, sig);
+            pla = fmaf(fo, k0, pla);
+            if (C == 2) kin = fmaf(c == 0 ? os : -oc, k0, kin);
+        }
+        const float wt = A.w[v * A.n_out + i];
+        acc_a = fmaf(wt, sig, acc_a);
+        acc_p = fmaf(-wt, kin, acc_p);
+        if (A.y) A.y[v * A.n_out + i] = pla;
+    }
+    if (A.d_anchor) A.d_anchor[i] = A.anchor_scale * acc_a;
+    if (C == 2 && A.d_phase) A.d_phase[i] = acc_p;
+}
+
+hipError_t eval_lr_launch(const EvalLRArgs& a, hipStream_t s)
+{
+    if (a.n_out <= 0 || a.batch <= 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((a.n_out + 255) / 256);
+    if (a.channels == 2) LX_LAUNCH("eval_grad", s, (lx_eval_grad_lr<2><<<blocks, 256, 0, s>>>(a)));
+    else LX_LAUNCH("eval_grad", s, (lx_eval_grad_lr<1><<<blocks, 256, 0, s>>>(a)));
+    return hipSuccess;
+}
+
 }  // namespace lx

@@ -88,6 +88,7 @@ enum ScanMode : int {
     kScanSym = 0,   // values x (by rank); output L + U - x
     kScanUV = 1,    // forward stream u, backward stream v (by rank); output L + R
     kScanPLPR = 2,  // values x (by rank); outputs L and U kept apart, by rank
+    kScanUVLR = 3,  // forward stream u, backward stream v (by rank); outputs L and R kept apart
 };
 
 struct ScanArgs {
@@ -140,6 +141,8 @@ struct BucketArgs {
     int64_t ld = 0;                  // row stride of u, v
     float* u = nullptr;              // [channels][batch][ld] (overwritten)
     float* v = nullptr;
+    bool ties = false;               // also sum the inputs equal to s_out[t], at t, into `tie`
+    float* tie = nullptr;            // same layout as u (when ties)
     float* partial = nullptr;        // scratch for the LDS-binned path
     int64_t partial_floats = 0;
     int lds_bytes = 0;               // LDS budget per workgroup (0: global path)
@@ -220,6 +223,29 @@ struct EvalGradArgs {
     int lds_bytes = 0;
 };
 hipError_t eval_grad_launch(const EvalGradArgs& a, hipStream_t s);
+// The same outputs for a small output side from interval sums of the input
+// side: with the outputs sorted (s_out, perm_out: rank -> original index),
+// L = strict-and-tied left part, R = strict right part (both by rank, from
+// the u / v scan) and T = the tie sums at the first rank of each run of
+// equal outputs.
+struct EvalLRArgs {
+    int channels = 1;
+    int64_t n_out = 0, batch = 0;
+    int64_t ld = 0;                     // row stride of L, R, T: [channels][batch][ld]
+    float anchor_scale = -1.f;          // -1/t (0 at t = 0)
+    const float* s_out = nullptr;       // sorted outputs [n_out]
+    const uint32_t* perm_out = nullptr; // rank -> original index
+    const float* out_cos = nullptr;     // output phases, original order (phased)
+    const float* out_sin = nullptr;
+    const float* L = nullptr;
+    const float* R = nullptr;
+    const float* T = nullptr;
+    const float* w = nullptr;           // output-side weights [batch][n_out], original order
+    float* y = nullptr;                 // plain product [batch][n_out], or null
+    float* d_anchor = nullptr;          // [n_out], or null
+    float* d_phase = nullptr;           // [n_out], or null
+};
+hipError_t eval_lr_launch(const EvalLRArgs& a, hipStream_t s);
 
 // ---- Gram (gram.hip) ----
 struct GramArgs {

@@ -9,7 +9,8 @@
 // each O(n) work and O(log n) depth as a scan of affine maps.  Both parts
 // contain the diagonal, so the symmetric product is L + U - x.  For a != b
 // the values are the interval sums u (forward) and v (backward) and the
-// product is L + R.  The "evaluate" path keeps L and U apart (PL, PR).
+// product is L + R.  The "evaluate" path keeps L and U apart (PL, PR), and
+// the gradient of a small output side keeps L and R apart (UV in, PL/PR out).
 //
 // Reduce-then-scan (every workgroup runs to completion without waiting on
 // another, and the combine tree is fixed, so results are deterministic):
@@ -48,7 +49,7 @@ __device__ __forceinline__ void load_values(const ScanArgs& A, int64_t vec, int6
                                             float (&fv)[C][kScanItems], float (&bv)[C][kScanItems])
 {
     const int64_t n = A.n;
-    if (MODE == kScanUV) {
+    if (MODE == kScanUV || MODE == kScanUVLR) {
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             load_run<kScanItems>(A.u + row_off(A, c, vec), r0, n, fv[c]);
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(kScanThreads) void lx_scan_apply(ScanArgs A)
             L = e[i] * L + (double)fv[c][i];
             Lr[i] = L;
         }
-        if (MODE == kScanPLPR) {
+        if (MODE == kScanPLPR || MODE == kScanUVLR) {
             float pl[kScanItems], pr[kScanItems];
 #pragma unroll
             for (int i = kScanItems - 1; i >= 0; --i) {
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(kScanThreads) void lx_scan_apply(ScanArgs A)
             }
         }
     }
-    if (MODE != kScanPLPR) {
+    if (MODE != kScanPLPR && MODE != kScanUVLR) {
         if (RANDOM) {
             uint32_t idx[kScanItems];
             load_run<kScanItems>(A.perm, r0, n, idx);
@@ -277,11 +278,11 @@ template <int C, int MODE, bool RANDOM>
 static hipError_t scan_launch_t(const ScanArgs& a, hipStream_t s)
 {
     const int64_t blocks = a.tiles * a.batch;
-    LX_LAUNCH(MODE == kScanUV ? "scan_reduce_uv" : (RANDOM ? "scan_reduce_gather" : "scan_reduce"), s,
+    LX_LAUNCH(MODE == kScanUV || MODE == kScanUVLR ? "scan_reduce_uv" : (RANDOM ? "scan_reduce_gather" : "scan_reduce"), s,
               (lx_scan_reduce<C, MODE, RANDOM><<<(unsigned)blocks, kScanThreads, 0, s>>>(a)));
     const hipError_t e = scan_carry_launch(a.agg, a.gagg, a.carry, a.tiles, (int64_t)a.channels * a.batch, s);
     if (e != hipSuccess) return e;
-    LX_LAUNCH(MODE == kScanPLPR ? "scan_apply_tables" : (RANDOM ? "scan_apply_scatter" : "scan_apply"), s,
+    LX_LAUNCH(MODE == kScanPLPR || MODE == kScanUVLR ? "scan_apply_tables" : (RANDOM ? "scan_apply_scatter" : "scan_apply"), s,
               (lx_scan_apply<C, MODE, RANDOM><<<(unsigned)blocks, kScanThreads, 0, s>>>(a)));
     return hipSuccess;
 }
@@ -296,6 +297,7 @@ hipError_t scan_launch(const ScanArgs& a, hipStream_t s)
         case kScanSym: return a.random ? LX_SCAN(kScanSym, true) : LX_SCAN(kScanSym, false);
         case kScanUV: return a.random ? LX_SCAN(kScanUV, true) : LX_SCAN(kScanUV, false);
         case kScanPLPR: return a.random ? LX_SCAN(kScanPLPR, true) : LX_SCAN(kScanPLPR, false);
+        case kScanUVLR: return LX_SCAN(kScanUVLR, false);
         default: return hipErrorInvalidValue;
     }
 #undef LX_SCAN

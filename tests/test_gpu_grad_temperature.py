@@ -328,3 +328,33 @@ def test_backward_subset_of_outputs_and_errors(gpu):
                                    vp(D.data_ptr()), None, None, None, None) == lx.ERR_INVALID_ARGUMENT
         assert lib.laplex_backward(h, vp(X.data_ptr()), vp(G.data_ptr()), 1, 2, vp(D.data_ptr()), None,
                                    None, None, None, None) == lx.ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("phased", [False, True])
+def test_backward_general_small_output_side_large(gpu, phased):
+    # y = K x with a small column side (k <= 1024) and a large row side: the
+    # gradients on b come from the rows bucketed into b's intervals; checked
+    # on sampled outputs against the dense definition
+    n, k, B = (1 << 21) + 5, 1000, 2
+    say(f"[backward general large] n={n} k={k} phased={phased}")
+    rng = np.random.default_rng(77 + phased)
+    a = (rng.standard_normal(n) * 30).astype(np.float32)
+    b = rng.uniform(-60, 60, k).astype(np.float32)
+    b[:50] = a[rng.integers(0, n, 50)]  # ties between the sides
+    b[50:60] = b[60]                    # ties within b
+    phi = phases(n, rng) if phased else None
+    psi = phases(k, rng) if phased else None
+    x = rng.standard_normal((B, k)).astype(np.float32)
+    g = rng.standard_normal((B, n)).astype(np.float32)
+    with lx.laplex_plan_create(dev(a), b=dev(b), phi=None if phi is None else dev(phi),
+                               psi=None if psi is None else dev(psi)) as plan:
+        got = {key: host(v) for key, v in lx.laplex_backward(plan, dev(x), dev(g)).items()}
+    ref_dx = oracle.apply_sweep(a, g, b=b, phi=phi, psi=psi, transpose=True)
+    for v in range(B):
+        assert oracle.rel_l2(got["dx"][v], ref_dx[v]) < TOL
+    cols = np.concatenate([np.arange(0, 70), rng.integers(0, k, 30)])
+    rows = rng.integers(0, n, 200)
+    ref = oracle.grad_dense(a, g, x, b=b, phi=phi, psi=psi, rows=rows, cols=cols)
+    for key, idx in [("db", cols), ("da", rows)] + ([("dpsi", cols), ("dphi", rows)] if phased else []):
+        err = oracle.rel_l2(got[key][idx], ref[key])
+        assert err < TOL, f"{key}: rel L2 {err:.3e}"
