@@ -54,6 +54,30 @@ constexpr int kBucketVG = 8;                    // vectors per workgroup (max)
 
 __device__ __forceinline__ uint64_t match_bits11(uint32_t d) { return match_bits<11>(d); }
 
+// Interval search through a lookup table: the range [s_0, s_{n-1}] of the
+// sorted outputs is cut into kLut equal cells and tab[k] = #{s < left edge
+// of cell k} (tab[kLut] = n), so the interval of q lies in [tab[k],
+// tab[k+1]] for q's cell k, a few candidates for smooth data.  The result is
+// checked against its neighbours and a full bisection replaces it when the
+// cell arithmetic rounded q into the wrong cell: the answer is always the
+// exact #{s < q}.
+constexpr int kLut = 4096;
+
+__device__ __forceinline__ uint32_t lower_bound_lut(const float* so, int no, const uint16_t* tab, float lo_v,
+                                                    float inv_w, float q)
+{
+    const float fk = (q - lo_v) * inv_w;
+    const int k = !(fk >= 0.f) ? 0 : (fk >= (float)(kLut - 1) ? kLut - 1 : (int)fk);
+    int lo = tab[k], hi = tab[k + 1];
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (so[mid] < q) lo = mid + 1;
+        else hi = mid;
+    }
+    if ((lo > 0 && !(so[lo - 1] < q)) || (lo < no && so[lo] < q)) lo = (int)lower_bound_f(so, no, q);
+    return (uint32_t)lo;
+}
+
 template <int C, bool TIES>
 __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, int VG, int groups,
                                                                int64_t chunk_len)
@@ -67,6 +91,7 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, in
     float4* coef = reinterpret_cast<float4*>(start + pad64(nbins + 1));                // [kSub]: (au0, au1, bv0, bv1)
     float4* xs = coef + kSub;                                                          // [kSub][2]: 8 vectors
     uint8_t* tflag = reinterpret_cast<uint8_t*>(xs + 2 * kSub);                        // [kSub] (TIES): q == s_t
+    uint16_t* tab = reinterpret_cast<uint16_t*>(tflag + (TIES ? kSub : 0));            // [kLut + 1]
     __shared__ uint32_t sred[kGenWaves];
 
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
@@ -75,6 +100,13 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, in
     const int64_t v0 = (int64_t)g * VG;
     const int nv = (int)((A.batch - v0) < VG ? (A.batch - v0) : VG);
     for (int i = tid; i < no; i += kGenThreads) so[i] = A.s_out[i];
+    __syncthreads();
+    // interval lookup table (finite anchors: plans reject others)
+    const float lo_v = so[0], hi_v = so[no - 1];
+    const float width = (hi_v - lo_v) / (float)kLut;
+    const float inv_w = width > 0.f ? 1.f / width : 0.f;
+    for (int k = tid; k <= kLut; k += kGenThreads)
+        tab[k] = (uint16_t)(k == kLut ? no : lower_bound_f(so, no, lo_v + (float)k * width));
 
     float au[kBucketVG][C], av[kBucketVG][C];  // u_tid and v_tid of each vector
     float at[TIES ? kBucketVG : 1][C];         // tie_tid
@@ -93,20 +125,35 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, in
     for (int64_t sub0 = j0; sub0 < j1; sub0 += kSub) {
         for (int i = tid; i < kGenWaves * nbins; i += kGenThreads) wcnt[i] = 0;
         __syncthreads();
-        // this thread's items: element sub0 + 128 w + 64 j + lane (wave-striped)
+        // this thread's items: element sub0 + 128 w + 64 j + lane (wave-striped);
+        // the vectors' values are loaded first, in flight during the search
         int64_t idx[kSubItems];
         uint32_t tt[kSubItems], slot[kSubItems];
         bool tie[kSubItems];
         float4 cf[kSubItems];
+        float xin[kSubItems][kBucketVG];
+#pragma unroll
+        for (int j = 0; j < kSubItems; ++j) idx[j] = sub0 + w * (kSubItems * kWave) + j * kWave + lane;
+        if (nv == kBucketVG && sub0 + kSub <= j1) {
+#pragma unroll
+            for (int j = 0; j < kSubItems; ++j)
+#pragma unroll
+                for (int vi = 0; vi < kBucketVG; ++vi) xin[j][vi] = A.x[(v0 + vi) * A.n_in + idx[j]];
+        } else {
+#pragma unroll
+            for (int j = 0; j < kSubItems; ++j)
+#pragma unroll
+                for (int vi = 0; vi < kBucketVG; ++vi)
+                    xin[j][vi] = (vi < nv && idx[j] < j1) ? A.x[(v0 + vi) * A.n_in + idx[j]] : 0.f;
+        }
 #pragma unroll
         for (int j = 0; j < kSubItems; ++j) {
-            idx[j] = sub0 + w * (kSubItems * kWave) + j * kWave + lane;
             float al = 0.f, be = 0.f, f0 = 1.f, f1 = 0.f;
             uint32_t t = (uint32_t)no;  // past the end: weight 0 in the last interval
             tie[j] = false;
             if (idx[j] < j1) {
                 const float q = A.in_anchor[idx[j]];
-                t = (uint32_t)lower_bound_f(so, no, q);
+                t = lower_bound_lut(so, no, tab, lo_v, inv_w, q);
                 tie[j] = t < (uint32_t)no && so[t] == q;
                 al = t < (uint32_t)no ? decay_f(q, so[t], A.inv_t) : 0.f;
                 be = t > 0 ? decay_f(so[t - 1], q, A.inv_t) : 0.f;
@@ -161,12 +208,8 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, in
             const uint32_t sl = slot[j] + start[tt[j]] + wcnt[w * nbins + tt[j]];
             coef[sl] = cf[j];
             if (TIES) tflag[sl] = tie[j] ? 1 : 0;
-            float xv[kBucketVG];
-#pragma unroll
-            for (int vi = 0; vi < kBucketVG; ++vi)
-                xv[vi] = (vi < nv && idx[j] < j1) ? A.x[(v0 + vi) * A.n_in + idx[j]] : 0.f;
-            xs[2 * sl] = make_float4(xv[0], xv[1], xv[2], xv[3]);
-            xs[2 * sl + 1] = make_float4(xv[4], xv[5], xv[6], xv[7]);
+            xs[2 * sl] = make_float4(xin[j][0], xin[j][1], xin[j][2], xin[j][3]);
+            xs[2 * sl + 1] = make_float4(xin[j][4], xin[j][5], xin[j][6], xin[j][7]);
         }
         __syncthreads();
         if (tid < no) {
@@ -223,7 +266,7 @@ static size_t bucket_sorted_lds(int64_t no, int C, bool ties)
     (void)C;
     const int64_t nbins = no + 1;
     return (size_t)(pad64(no) + pad64(kGenWaves * nbins) / 2 + pad64(nbins + 1)) * 4 + (size_t)kSub * 16 * 3 +
-           (ties ? (size_t)kSub : 0);
+           (ties ? (size_t)kSub : 0) + (size_t)(kLut + 1) * 2;
 }
 
 // Sums the per-workgroup partials in chunk order (float64) into u, v and,
