@@ -143,17 +143,19 @@ __global__ __launch_bounds__(kRadix) void lx_sort_scan_hist(const uint32_t* __re
 }
 
 template <bool FIRST, bool LAST, bool VALS>
-__global__ __launch_bounds__(kSortThreads, 4) void lx_sort_pass(
+__global__ __launch_bounds__(kSortThreads, VALS ? 4 : 6) void lx_sort_pass(
     const float* __restrict__ a_in, const uint32_t* __restrict__ keys_in, uint32_t* __restrict__ keys_out,
     const uint2* __restrict__ kv_in, uint2* __restrict__ kv_out, float* __restrict__ sorted_out, uint16_t* __restrict__ rec, uint32_t* __restrict__ tab_base,
     uint16_t* __restrict__ tab_start, const uint32_t* __restrict__ bin_base, uint32_t* __restrict__ state,
     uint32_t* __restrict__ ticket, int shift, int64_t n, SortValPass vals)
 {
-    __shared__ uint16_t s_hist[kSortWaves][kRadix];  // per-wave counts, then wave offsets (<= tile size)
-    __shared__ uint32_t s_start[kRadix];             // tile-local start of each bin
+    __shared__ uint16_t s_hist[kSortWaves][kRadix];  // per-wave counts, then slot of each wave's first key
     __shared__ uint32_t s_off[kRadix];               // global position of slot 0 of each bin's run
-    __shared__ uint32_t s_buf[kSortTile];
-    __shared__ float s_val[VALS ? kSortTile : 1];    // one value row in slot order
+    // Slots in digit order: the keys (and, with value rows, each key with
+    // its first-row value as one 8-byte pair, so a key and its value are
+    // placed by one scattered LDS write)
+    __shared__ uint32_t s_buf[VALS ? 1 : kSortTile];
+    __shared__ uint2 s_kv[VALS ? kSortTile : 1];
     __shared__ uint32_t s_red[kSortWaves];
     __shared__ uint32_t s_tile;
 
@@ -269,7 +271,12 @@ __global__ __launch_bounds__(kSortThreads, 4) void lx_sort_pass(
     }
     uint32_t tile_total;
     const uint32_t start = block_exsum_u32<kSortWaves>(tid < kRadix ? count : 0u, s_red, tile_total);
-    if (tid < kRadix) s_start[tid] = start;
+    // the tile start of each bin folded into its wave offsets: the slot of
+    // each wave's first key of each bin, one table read per key below
+    if (tid < kRadix) {
+#pragma unroll
+        for (int i = 0; i < kSortWaves; ++i) s_hist[i][tid] = (uint16_t)(s_hist[i][tid] + start);
+    }
     __syncthreads();
 
     // Slots in the tile's digit order.  The replay record (the tile position
@@ -278,8 +285,9 @@ __global__ __launch_bounds__(kSortThreads, 4) void lx_sort_pass(
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
         const uint32_t d = (key[j] >> shift) & 0xFFu;
-        pos[j] += s_start[d] + s_hist[w][d];
-        s_buf[pos[j]] = (uint32_t)(wpos + j * kWave + lane);
+        pos[j] += s_hist[w][d];
+        if (VALS) s_kv[pos[j]].x = (uint32_t)(wpos + j * kWave + lane);
+        else s_buf[pos[j]] = (uint32_t)(wpos + j * kWave + lane);
     }
     __syncthreads();
     {
@@ -287,14 +295,14 @@ __global__ __launch_bounds__(kSortThreads, 4) void lx_sort_pass(
 #pragma unroll
         for (int q = 0; q < kSortItems / 2; ++q) {
             const uint32_t i = (uint32_t)(q * kSortThreads + tid);  // pair of slots 2i, 2i+1
-            rec2[i] = s_buf[2 * i] | (s_buf[2 * i + 1] << 16);
+            rec2[i] = VALS ? (s_kv[2 * i].x | (s_kv[2 * i + 1].x << 16)) : (s_buf[2 * i] | (s_buf[2 * i + 1] << 16));
         }
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kSortItems; ++j) {
-        s_buf[pos[j]] = key[j];
-        if (VALS) s_val[pos[j]] = v0[j];
+        if (VALS) s_kv[pos[j]] = make_uint2(key[j], __float_as_uint(v0[j]));
+        else s_buf[pos[j]] = key[j];
     }
 
     // Decoupled look-back, kLookback predecessors per round: sum their own
@@ -345,15 +353,16 @@ __global__ __launch_bounds__(kSortThreads, 4) void lx_sort_pass(
 #pragma unroll
     for (int q = 0; q < kSortItems; ++q) {
         const uint32_t i = (uint32_t)(q * kSortThreads + tid);
-        const uint32_t k = s_buf[i];
+        const uint2 kv = VALS ? s_kv[i] : make_uint2(s_buf[i], 0u);
+        const uint32_t k = kv.x;
         const uint32_t dst = s_off[(k >> shift) & 0xFFu] + i;
         if (dst < (uint32_t)n) {
             if (PAIR_OUT) {
-                kv_out[dst] = make_uint2(k, __float_as_uint(s_val[i]));
+                kv_out[dst] = kv;
             } else {
                 if (LAST) sorted_out[dst] = float_of_key(k);
                 else keys_out[dst] = k;
-                if (VALS) vout0[dst] = s_val[i];
+                if (VALS) vout0[dst] = __uint_as_float(kv.y);
             }
         }
     }
@@ -375,14 +384,15 @@ __global__ __launch_bounds__(kSortThreads, 4) void lx_sort_pass(
             }
             __syncthreads();
 #pragma unroll
-            for (int j = 0; j < kSortItems; ++j) s_val[pos[j]] = v[j];
+            for (int j = 0; j < kSortItems; ++j) s_kv[pos[j]].y = __float_as_uint(v[j]);
             __syncthreads();
             float* vout = vals.out[r];
 #pragma unroll
             for (int q = 0; q < kSortItems; ++q) {
                 const uint32_t i = (uint32_t)(q * kSortThreads + tid);
-                const uint32_t dst = s_off[(s_buf[i] >> shift) & 0xFFu] + i;
-                if (dst < (uint32_t)n) vout[dst] = s_val[i];
+                const uint2 kv = s_kv[i];
+                const uint32_t dst = s_off[(kv.x >> shift) & 0xFFu] + i;
+                if (dst < (uint32_t)n) vout[dst] = __uint_as_float(kv.y);
             }
         }
     }
