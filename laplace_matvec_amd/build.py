@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("LAPLEX_ARCH", "gfx950")
 
-LIB_SOURCES = ["api.hip", "sort.hip", "scan.hip", "general.hip", "gram.hip", "grad.hip"]
+LIB_SOURCES = ["api.hip", "sort.hip", "small.hip", "scan.hip", "general.hip", "gram.hip", "grad.hip"]
 INPUT_SOURCES = ["inputs_philox.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

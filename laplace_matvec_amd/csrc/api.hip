@@ -481,6 +481,59 @@ laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, cons
     LX_PLAN_TRY(plan_alloc(p, (void**)&flag, 256, s), "alloc flag");
     LX_PLAN_TRY(lx::fill_u32(flag, 0u, 1, s), "clear flag");
     LX_PLAN_TRY(plan_alloc(p, (void**)&p->sa, (size_t)n * 4, s), "alloc sorted a");
+    if (sym && n <= lx::kSmallMax && n < replay_min()) {
+        // A small symmetric plan in one workgroup: the sorted anchors, the
+        // permutation (the sort records are never needed below the replay
+        // size) and the phase factors by rank; y = K x too for a few vectors.
+        LX_PLAN_TRY(plan_alloc(p, (void**)&p->pa, (size_t)n * 4, s), "alloc permutation");
+        p->sb = p->sa;
+        p->pb = p->pa;
+        if (p->phased) {
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->cphi, (size_t)n * 4, s), "alloc phases");
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->sphi, (size_t)n * 4, s), "alloc phases");
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->cpsi, (size_t)n * 4, s), "alloc phases");
+            LX_PLAN_TRY(plan_alloc(p, (void**)&p->spsi, (size_t)n * 4, s), "alloc phases");
+        }
+        const bool with_y = x != nullptr && batch <= 8;
+        lx::SmallSymArgs S;
+        S.n = n;
+        S.batch = with_y ? (int)batch : 0;
+        S.inv_t = p->inv_t;
+        S.a = a;
+        S.phi = phi;
+        S.psi = psi;
+        S.x = with_y ? x : nullptr;
+        S.y = with_y ? y : nullptr;
+        S.sa = p->sa;
+        S.perm = p->pa;
+        S.cphi = p->cphi;
+        S.sphi = p->sphi;
+        S.cpsi = p->cpsi;
+        S.spsi = p->spsi;
+        S.flag = flag;
+        LX_PLAN_TRY(lx::small_sym_launch(S, s), "small plan");
+        LX_PLAN_TRY(hipMemcpyAsync(&host_flag, flag, 4, hipMemcpyDeviceToHost, s), "read flag");
+        LX_PLAN_TRY(hipStreamSynchronize(s), "synchronize");
+        if (host_flag & 1u) return bail(fail(LAPLEX_ERR_NONFINITE_ANCHOR, "NaN or Inf among anchors or phases"));
+        if (x) {
+            // x in its original order is kept for a later backward
+            laplex_status st2 = with_y ? LAPLEX_OK : laplex_apply(p, x, y, batch, 0, stream);
+            float* keep = nullptr;
+            if (st2 == LAPLEX_OK)
+                st2 = from_hip(plan_alloc(p, (void**)&keep, (size_t)(batch * n) * 4, s), "alloc kept x");
+            if (st2 == LAPLEX_OK)
+                st2 = from_hip(hipMemcpyAsync(keep, x, (size_t)(batch * n) * 4, hipMemcpyDeviceToDevice, s), "copy x");
+            p->kept_x = keep;
+            p->kept_by_rank = false;
+            p->kept_batch = batch;
+            if (st2 != LAPLEX_OK) {
+                plan_release(p);
+                return st2;
+            }
+        }
+        *out = p;
+        return LAPLEX_OK;
+    }
     {
         void* rec = nullptr;
         LX_PLAN_TRY(plan_alloc(p, &rec, lx::sort_record_bytes(n), s), "alloc sort records");

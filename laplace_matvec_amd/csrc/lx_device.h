@@ -177,6 +177,47 @@ __device__ __forceinline__ Aff<T> block_exscan_down(Aff<T> x, Aff<T>* sh, Aff<T>
     return compose(pre, ex);
 }
 
+// The same exclusive scans without the block total, for kernels with many
+// waves per workgroup: the wave totals are combined by a scan across lanes,
+// not by a loop over all of them in every thread (which would keep NW
+// composites live in registers).
+template <class T, int NW>
+__device__ __forceinline__ Aff<T> block_exscan_up_lean(Aff<T> x, Aff<T>* sh)
+{
+    static_assert(NW <= kWave, "waves per block");
+    const int lane = lane_id();
+    const int w = (int)threadIdx.x / kWave;
+    const Aff<T> inc = wave_scan_up(x);
+    Aff<T> ex{__shfl_up(inc.m, 1), __shfl_up(inc.v, 1)};
+    if (lane == 0) ex = aff_identity<T>();
+    if (lane == kWave - 1) sh[w] = inc;
+    __syncthreads();
+    Aff<T> t = lane < NW ? sh[lane] : aff_identity<T>();
+    t = wave_scan_up(t);
+    Aff<T> pre{__shfl(t.m, w > 0 ? w - 1 : 0), __shfl(t.v, w > 0 ? w - 1 : 0)};
+    if (w == 0) pre = aff_identity<T>();
+    __syncthreads();
+    return compose(pre, ex);
+}
+template <class T, int NW>
+__device__ __forceinline__ Aff<T> block_exscan_down_lean(Aff<T> x, Aff<T>* sh)
+{
+    static_assert(NW <= kWave, "waves per block");
+    const int lane = lane_id();
+    const int w = (int)threadIdx.x / kWave;
+    const Aff<T> inc = wave_scan_down(x);
+    Aff<T> ex{__shfl_down(inc.m, 1), __shfl_down(inc.v, 1)};
+    if (lane == kWave - 1) ex = aff_identity<T>();
+    if (lane == 0) sh[w] = inc;
+    __syncthreads();
+    Aff<T> t = lane < NW ? sh[lane] : aff_identity<T>();
+    t = wave_scan_down(t);
+    Aff<T> pre{__shfl(t.m, w + 1 < NW ? w + 1 : 0), __shfl(t.v, w + 1 < NW ? w + 1 : 0)};
+    if (w + 1 >= NW) pre = aff_identity<T>();
+    __syncthreads();
+    return compose(pre, ex);
+}
+
 // Block-wide exclusive sum of uint32 over NW waves.
 template <int NW>
 __device__ __forceinline__ uint32_t block_exsum_u32(uint32_t x, uint32_t* sh, uint32_t& total)

@@ -247,6 +247,29 @@ struct EvalLRArgs {
 };
 hipError_t eval_lr_launch(const EvalLRArgs& a, hipStream_t s);
 
+// ---- small symmetric plans (small.hip) ----
+// n <= kSmallMax anchors in one workgroup: stable sort, permutation, phase
+// factors by rank and, when x is given, y = K x for `batch` vectors.
+constexpr int64_t kSmallMax = 8192;
+struct SmallSymArgs {
+    int64_t n = 0;
+    int batch = 0;
+    double inv_t = 1.0;
+    const float* a = nullptr;              // anchors, original order
+    const float* phi = nullptr;            // phases (both or neither), original order
+    const float* psi = nullptr;
+    const float* x = nullptr;              // [batch][n], or null: plan only
+    float* y = nullptr;                    // [batch][n]
+    float* sa = nullptr;                   // sorted anchors [n]
+    uint32_t* perm = nullptr;              // rank -> original index [n]
+    float* cphi = nullptr;                 // cos/sin of the phases by rank (phased)
+    float* sphi = nullptr;
+    float* cpsi = nullptr;
+    float* spsi = nullptr;
+    uint32_t* flag = nullptr;              // bit 0 set for a NaN/Inf anchor or phase
+};
+hipError_t small_sym_launch(const SmallSymArgs& a, hipStream_t s);
+
 // ---- Gram (gram.hip) ----
 struct GramArgs {
     int64_t n = 0, k = 0;
