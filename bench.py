@@ -110,6 +110,35 @@ def counter_traffic(kernel: str, workload: str):
     return None
 
 
+def counter_step_bytes(workload: str):
+    """HBM bytes of one whole step from the committed rocprofv3 counter
+    record (every kernel of the step, calibrated FETCH_SIZE + WRITE_SIZE),
+    if the hashes of all the kernel sources it names still match."""
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*counters*.txt")):
+        kv = {}
+        for line in open(path):
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("kernel") != "step" or kv.get("workload") != workload:
+            continue
+        srcs = kv.get("source", "").split(",")
+        shas = kv.get("source_sha", "").split(",")
+        if len(srcs) != len(shas):
+            return None
+        for src, want in zip(srcs, shas):
+            path_src = os.path.join(ROOT, "laplace_matvec_amd", "csrc", src)
+            if not os.path.exists(path_src):
+                return None
+            if hashlib.sha256(open(path_src, "rb").read()).hexdigest()[:16] != want:
+                return None
+        try:
+            return float(kv["hbm_bytes_per_step"])
+        except (KeyError, ValueError):
+            return None
+    return None
+
+
 def cpu_baseline(sample: int):
     """The fp64 oracle (sort + two sweeps, single thread) on a bounded sample
     of the same workload; elements/s."""
@@ -258,6 +287,15 @@ def main():
         extra["model_bytes_per_step"] = model
         extra["model_gbps_end_to_end"] = round(model / (ms / 1e3) / 1e9, 1)
         extra["model_frac_end_to_end"] = round(model / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
+        # bytes any implementation must move: read a and x, write y
+        comp = (4.0 + 8.0 * batch) * n
+        extra["compulsory_bytes_per_step"] = comp
+        extra["compulsory_gbps_end_to_end"] = round(comp / (ms / 1e3) / 1e9, 1)
+        # what the HBM counters saw for a whole step (committed record), over this run's step time
+        cb = counter_step_bytes(W.name)
+        extra["counter_bytes_per_step"] = cb
+        extra["counter_gbps_end_to_end"] = None if cb is None else round(cb / (ms / 1e3) / 1e9, 1)
+        extra["counter_frac_end_to_end"] = None if cb is None else round(cb / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
     out = {
         "metric": (METRIC if cfg == 5 else f"LAPLEX {W.kind} elements/s ({W.name})") if not args.backward
         else f"LAPLEX training step (forward + backward) elements/s ({W.name})",
