@@ -71,10 +71,10 @@ def model_bytes(kernel: str, n: int, batch: int = 1, channels: int = 1, vals: in
         "scan_apply": 4.0 + 2 * factors + 8.0 * batch,
         "scan_reduce_gather": 8.0 + factors + 8.0 * batch,
         "scan_apply_scatter": 8.0 + 2 * factors + 8.0 * batch,
-        # gradient by rank: s, u and w read; per half launch also the anchor
-        # row (written, or read and written) and, in one of the two, dx
+        # gradient by rank: s, u and w read; the apply also writes the anchor
+        # row, dx and (phased) the two phase rows
         "grad_reduce": 4.0 + 2 * factors + 8.0 * batch,
-        "grad_apply": 4.0 + 2 * factors + 8.0 * batch + 6.0 + 2.0 * batch,
+        "grad_apply": 4.0 + 2 * factors + 8.0 * batch + 4.0 + 4.0 * batch + factors,
     }.get(kernel)
     return None if per is None else per * n
 

@@ -110,12 +110,8 @@ __device__ __forceinline__ void block_exscan4(Aff<double> f0, Aff<double> f1, Af
     Aff<double>* buf = sh + parity * (kGradWaves * 4);
     const Aff<double> if0 = wave_scan_up(f0), if1 = wave_scan_up(f1);
     const Aff<double> ib0 = wave_scan_down(b0), ib1 = wave_scan_down(b1);
-    Aff<double> ef0{__shfl_up(if0.m, 1), __shfl_up(if0.v, 1)};
-    Aff<double> ef1{__shfl_up(if1.m, 1), __shfl_up(if1.v, 1)};
-    Aff<double> eb0{__shfl_down(ib0.m, 1), __shfl_down(ib0.v, 1)};
-    Aff<double> eb1{__shfl_down(ib1.m, 1), __shfl_down(ib1.v, 1)};
-    if (lane == 0) ef0 = ef1 = aff_identity<double>();
-    if (lane == kWave - 1) eb0 = eb1 = aff_identity<double>();
+    const Aff<double> ef0 = wave_shift_up(if0), ef1 = wave_shift_up(if1);
+    const Aff<double> eb0 = wave_shift_down(ib0), eb1 = wave_shift_down(ib1);
     if (lane == kWave - 1) {
         buf[w * 4 + 0] = if0;
         buf[w * 4 + 1] = if1;
@@ -213,14 +209,8 @@ __global__ __launch_bounds__(kGradThreads) void lx_grad_sym_reduce(GradSymArgs A
     }
 }
 
-// One half of the symmetric gradient for one vector: for each channel the
-// decay scan (L forward, U backward) and the tie scan (Tp, Ts) over this
-// thread's ranks, entered from the carries, combined on the way back into
-//   K0 = L + U - x  and  S0 = (L - Tp) - (U - Ts),
-// and folded into the batch sums (anchor, phase) and the plain product.
-// One per-anchor result: through perm into original order, or by rank;
-// ADD accumulates into what is there (the second half of the anchor sum).
-template <bool RANDOM, bool ADD>
+// One per-anchor result: through perm into original order, or by rank.
+template <bool RANDOM>
 __device__ __forceinline__ void grad_store_out(const GradSymArgs& A, float* dst, int64_t r0,
                                                const float (&val)[kGradItems])
 {
@@ -231,31 +221,24 @@ __device__ __forceinline__ void grad_store_out(const GradSymArgs& A, float* dst,
         load_run<kGradItems>(A.perm, r0, n, idx);
 #pragma unroll
         for (int i = 0; i < kGradItems; ++i)
-            if (r0 + i < n) dst[idx[i]] = ADD ? dst[idx[i]] + val[i] : val[i];
+            if (r0 + i < n) dst[idx[i]] = val[i];
     } else {
-        float v[kGradItems];
-        if (ADD) {
-            load_run<kGradItems>(dst, r0, n, v);
-#pragma unroll
-            for (int i = 0; i < kGradItems; ++i) v[i] += val[i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < kGradItems; ++i) v[i] = val[i];
-        }
-        store_run<kGradItems>(dst, r0, n, v);
+        store_run<kGradItems>(dst, r0, n, val);
     }
 }
 
-// Half H of the symmetric gradient over one tile (one launch per half; the
-// second adds its anchor part to the first's).  For every vector and channel:
-// the decay scan (L forward, U backward) and the tie scan (Tp, Ts) over this
-// thread's ranks, entered from the carries, combined on the way back into
+// Both halves of the symmetric gradient over one tile.  For every half,
+// vector and channel: the decay scan (L forward, U backward) and the tie
+// scan (Tp, Ts) over this thread's ranks, entered from the carries,
+// combined on the way back into
 //   K0 = L + U - x  and  S0 = (L - Tp) - (U - Ts),
 // and folded into the batch sums (anchor, phase) and the plain product.
-// Vectors and channels run in a loop that is not unrolled, and the decays
-// and tie masks are re-read from LDS in it, which keeps one step's state
-// live at a time.
-template <int C, bool RANDOM, int H>
+// The anchor sum of both halves stays in registers, the decays are computed
+// once per tile, and the second half re-reads the tile's inputs from cache.
+// Halves, vectors and channels run in loops that are not unrolled, and the
+// decays and tie masks are re-read from LDS in them, which keeps one step's
+// state live at a time.
+template <int C, bool RANDOM>
 __global__ __launch_bounds__(kGradThreads, 4) void lx_grad_sym_apply(GradSymArgs A)
 {
     __shared__ Aff<double> sh[2 * kGradWaves * 4];
@@ -275,103 +258,109 @@ __global__ __launch_bounds__(kGradThreads, 4) void lx_grad_sym_apply(GradSymArgs
         st[threadIdx.x] = ties;
     }
     __syncthreads();
-    // half 0: input w with the column phases, weight u, output phases phi;
-    // half 1: input u with the row phases, weight w, output phases psi
-    const float* in_v = H == 0 ? A.ws : A.us;
-    const float* wt_v = H == 0 ? A.us : A.ws;
-    const float* icos = H == 0 ? A.cpsi : A.cphi;
-    const float* isin = H == 0 ? A.spsi : A.sphi;
-    const float* ocos = H == 0 ? A.cphi : A.cpsi;
-    const float* osin = H == 0 ? A.sphi : A.spsi;
-    const bool want_dx = A.dx != nullptr && A.dx_half == H;
-    float g_a[kGradItems], g_p[kGradItems];
+    float g_a[kGradItems];
 #pragma unroll
-    for (int i = 0; i < kGradItems; ++i) g_a[i] = g_p[i] = 0.f;
+    for (int i = 0; i < kGradItems; ++i) g_a[i] = 0.f;
 
 #pragma unroll 1
-    for (int64_t vec = 0; vec < A.batch; ++vec) {
-        float dxo[kGradItems];
+    for (int h = 0; h < 2; ++h) {
+        // half 0: input w with the column phases, weight u, output phases phi;
+        // half 1: input u with the row phases, weight w, output phases psi
+        const float* in_v = h == 0 ? A.ws : A.us;
+        const float* wt_v = h == 0 ? A.us : A.ws;
+        const float* icos = h == 0 ? A.cpsi : A.cphi;
+        const float* isin = h == 0 ? A.spsi : A.sphi;
+        const float* ocos = h == 0 ? A.cphi : A.cpsi;
+        const float* osin = h == 0 ? A.sphi : A.spsi;
+        const bool want_dx = A.dx != nullptr && A.dx_half == h;
+        float g_p[kGradItems];
 #pragma unroll
-        for (int i = 0; i < kGradItems; ++i) dxo[i] = 0.f;
+        for (int i = 0; i < kGradItems; ++i) g_p[i] = 0.f;
 #pragma unroll 1
-        for (int c = 0; c < C; ++c) {
-            double e[kGradItems + 1];
+        for (int64_t vec = 0; vec < A.batch; ++vec) {
+            float dxo[kGradItems];
 #pragma unroll
-            for (int i = 0; i <= kGradItems; ++i) e[i] = se[threadIdx.x * kGradItems + i];
-            const uint32_t ties = st[threadIdx.x];
-            float val[kGradItems], wt[kGradItems], fo[kGradItems], fk[kGradItems];
-            load_run<kGradItems>(in_v + vec * A.ld, r0, n, val);
-            load_run<kGradItems>(wt_v + vec * A.ld, r0, n, wt);
-            if (C == 2) {
-                float fi[kGradItems];
-                load_run<kGradItems>(c == 0 ? icos : isin, r0, n, fi);
-                load_run<kGradItems>(c == 0 ? ocos : osin, r0, n, fo);
-                load_run<kGradItems>(c == 0 ? osin : ocos, r0, n, fk);
-                const float sg = c == 0 ? 1.f : -1.f;  // sine product: s_out K0_c - c_out K0_s
+            for (int i = 0; i < kGradItems; ++i) dxo[i] = 0.f;
+#pragma unroll 1
+            for (int c = 0; c < C; ++c) {
+                double e[kGradItems + 1];
+#pragma unroll
+                for (int i = 0; i <= kGradItems; ++i) e[i] = se[threadIdx.x * kGradItems + i];
+                const uint32_t ties = st[threadIdx.x];
+                float val[kGradItems], wt[kGradItems], fo[kGradItems], fk[kGradItems];
+                load_run<kGradItems>(in_v + vec * A.ld, r0, n, val);
+                load_run<kGradItems>(wt_v + vec * A.ld, r0, n, wt);
+                if (C == 2) {
+                    float fi[kGradItems];
+                    load_run<kGradItems>(c == 0 ? icos : isin, r0, n, fi);
+                    load_run<kGradItems>(c == 0 ? ocos : osin, r0, n, fo);
+                    load_run<kGradItems>(c == 0 ? osin : ocos, r0, n, fk);
+                    const float sg = c == 0 ? 1.f : -1.f;  // sine product: s_out K0_c - c_out K0_s
+#pragma unroll
+                    for (int i = 0; i < kGradItems; ++i) {
+                        val[i] *= fi[i];
+                        fk[i] *= sg;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < kGradItems; ++i) fo[i] = fk[i] = 1.f;
+                }
+                Aff<double> fd = aff_identity<double>(), bd = aff_identity<double>();
+                Aff<double> ft = aff_identity<double>(), bt = aff_identity<double>();
 #pragma unroll
                 for (int i = 0; i < kGradItems; ++i) {
-                    val[i] *= fi[i];
-                    fk[i] *= sg;
+                    fd = compose(fd, Aff<double>{e[i], (double)val[i]});
+                    ft = compose(ft, Aff<double>{tie_mult(ties, i), (double)val[i]});
                 }
-            } else {
 #pragma unroll
-                for (int i = 0; i < kGradItems; ++i) fo[i] = fk[i] = 1.f;
+                for (int i = kGradItems - 1; i >= 0; --i) {
+                    bd = compose(bd, Aff<double>{e[i + 1], (double)val[i]});
+                    bt = compose(bt, Aff<double>{tie_mult(ties, i + 1), (double)val[i]});
+                }
+                Aff<double> fxd, fxt, bxd, bxt;
+                block_exscan4(fd, ft, bd, bt, sh, parity, fxd, fxt, bxd, bxt);
+                parity ^= 1;
+                const double* cd = A.carry + (grad_row(C, h, c, 0, A.batch, vec) * A.tiles + tile) * 2;
+                const double* ct = A.carry + (grad_row(C, h, c, 1, A.batch, vec) * A.tiles + tile) * 2;
+                double L = fxd.m * cd[0] + fxd.v;
+                double T = fxt.m * ct[0] + fxt.v;
+                double Lr[kGradItems], Sr[kGradItems];  // L and L - Tp by rank
+#pragma unroll
+                for (int i = 0; i < kGradItems; ++i) {
+                    L = e[i] * L + (double)val[i];
+                    T = tie_mult(ties, i) * T + (double)val[i];
+                    Lr[i] = L;
+                    Sr[i] = L - T;
+                }
+                double U = bxd.m * cd[1] + bxd.v;
+                double Tb = bxt.m * ct[1] + bxt.v;
+#pragma unroll
+                for (int i = kGradItems - 1; i >= 0; --i) {
+                    U = e[i + 1] * U + (double)val[i];
+                    Tb = tie_mult(ties, i + 1) * Tb + (double)val[i];
+                    const float k0 = (float)(Lr[i] + U - (double)val[i]);
+                    const float s0 = (float)(Sr[i] - (U - Tb));
+                    g_a[i] = fmaf(A.anchor_scale * wt[i] * fo[i], s0, g_a[i]);
+                    if (C == 2) g_p[i] = fmaf(-wt[i] * fk[i], k0, g_p[i]);
+                    dxo[i] = fmaf(fo[i], k0, dxo[i]);
+                }
             }
-            Aff<double> fd = aff_identity<double>(), bd = aff_identity<double>();
-            Aff<double> ft = aff_identity<double>(), bt = aff_identity<double>();
+            if (want_dx) {
+                if (RANDOM) {
+                    uint32_t idx[kGradItems];
+                    load_run<kGradItems>(A.perm, r0, n, idx);
+                    float* dv = A.dx + vec * n;
 #pragma unroll
-            for (int i = 0; i < kGradItems; ++i) {
-                fd = compose(fd, Aff<double>{e[i], (double)val[i]});
-                ft = compose(ft, Aff<double>{tie_mult(ties, i), (double)val[i]});
-            }
-#pragma unroll
-            for (int i = kGradItems - 1; i >= 0; --i) {
-                bd = compose(bd, Aff<double>{e[i + 1], (double)val[i]});
-                bt = compose(bt, Aff<double>{tie_mult(ties, i + 1), (double)val[i]});
-            }
-            Aff<double> fxd, fxt, bxd, bxt;
-            block_exscan4(fd, ft, bd, bt, sh, parity, fxd, fxt, bxd, bxt);
-            parity ^= 1;
-            const double* cd = A.carry + (grad_row(C, H, c, 0, A.batch, vec) * A.tiles + tile) * 2;
-            const double* ct = A.carry + (grad_row(C, H, c, 1, A.batch, vec) * A.tiles + tile) * 2;
-            double L = fxd.m * cd[0] + fxd.v;
-            double T = fxt.m * ct[0] + fxt.v;
-            double Lr[kGradItems], Sr[kGradItems];  // L and L - Tp by rank
-#pragma unroll
-            for (int i = 0; i < kGradItems; ++i) {
-                L = e[i] * L + (double)val[i];
-                T = tie_mult(ties, i) * T + (double)val[i];
-                Lr[i] = L;
-                Sr[i] = L - T;
-            }
-            double U = bxd.m * cd[1] + bxd.v;
-            double Tb = bxt.m * ct[1] + bxt.v;
-#pragma unroll
-            for (int i = kGradItems - 1; i >= 0; --i) {
-                U = e[i + 1] * U + (double)val[i];
-                Tb = tie_mult(ties, i + 1) * Tb + (double)val[i];
-                const float k0 = (float)(Lr[i] + U - (double)val[i]);
-                const float s0 = (float)(Sr[i] - (U - Tb));
-                g_a[i] = fmaf(A.anchor_scale * wt[i] * fo[i], s0, g_a[i]);
-                if (C == 2) g_p[i] = fmaf(-wt[i] * fk[i], k0, g_p[i]);
-                dxo[i] = fmaf(fo[i], k0, dxo[i]);
-            }
-        }
-        if (want_dx) {
-            if (RANDOM) {
-                uint32_t idx[kGradItems];
-                load_run<kGradItems>(A.perm, r0, n, idx);
-                float* dv = A.dx + vec * n;
-#pragma unroll
-                for (int i = 0; i < kGradItems; ++i)
-                    if (r0 + i < n) dv[idx[i]] = dxo[i];
-            } else {
-                store_run<kGradItems>(A.dx + vec * A.out_ld, r0, n, dxo);
+                    for (int i = 0; i < kGradItems; ++i)
+                        if (r0 + i < n) dv[idx[i]] = dxo[i];
+                } else {
+                    store_run<kGradItems>(A.dx + vec * A.out_ld, r0, n, dxo);
+                }
             }
         }
+        if (C == 2) grad_store_out<RANDOM>(A, h == 0 ? A.dphi : A.dpsi, r0, g_p);
     }
-    grad_store_out<RANDOM, H == 1>(A, A.da, r0, g_a);
-    if (C == 2) grad_store_out<RANDOM, false>(A, H == 0 ? A.dphi : A.dpsi, r0, g_p);
+    grad_store_out<RANDOM>(A, A.da, r0, g_a);
 }
 
 size_t grad_sym_scratch_doubles(int64_t n, int64_t batch, int channels)
@@ -388,8 +377,7 @@ static hipError_t grad_sym_launch_t(const GradSymArgs& a, hipStream_t s)
     LX_LAUNCH("grad_reduce", s, (lx_grad_sym_reduce<C, RANDOM><<<(unsigned)(a.tiles * a.batch), kGradThreads, 0, s>>>(a)));
     const hipError_t e = scan_carry_launch(a.agg, a.gagg, a.carry, a.tiles, 4 * (int64_t)C * a.batch, s);
     if (e != hipSuccess) return e;
-    LX_LAUNCH("grad_apply", s, (lx_grad_sym_apply<C, RANDOM, 0><<<(unsigned)a.tiles, kGradThreads, 0, s>>>(a)));
-    LX_LAUNCH("grad_apply", s, (lx_grad_sym_apply<C, RANDOM, 1><<<(unsigned)a.tiles, kGradThreads, 0, s>>>(a)));
+    LX_LAUNCH("grad_apply", s, (lx_grad_sym_apply<C, RANDOM><<<(unsigned)a.tiles, kGradThreads, 0, s>>>(a)));
     return hipSuccess;
 }
 

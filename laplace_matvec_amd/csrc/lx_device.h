@@ -101,32 +101,129 @@ __device__ __forceinline__ Aff<T> compose(Aff<T> p, Aff<T> q)
     return Aff<T>{p.m * q.m, q.m * p.v + q.v};
 }
 
-// Inclusive scan over the lanes of a wave in ascending lane order.
+// A 64-bit value moved between lanes by DPP (vector ALU moves, without the
+// LDS round trip of a shuffle).  CTRL 0x110+d (row_shr:d) reads lane - d and
+// 0x100+d (row_shl:d) lane + d inside each row of 16 lanes; 0x142
+// (row_bcast:15) gives the rows in ROW_MASK lane 15 of the row below them,
+// 0x143 (row_bcast:31) lane 31; 0x138 (wave_shr:1) reads lane - 1 and 0x130
+// (wave_shl:1) lane + 1 across the whole wave.  Lanes without a source, or
+// outside ROW_MASK, get 0; callers ignore them.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_move(double x)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t hi =
+        (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ Aff<double> dpp_move(Aff<double> x)
+{
+    return Aff<double>{dpp_move<CTRL, ROW_MASK>(x.m), dpp_move<CTRL, ROW_MASK>(x.v)};
+}
+
+// The value of lane L (a constant), in scalar registers.
+__device__ __forceinline__ double read_lane(double x, int l)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ Aff<double> read_lane(Aff<double> x, int l)
+{
+    return Aff<double>{read_lane(x.m, l), read_lane(x.v, l)};
+}
+
+// Inclusive scan over the lanes of a wave in ascending lane order.  All
+// lanes of the wave must be active.  Float64 composites: distances 1, 2, 4,
+// 8 inside each row of 16 lanes by DPP, then each row takes the composite
+// of all rows below it (row broadcasts of lanes 15 and 31).  Other types:
+// shuffles at distances 1 .. 32.
 template <class T>
 __device__ __forceinline__ Aff<T> wave_scan_up(Aff<T> x)
 {
     const int lane = lane_id();
+    if constexpr (sizeof(T) == 8) {
+        Aff<double> y;
+        y = dpp_move<0x111>(x);
+        if ((lane & 15) >= 1) x = compose(y, x);
+        y = dpp_move<0x112>(x);
+        if ((lane & 15) >= 2) x = compose(y, x);
+        y = dpp_move<0x114>(x);
+        if ((lane & 15) >= 4) x = compose(y, x);
+        y = dpp_move<0x118>(x);
+        if ((lane & 15) >= 8) x = compose(y, x);
+        y = dpp_move<0x142, 0xA>(x);  // rows 1, 3 <- lane 15 of rows 0, 2
+        if (lane & 16) x = compose(y, x);
+        y = dpp_move<0x143, 0xC>(x);  // rows 2, 3 <- lane 31 (rows 0 and 1)
+        if (lane & 32) x = compose(y, x);
+    } else {
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const T m = __shfl_up(x.m, d);
-        const T v = __shfl_up(x.v, d);
-        if (lane >= d) x = compose(Aff<T>{m, v}, x);
+        for (int d = 1; d < kWave; d <<= 1) {
+            const T m = __shfl_up(x.m, d);
+            const T v = __shfl_up(x.v, d);
+            if (lane >= d) x = compose(Aff<T>{m, v}, x);
+        }
     }
     return x;
 }
 
 // Inclusive scan over the lanes in descending lane order (lane 63 first).
+// All lanes of the wave must be active.  Float64 composites: distances 1,
+// 2, 4, 8 inside each row by DPP, then each row takes the composite of the
+// rows above it, from the row totals at lanes 16, 32 and 48.
 template <class T>
 __device__ __forceinline__ Aff<T> wave_scan_down(Aff<T> x)
 {
     const int lane = lane_id();
+    if constexpr (sizeof(T) == 8) {
+        Aff<double> y;
+        y = dpp_move<0x101>(x);
+        if ((lane & 15) + 1 < 16) x = compose(y, x);
+        y = dpp_move<0x102>(x);
+        if ((lane & 15) + 2 < 16) x = compose(y, x);
+        y = dpp_move<0x104>(x);
+        if ((lane & 15) + 4 < 16) x = compose(y, x);
+        y = dpp_move<0x108>(x);
+        if ((lane & 15) + 8 < 16) x = compose(y, x);
+        const Aff<double> r1 = read_lane(x, 16), r2 = read_lane(x, 32), r3 = read_lane(x, 48);
+        const Aff<double> r32 = compose(r3, r2);
+        const int row = lane >> 4;
+        const Aff<double> above = row == 2 ? r3 : (row == 1 ? r32 : compose(r32, r1));
+        if (row < 3) x = compose(above, x);
+    } else {
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const T m = __shfl_down(x.m, d);
-        const T v = __shfl_down(x.v, d);
-        if (lane + d < kWave) x = compose(Aff<T>{m, v}, x);
+        for (int d = 1; d < kWave; d <<= 1) {
+            const T m = __shfl_down(x.m, d);
+            const T v = __shfl_down(x.v, d);
+            if (lane + d < kWave) x = compose(Aff<T>{m, v}, x);
+        }
     }
     return x;
+}
+
+// Exclusive versions of a wave scan's result: the inclusive value of the
+// lane below (up) or above (down), identity at the wave's first lane.
+template <class T>
+__device__ __forceinline__ Aff<T> wave_shift_up(Aff<T> inc)
+{
+    Aff<T> ex;
+    if constexpr (sizeof(T) == 8) ex = dpp_move<0x138>(inc);
+    else ex = Aff<T>{__shfl_up(inc.m, 1), __shfl_up(inc.v, 1)};
+    if (lane_id() == 0) ex = aff_identity<T>();
+    return ex;
+}
+template <class T>
+__device__ __forceinline__ Aff<T> wave_shift_down(Aff<T> inc)
+{
+    Aff<T> ex;
+    if constexpr (sizeof(T) == 8) ex = dpp_move<0x130>(inc);
+    else ex = Aff<T>{__shfl_down(inc.m, 1), __shfl_down(inc.v, 1)};
+    if (lane_id() == kWave - 1) ex = aff_identity<T>();
+    return ex;
 }
 
 // Block-wide exclusive scans of one Aff per thread, ascending (up) or
@@ -139,8 +236,7 @@ __device__ __forceinline__ Aff<T> block_exscan_up(Aff<T> x, Aff<T>* sh, Aff<T>& 
     const int lane = lane_id();
     const int w = (int)threadIdx.x / kWave;
     const Aff<T> inc = wave_scan_up(x);
-    Aff<T> ex{__shfl_up(inc.m, 1), __shfl_up(inc.v, 1)};
-    if (lane == 0) ex = aff_identity<T>();
+    const Aff<T> ex = wave_shift_up(inc);
     if (lane == kWave - 1) sh[w] = inc;
     __syncthreads();
     Aff<T> pre = aff_identity<T>();
@@ -161,8 +257,7 @@ __device__ __forceinline__ Aff<T> block_exscan_down(Aff<T> x, Aff<T>* sh, Aff<T>
     const int lane = lane_id();
     const int w = (int)threadIdx.x / kWave;
     const Aff<T> inc = wave_scan_down(x);
-    Aff<T> ex{__shfl_down(inc.m, 1), __shfl_down(inc.v, 1)};
-    if (lane == kWave - 1) ex = aff_identity<T>();
+    const Aff<T> ex = wave_shift_down(inc);
     if (lane == 0) sh[w] = inc;
     __syncthreads();
     Aff<T> pre = aff_identity<T>();
@@ -188,8 +283,7 @@ __device__ __forceinline__ Aff<T> block_exscan_up_lean(Aff<T> x, Aff<T>* sh)
     const int lane = lane_id();
     const int w = (int)threadIdx.x / kWave;
     const Aff<T> inc = wave_scan_up(x);
-    Aff<T> ex{__shfl_up(inc.m, 1), __shfl_up(inc.v, 1)};
-    if (lane == 0) ex = aff_identity<T>();
+    const Aff<T> ex = wave_shift_up(inc);
     if (lane == kWave - 1) sh[w] = inc;
     __syncthreads();
     Aff<T> t = lane < NW ? sh[lane] : aff_identity<T>();
@@ -206,8 +300,7 @@ __device__ __forceinline__ Aff<T> block_exscan_down_lean(Aff<T> x, Aff<T>* sh)
     const int lane = lane_id();
     const int w = (int)threadIdx.x / kWave;
     const Aff<T> inc = wave_scan_down(x);
-    Aff<T> ex{__shfl_down(inc.m, 1), __shfl_down(inc.v, 1)};
-    if (lane == kWave - 1) ex = aff_identity<T>();
+    const Aff<T> ex = wave_shift_down(inc);
     if (lane == 0) sh[w] = inc;
     __syncthreads();
     Aff<T> t = lane < NW ? sh[lane] : aff_identity<T>();
