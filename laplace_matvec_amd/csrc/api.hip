@@ -901,7 +901,9 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
     Bk.ld = pad64(no);
     Bk.lds_bytes = p->lds_bytes;
     Bk.partial_floats = lx::bucket_partial_floats(Bk, nullptr, nullptr);
-    const size_t need = scan_ws_bytes(no, batch, ch, 0, 2) + align256((size_t)Bk.partial_floats * 4);
+    const size_t layout_bytes = Bk.partial_floats ? (size_t)lx::bucket_layout_bytes(Bk) : 0;
+    const size_t need = scan_ws_bytes(no, batch, ch, 0, 2) + align256((size_t)Bk.partial_floats * 4) +
+                        align256(layout_bytes);
     LX_TRY(ensure_ws(p, need, s), "workspace");
     Carve cv(p->ws);
     lx::ScanArgs A;
@@ -923,6 +925,7 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
     Bk.u = u;
     Bk.v = v;
     Bk.partial = Bk.partial_floats ? cv.take<float>((size_t)Bk.partial_floats) : nullptr;
+    Bk.layout = layout_bytes ? (void*)cv.take<char>(layout_bytes) : nullptr;
     LX_TRY(lx::bucket_launch(Bk, s), "bucket inputs");
     LX_TRY(lx::scan_launch(A, s), "scan over the output side");
     (void)p_i;
@@ -976,8 +979,9 @@ laplex_status grad_small_side(laplex_plan p, const GradSide& G, const float* V, 
     Bk.partial_floats = lx::bucket_partial_floats(Bk, nullptr, nullptr);
     if (Bk.partial_floats == 0) return LAPLEX_OK;  // not the LDS-binned shape: the table path instead
     const size_t rows = (size_t)ch * batch * Bk.ld;
+    const size_t layout_bytes = (size_t)lx::bucket_layout_bytes(Bk);
     const size_t need = scan_ws_bytes(G.no, batch, ch, 0, 2) + 3 * align256(rows * 4) +
-                        align256((size_t)Bk.partial_floats * 4);
+                        align256((size_t)Bk.partial_floats * 4) + align256(layout_bytes);
     LX_TRY(ensure_ws(p, need, s), "workspace");
     Carve cv(p->ws);
     lx::ScanArgs A;
@@ -997,6 +1001,7 @@ laplex_status grad_small_side(laplex_plan p, const GradSide& G, const float* V, 
     Bk.v = v;
     Bk.tie = tie;
     Bk.partial = cv.take<float>((size_t)Bk.partial_floats);
+    Bk.layout = cv.take<char>(layout_bytes);
     LX_TRY(lx::bucket_launch(Bk, s), "bucket inputs");
     LX_TRY(lx::scan_launch(A, s), "scan over the output side");
     lx::EvalLRArgs E;

@@ -37,20 +37,35 @@ constexpr int kGenThreads = 1024;
 
 // ------------------------------------------------------------- bucketing
 
-// Sorted bucketing for a small sorted output side (n_out <= 1024).  A
-// workgroup owns up to 8 vectors and a contiguous chunk of inputs, processed
-// in sub-chunks of 2048: each input's interval t and factors are computed
-// once, the sub-chunk is counting-sorted by t (stable: wave ballots give the
-// rank among equal t in index order, integer LDS counters the offsets), and
-// the factors and the values of all the workgroup's vectors are laid out in
-// interval order in LDS.  Thread j then owns u_j and v_j of every vector in
+// Sorted bucketing for a small sorted output side (n_out <= 1024), in two
+// kernels.  The input side is cut into sub-chunks of 2048 inputs.
+//
+// lx_bucket_layout (once per call, one workgroup per sub-chunk): each
+// input's interval t = #{s < q} (lookup table, below), then a stable
+// counting sort of the sub-chunk by t (wave ballots give the rank among
+// equal t in index order, integer LDS counters the offsets).  It records,
+// per input, its slot in interval order; per sub-chunk and interval, the
+// slot where the interval starts; and, in slot order, each input's factors
+// alpha = exp(-(s_t - q)) and beta = exp(-(q - s_{t-1})) times the cos and
+// sin of its phase.  Inputs past the end go to a bin after the last
+// interval, so they are never visited.
+//
+// lx_bucket_sorted (per group of up to 8 vectors, one workgroup per group
+// and chunk of sub-chunks): the values of the group's vectors are placed
+// in LDS by slot, and thread j owns u_j and v_j of every vector in
 // registers: it adds the alpha parts of interval j and the beta parts of
-// interval j+1, slot by slot.  No float atomics, and a fixed summation
-// order, so the results are deterministic.
+// interval j+1, slot by slot (LDS reads and FMAs only).  The
+// next sub-chunk's inputs load while the current one is accumulated.  No
+// float atomics, and a fixed summation order, so results are deterministic.
+//
+// The search, the sort and the factors depend on the anchors and phases
+// only, so doing them once instead of once per vector group leaves the
+// group kernel two barriers per sub-chunk and no transcendental work.
 constexpr int kSub = 2048;                      // inputs per sub-chunk
 constexpr int kSubItems = kSub / kGenThreads;   // 2 per thread
 constexpr int kGenWaves = kGenThreads / kWave;  // 16
 constexpr int kBucketVG = 8;                    // vectors per workgroup (max)
+constexpr int kBinStride = 1032;                // per-wave counter row: bins 0 .. n_out + 1 (<= 1025), padded
 
 __device__ __forceinline__ uint64_t match_bits11(uint32_t d) { return match_bits<11>(d); }
 
@@ -78,35 +93,154 @@ __device__ __forceinline__ uint32_t lower_bound_lut(const float* so, int no, con
     return (uint32_t)lo;
 }
 
+// Layout arrays in the scratch (bytes, each region 256-byte aligned):
+//   slot  : uint16[n_in]           slot of each input inside its sub-chunk
+//   start : uint16[subs][stride]   first slot of each bin t = 0 .. n_out + 1
+//   coef  : float4[subs * kSub]    by slot: (alpha cos, alpha sin, beta cos, beta sin)
+//   tie   : uint8[subs * kSub]     by slot, gradients only: 1 where the input equals s_t
+struct BucketLayout {
+    uint16_t* slot;
+    uint16_t* start;
+    float4* coef;
+    uint8_t* tie;
+    int64_t stride;
+};
+
+static inline size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+static BucketLayout bucket_layout_at(void* base, int64_t n_in, int64_t n_out, bool ties)
+{
+    const int64_t subs = (n_in + kSub - 1) / kSub;
+    BucketLayout L;
+    L.stride = (n_out + 2 + 7) & ~(int64_t)7;
+    char* p = (char*)base;
+    L.slot = (uint16_t*)p; p += al256((size_t)n_in * 2);
+    L.start = (uint16_t*)p; p += al256((size_t)subs * L.stride * 2);
+    L.coef = (float4*)p; p += al256((size_t)subs * kSub * 16);
+    L.tie = ties ? (uint8_t*)p : nullptr;
+    return L;
+}
+
+int64_t bucket_layout_bytes(const BucketArgs& a)
+{
+    const int64_t subs = (a.n_in + kSub - 1) / kSub;
+    const int64_t stride = (a.n_out + 2 + 7) & ~(int64_t)7;
+    return (int64_t)(al256((size_t)a.n_in * 2) + al256((size_t)subs * stride * 2) + al256((size_t)subs * kSub * 16) +
+                     (a.ties ? al256((size_t)subs * kSub) : 0));
+}
+
+template <int C>
+__global__ __launch_bounds__(kGenThreads) void lx_bucket_layout(BucketArgs A, BucketLayout L)
+{
+    __shared__ float so[kGenThreads];
+    __shared__ uint16_t wcnt[kGenWaves][kBinStride];  // per-wave counts, then each wave's first slot
+    __shared__ uint32_t start[kBinStride];
+    __shared__ uint16_t tab[kLut + 1];
+    __shared__ uint32_t sred[kGenWaves];
+
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+    const int no = (int)A.n_out;
+    const int nbins = no + 2;  // intervals 0 .. no, and the bin of inputs past the end
+    const int64_t sub = blockIdx.x;
+    const int64_t sub0 = sub * kSub;
+    for (int i = tid; i < no; i += kGenThreads) so[i] = A.s_out[i];
+    for (int i = tid; i < kGenWaves * kBinStride; i += kGenThreads) (&wcnt[0][0])[i] = 0;
+    __syncthreads();
+    const float lo_v = so[0], hi_v = so[no - 1];
+    const float width = (hi_v - lo_v) / (float)kLut;
+    const float inv_w = width > 0.f ? 1.f / width : 0.f;
+    for (int k = tid; k <= kLut; k += kGenThreads)
+        tab[k] = (uint16_t)(k == kLut ? no : lower_bound_f(so, no, lo_v + (float)k * width));
+
+    // items wave-striped: element sub0 + 128 w + 64 j + lane
+    int64_t idx[kSubItems];
+    float q[kSubItems], fc[kSubItems], fs[kSubItems];
+    uint32_t tt[kSubItems], slot[kSubItems];
+#pragma unroll
+    for (int j = 0; j < kSubItems; ++j) {
+        idx[j] = sub0 + w * (kSubItems * kWave) + j * kWave + lane;
+        const int64_t ic = idx[j] < A.n_in ? idx[j] : A.n_in - 1;
+        q[j] = A.in_anchor[ic];
+        if (C == 2) {
+            fc[j] = A.in_cos[ic];
+            fs[j] = A.in_sin[ic];
+        }
+    }
+    __syncthreads();  // tab complete
+#pragma unroll
+    for (int j = 0; j < kSubItems; ++j)
+        tt[j] = idx[j] < A.n_in ? lower_bound_lut(so, no, tab, lo_v, inv_w, q[j]) : (uint32_t)(no + 1);
+    // stable rank among equal bins: per wave, items in (j, lane) order
+#pragma unroll
+    for (int j = 0; j < kSubItems; ++j) {
+        const uint64_t peers = match_bits11(tt[j]);
+        const uint32_t below = count_below(peers);
+        const uint32_t prev = wcnt[w][tt[j]];
+        slot[j] = prev + below;
+        if (below == 0) wcnt[w][tt[j]] = (uint16_t)(prev + (uint32_t)__popcll(peers));
+    }
+    __syncthreads();
+    // per bin: offsets of the waves and the sub-chunk count; bins past the
+    // block size (at most two) follow the block's exclusive sum
+    uint32_t cnt = 0;
+    for (int b = tid; b < nbins; b += kGenThreads) {
+        uint32_t c[kGenWaves];
+#pragma unroll
+        for (int ww = 0; ww < kGenWaves; ++ww) c[ww] = wcnt[ww][b];
+        uint32_t run = 0;
+#pragma unroll
+        for (int ww = 0; ww < kGenWaves; ++ww) {
+            wcnt[ww][b] = (uint16_t)run;
+            run += c[ww];
+        }
+        if (b == tid) cnt = run;
+        else start[b] = run;  // count for now
+    }
+    uint32_t tot;
+    const uint32_t ex = block_exsum_u32<kGenWaves>(cnt, sred, tot);
+    if (tid < nbins) start[tid] = ex;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t run = tot;
+        for (int b = kGenThreads; b < nbins; ++b) {
+            const uint32_t c = start[b];
+            start[b] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    uint16_t* st = L.start + sub * L.stride;
+    for (int b = tid; b < nbins; b += kGenThreads) st[b] = (uint16_t)start[b];
+#pragma unroll
+    for (int j = 0; j < kSubItems; ++j) {
+        if (idx[j] < A.n_in) {
+            const uint32_t t = tt[j];
+            const uint32_t sl = start[t] + wcnt[w][t] + slot[j];
+            const float f0 = C == 2 ? fc[j] : 1.f, f1 = C == 2 ? fs[j] : 0.f;
+            const float al = t < (uint32_t)no ? decay_f(q[j], so[t], A.inv_t) : 0.f;
+            const float be = t > 0 ? decay_f(so[t - 1], q[j], A.inv_t) : 0.f;
+            L.slot[idx[j]] = (uint16_t)sl;
+            L.coef[sub0 + sl] = make_float4(al * f0, al * f1, be * f0, be * f1);
+            if (L.tie) L.tie[sub0 + sl] = (t < (uint32_t)no && so[t] == q[j]) ? 1 : 0;
+        }
+    }
+}
+
 template <int C, bool TIES>
-__global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, int VG, int groups,
+__global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, BucketLayout L, int VG, int groups,
                                                                int64_t chunk_len)
 {
     extern __shared__ float lds[];
     const int no = (int)A.n_out;  // <= kGenThreads
-    const int nbins = no + 1;     // intervals t = 0..no
-    float* so = lds;                                                                   // [no]
-    uint16_t* wcnt = reinterpret_cast<uint16_t*>(lds + pad64(no));                     // [16][nbins]
-    uint32_t* start = reinterpret_cast<uint32_t*>(wcnt + pad64(kGenWaves * nbins));    // [nbins+1]
-    float4* coef = reinterpret_cast<float4*>(start + pad64(nbins + 1));                // [kSub]: (au0, au1, bv0, bv1)
-    float4* xs = coef + kSub;                                                          // [kSub][2]: 8 vectors
-    uint8_t* tflag = reinterpret_cast<uint8_t*>(xs + 2 * kSub);                        // [kSub] (TIES): q == s_t
-    uint16_t* tab = reinterpret_cast<uint16_t*>(tflag + (TIES ? kSub : 0));            // [kLut + 1]
-    __shared__ uint32_t sred[kGenWaves];
+    float4* xs = reinterpret_cast<float4*>(lds);                // [kSub][2]: 8 vectors by slot
+    float4* cs = xs + 2 * kSub;                                 // [kSub]: factors by slot
+    uint8_t* ts = reinterpret_cast<uint8_t*>(cs + kSub);        // [kSub]: tie flags by slot (TIES)
 
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
     const int g = (int)(blockIdx.x % groups);
     const int64_t chunk = blockIdx.x / groups;
     const int64_t v0 = (int64_t)g * VG;
     const int nv = (int)((A.batch - v0) < VG ? (A.batch - v0) : VG);
-    for (int i = tid; i < no; i += kGenThreads) so[i] = A.s_out[i];
-    __syncthreads();
-    // interval lookup table (finite anchors: plans reject others)
-    const float lo_v = so[0], hi_v = so[no - 1];
-    const float width = (hi_v - lo_v) / (float)kLut;
-    const float inv_w = width > 0.f ? 1.f / width : 0.f;
-    for (int k = tid; k <= kLut; k += kGenThreads)
-        tab[k] = (uint16_t)(k == kLut ? no : lower_bound_f(so, no, lo_v + (float)k * width));
 
     float au[kBucketVG][C], av[kBucketVG][C];  // u_tid and v_tid of each vector
     float at[TIES ? kBucketVG : 1][C];         // tie_tid
@@ -122,100 +256,64 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, in
     const int64_t j0 = chunk * chunk_len;
     int64_t j1 = j0 + chunk_len;
     if (j1 > A.n_in) j1 = A.n_in;
+
+    // One sub-chunk's inputs, loaded one sub-chunk ahead: the values of the
+    // group's vectors and the slot of this thread's items (element
+    // sub0 + 128 w + 64 j + lane), the factors (and tie flags) of slots
+    // 128 w + 64 j + lane, and the starts of intervals tid .. tid + 2.
+    // (Slots, flags and starts stay narrow until used: a widening next to
+    // the load would make the accumulation wait for the whole prefetch.)
+    float xin[kSubItems][kBucketVG];
+    float cfn[kSubItems][4];
+    uint8_t tfn[TIES ? kSubItems : 1];
+    uint16_t sln[kSubItems], stn[3];
+    auto load_sub = [&](int64_t base) {
+        const int64_t sub = base / kSub;
+#pragma unroll
+        for (int j = 0; j < kSubItems; ++j) {
+            const int p = w * (kSubItems * kWave) + j * kWave + lane;
+            const int64_t id = base + p;
+            const int64_t idc = id < j1 ? id : j0;  // a valid address; the value is not used
+#pragma unroll
+            for (int vi = 0; vi < kBucketVG; ++vi) {
+                const int64_t vv = v0 + (vi < nv ? vi : 0);
+                xin[j][vi] = A.x[vv * A.n_in + idc];
+            }
+            sln[j] = L.slot[idc];
+            const float4 cf = L.coef[base + p];
+            cfn[j][0] = cf.x;
+            cfn[j][1] = cf.y;
+            cfn[j][2] = cf.z;
+            cfn[j][3] = cf.w;
+            if (TIES) tfn[j] = L.tie[base + p];
+        }
+        const uint16_t* st = L.start + sub * L.stride;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) stn[k] = st[tid + k < no + 2 ? tid + k : 0];
+    };
+    if (j0 < j1) load_sub(j0);
     for (int64_t sub0 = j0; sub0 < j1; sub0 += kSub) {
-        for (int i = tid; i < kGenWaves * nbins; i += kGenThreads) wcnt[i] = 0;
-        __syncthreads();
-        // this thread's items: element sub0 + 128 w + 64 j + lane (wave-striped);
-        // the vectors' values are loaded first, in flight during the search
-        int64_t idx[kSubItems];
-        uint32_t tt[kSubItems], slot[kSubItems];
-        bool tie[kSubItems];
-        float4 cf[kSubItems];
-        float xin[kSubItems][kBucketVG];
-#pragma unroll
-        for (int j = 0; j < kSubItems; ++j) idx[j] = sub0 + w * (kSubItems * kWave) + j * kWave + lane;
-        if (nv == kBucketVG && sub0 + kSub <= j1) {
-#pragma unroll
-            for (int j = 0; j < kSubItems; ++j)
-#pragma unroll
-                for (int vi = 0; vi < kBucketVG; ++vi) xin[j][vi] = A.x[(v0 + vi) * A.n_in + idx[j]];
-        } else {
-#pragma unroll
-            for (int j = 0; j < kSubItems; ++j)
-#pragma unroll
-                for (int vi = 0; vi < kBucketVG; ++vi)
-                    xin[j][vi] = (vi < nv && idx[j] < j1) ? A.x[(v0 + vi) * A.n_in + idx[j]] : 0.f;
-        }
+        __syncthreads();  // the previous sub-chunk's slots have been read
 #pragma unroll
         for (int j = 0; j < kSubItems; ++j) {
-            float al = 0.f, be = 0.f, f0 = 1.f, f1 = 0.f;
-            uint32_t t = (uint32_t)no;  // past the end: weight 0 in the last interval
-            tie[j] = false;
-            if (idx[j] < j1) {
-                const float q = A.in_anchor[idx[j]];
-                t = lower_bound_lut(so, no, tab, lo_v, inv_w, q);
-                tie[j] = t < (uint32_t)no && so[t] == q;
-                al = t < (uint32_t)no ? decay_f(q, so[t], A.inv_t) : 0.f;
-                be = t > 0 ? decay_f(so[t - 1], q, A.inv_t) : 0.f;
-                if (C == 2) {
-                    f0 = A.in_cos[idx[j]];
-                    f1 = A.in_sin[idx[j]];
-                }
-            }
-            tt[j] = t;
-            cf[j] = make_float4(al * f0, al * f1, be * f0, be * f1);
-        }
-        // stable rank among equal intervals: per wave, items in (j, lane) order
+            const int p = w * (kSubItems * kWave) + j * kWave + lane;
+            if (sub0 + p < j1) {
+                const uint32_t sl = sln[j];
+                float x8[kBucketVG];
 #pragma unroll
-        for (int j = 0; j < kSubItems; ++j) {
-            const uint64_t peers = match_bits11(tt[j]);
-            const uint32_t below = count_below(peers);
-            const uint32_t prev = wcnt[w * nbins + tt[j]];
-            slot[j] = prev + below;
-            if (below == 0) wcnt[w * nbins + tt[j]] = (uint16_t)(prev + (uint32_t)__popcll(peers));
-        }
-        __syncthreads();
-        // per interval: offsets of the waves and the sub-chunk count; then starts
-        uint32_t cnt0 = 0, cnt1 = 0;
-        if (tid < nbins) {
-            uint32_t run = 0;
-            for (int ww = 0; ww < kGenWaves; ++ww) {
-                const uint32_t c = wcnt[ww * nbins + tid];
-                wcnt[ww * nbins + tid] = (uint16_t)run;
-                run += c;
+                for (int vi = 0; vi < kBucketVG; ++vi) x8[vi] = vi < nv ? xin[j][vi] : 0.f;
+                xs[2 * sl] = make_float4(x8[0], x8[1], x8[2], x8[3]);
+                xs[2 * sl + 1] = make_float4(x8[4], x8[5], x8[6], x8[7]);
             }
-            cnt0 = run;
+            cs[p] = make_float4(cfn[j][0], cfn[j][1], cfn[j][2], cfn[j][3]);
+            if (TIES) ts[p] = tfn[TIES ? j : 0];
         }
-        if (tid + kGenThreads < nbins) {  // interval 1024 when no == 1024
-            uint32_t run = 0;
-            for (int ww = 0; ww < kGenWaves; ++ww) {
-                const uint32_t c = wcnt[ww * nbins + tid + kGenThreads];
-                wcnt[ww * nbins + tid + kGenThreads] = (uint16_t)run;
-                run += c;
-            }
-            cnt1 = run;
-        }
-        (void)cnt1;
-        uint32_t tot0;
-        const uint32_t ex0 = block_exsum_u32<kGenWaves>(cnt0, sred, tot0);
-        if (tid < nbins) start[tid] = ex0;
-        if (tid + kGenThreads < nbins) start[tid + kGenThreads] = tot0;
-        if (tid == 0) start[nbins] = kSub;
+        const uint32_t s0 = stn[0], s1 = stn[1], s2 = stn[2];
         __syncthreads();
-        // lay out factors and the values of every vector in interval order
-#pragma unroll
-        for (int j = 0; j < kSubItems; ++j) {
-            const uint32_t sl = slot[j] + start[tt[j]] + wcnt[w * nbins + tt[j]];
-            coef[sl] = cf[j];
-            if (TIES) tflag[sl] = tie[j] ? 1 : 0;
-            xs[2 * sl] = make_float4(xin[j][0], xin[j][1], xin[j][2], xin[j][3]);
-            xs[2 * sl + 1] = make_float4(xin[j][4], xin[j][5], xin[j][6], xin[j][7]);
-        }
-        __syncthreads();
+        if (sub0 + kSub < j1) load_sub(sub0 + kSub);
         if (tid < no) {
-            const uint32_t s0 = start[tid], s1 = start[tid + 1], s2 = start[tid + 2];
             for (uint32_t sl = s0; sl < s1; ++sl) {  // interval tid: alpha parts -> u_tid
-                const float4 f = coef[sl];
+                const float2 f = *reinterpret_cast<const float2*>(&cs[sl].x);
                 const float4 xa = xs[2 * sl], xb = xs[2 * sl + 1];
                 const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
@@ -224,7 +322,7 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, in
                     if (C == 2) au[vi][C - 1] = fmaf(f.y, xv[vi], au[vi][C - 1]);
                 }
                 if (TIES) {  // a tie's alpha is exactly 1: its factors are the phase's cos, sin
-                    const float tw = tflag[sl] ? 1.f : 0.f;
+                    const float tw = ts[sl] ? 1.f : 0.f;
 #pragma unroll
                     for (int vi = 0; vi < (TIES ? kBucketVG : 1); ++vi) {
                         at[vi][0] = fmaf(tw * f.x, xv[vi], at[vi][0]);
@@ -233,17 +331,16 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, in
                 }
             }
             for (uint32_t sl = s1; sl < s2; ++sl) {  // interval tid+1: beta parts -> v_tid
-                const float4 f = coef[sl];
+                const float2 f = *reinterpret_cast<const float2*>(&cs[sl].z);
                 const float4 xa = xs[2 * sl], xb = xs[2 * sl + 1];
                 const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
                 for (int vi = 0; vi < kBucketVG; ++vi) {
-                    av[vi][0] = fmaf(f.z, xv[vi], av[vi][0]);
-                    if (C == 2) av[vi][C - 1] = fmaf(f.w, xv[vi], av[vi][C - 1]);
+                    av[vi][0] = fmaf(f.x, xv[vi], av[vi][0]);
+                    if (C == 2) av[vi][C - 1] = fmaf(f.y, xv[vi], av[vi][C - 1]);
                 }
             }
         }
-        __syncthreads();
     }
     // partial layout [chunk][batch][C][P][no], P = 2 (u, v) or 3 (u, v, tie)
     constexpr int P = TIES ? 3 : 2;
@@ -263,10 +360,9 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, in
 
 static size_t bucket_sorted_lds(int64_t no, int C, bool ties)
 {
+    (void)no;
     (void)C;
-    const int64_t nbins = no + 1;
-    return (size_t)(pad64(no) + pad64(kGenWaves * nbins) / 2 + pad64(nbins + 1)) * 4 + (size_t)kSub * 16 * 3 +
-           (ties ? (size_t)kSub : 0) + (size_t)(kLut + 1) * 2;
+    return (size_t)kSub * 32 + (size_t)kSub * 16 + (ties ? (size_t)kSub : 0);
 }
 
 // Sums the per-workgroup partials in chunk order (float64) into u, v and,
@@ -364,15 +460,19 @@ hipError_t bucket_launch(BucketArgs& a, hipStream_t s)
     const bool two = a.channels == 2;
     const bool ties = a.ties;
     if (ties && !a.tie) return hipErrorInvalidValue;
-    if (vg > 0 && a.partial && a.n_in > 0) {
+    if (vg > 0 && a.partial && a.layout && a.n_in > 0) {
         const size_t shmem = bucket_sorted_lds(a.n_out, a.channels, ties);
         const unsigned blocks = (unsigned)((int64_t)chunks * groups);
+        const BucketLayout L = bucket_layout_at(a.layout, a.n_in, a.n_out, ties);
+        const unsigned subs = (unsigned)((a.n_in + kSub - 1) / kSub);
+        if (two) LX_LAUNCH("bucket_layout", s, (lx_bucket_layout<2><<<subs, kGenThreads, 0, s>>>(a, L)));
+        else LX_LAUNCH("bucket_layout", s, (lx_bucket_layout<1><<<subs, kGenThreads, 0, s>>>(a, L)));
 #define LX_BKS(CC, TT)                                                                                         \
     do {                                                                                                       \
         (void)hipFuncSetAttribute((const void*)lx_bucket_sorted<CC, TT>, hipFuncAttributeMaxDynamicSharedMemorySize, \
                                   (int)shmem);                                                                 \
         LX_LAUNCH("bucket_sorted", s,                                                                          \
-                  (lx_bucket_sorted<CC, TT><<<blocks, kGenThreads, shmem, s>>>(a, vg, groups, chunk_len)));     \
+                  (lx_bucket_sorted<CC, TT><<<blocks, kGenThreads, shmem, s>>>(a, L, vg, groups, chunk_len)));  \
     } while (0)
         if (two) {
             if (ties) LX_BKS(2, true);

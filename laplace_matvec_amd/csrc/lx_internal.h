@@ -145,11 +145,16 @@ struct BucketArgs {
     float* tie = nullptr;            // same layout as u (when ties)
     float* partial = nullptr;        // scratch for the LDS-binned path
     int64_t partial_floats = 0;
+    void* layout = nullptr;          // scratch for the LDS-binned path: bucket_layout_bytes()
     int lds_bytes = 0;               // LDS budget per workgroup (0: global path)
 };
 // Scratch floats the LDS-binned bucketing needs for these sizes (0 if it is
 // not used and the global-atomics path runs instead).
 int64_t bucket_partial_floats(const BucketArgs& a, int* groups, int* chunks);
+// Bytes of the per-call input layout of the LDS-binned path (slots of the
+// inputs, interval starts per sub-chunk, anchors and phase factors in slot
+// order), 256-byte aligned.
+int64_t bucket_layout_bytes(const BucketArgs& a);
 hipError_t bucket_launch(BucketArgs& a, hipStream_t s);
 
 struct EvalArgs {
