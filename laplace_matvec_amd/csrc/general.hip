@@ -78,11 +78,12 @@ __device__ __forceinline__ uint64_t match_bits11(uint32_t d) { return match_bits
 // exact #{s < q}.
 constexpr int kLut = 4096;
 
+template <int LUT = kLut>
 __device__ __forceinline__ uint32_t lower_bound_lut(const float* so, int no, const uint16_t* tab, float lo_v,
                                                     float inv_w, float q)
 {
     const float fk = (q - lo_v) * inv_w;
-    const int k = !(fk >= 0.f) ? 0 : (fk >= (float)(kLut - 1) ? kLut - 1 : (int)fk);
+    const int k = !(fk >= 0.f) ? 0 : (fk >= (float)(LUT - 1) ? LUT - 1 : (int)fk);
     int lo = tab[k], hi = tab[k + 1];
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
@@ -511,6 +512,109 @@ hipError_t bucket_launch(BucketArgs& a, hipStream_t s)
 
 // ------------------------------------------------------------- evaluation
 
+// Evaluation with the tables of a group of up to 8 vectors in LDS.  Row t
+// (t = 0 .. n_in) holds, per vector, PL_{t-1} and PR_t of both channels
+// side by side (zero outside the tables), so an output whose interval is
+// t reads one 16-byte entry per vector; rows are padded to 36 words so
+// that the rows of different outputs spread over the LDS banks.  The
+// interval comes from a lookup table over the sorted inputs, and each
+// thread loads its next output's anchor and phase factors while it
+// evaluates the current one.
+constexpr int kEvalVG = 8;
+constexpr int kEvalLut = 2048;
+template <int C>
+constexpr int eval_row_words() { return C == 2 ? 36 : 20; }
+
+template <int C>
+__global__ __launch_bounds__(kGenThreads) void lx_eval_rows(EvalArgs A, int VG, int groups, int64_t chunk_len)
+{
+    extern __shared__ float lds[];
+    constexpr int RW = eval_row_words<C>();
+    const int ni = (int)A.n_in;
+    const int g = (int)(blockIdx.x % groups);
+    const int64_t chunk = blockIdx.x / groups;
+    const int64_t v0 = (int64_t)g * VG;
+    const int nv = (int)((A.batch - v0) < VG ? (A.batch - v0) : VG);
+    float* si = lds;                                                  // [ni]
+    float* rows = lds + pad64(ni);                                    // [ni + 1][RW]
+    uint16_t* tab = reinterpret_cast<uint16_t*>(rows + (int64_t)(ni + 1) * RW);  // [kEvalLut + 1]
+    const int tid = threadIdx.x;
+    for (int i = tid; i < ni; i += kGenThreads) si[i] = A.s_in[i];
+    // entry (t, vi): PL_{t-1} of channels 0, 1 then PR_t of channels 0, 1
+    // (C == 2), or PL_{t-1}, PR_t (C == 1); tables read along t (coalesced)
+    constexpr int E = 2 * C;  // words per entry
+    for (int64_t i = tid; i < (int64_t)kEvalVG * C * (ni + 1); i += kGenThreads) {
+        const int64_t rowc = i / (ni + 1);  // vi * C + c
+        const int t = (int)(i - rowc * (ni + 1));
+        const int vi = (int)(rowc / C), c = (int)(rowc - (int64_t)vi * C);
+        const int64_t src = ((int64_t)c * A.batch + v0 + vi) * A.ld;
+        const bool have = vi < nv;
+        float* e = rows + (int64_t)t * RW + vi * E;
+        e[c] = have && t > 0 ? A.pl[src + t - 1] : 0.f;
+        e[C + c] = have && t < ni ? A.pr[src + t] : 0.f;
+    }
+    __syncthreads();
+    const float lo_v = si[0], hi_v = si[ni - 1];
+    const float width = (hi_v - lo_v) / (float)kEvalLut;
+    const float inv_w = width > 0.f ? 1.f / width : 0.f;
+    for (int k = tid; k <= kEvalLut; k += kGenThreads)
+        tab[k] = (uint16_t)(k == kEvalLut ? ni : lower_bound_f(si, ni, lo_v + (float)k * width));
+    __syncthreads();
+
+    const int64_t i0 = chunk * chunk_len;
+    int64_t i1 = i0 + chunk_len;
+    if (i1 > A.n_out) i1 = A.n_out;
+    int64_t i = i0 + tid;
+    const int64_t last = i1 > i0 ? i1 - 1 : i0;
+    float o_n = 0.f, c_n = 1.f, s_n = 0.f;
+    auto load_out = [&](int64_t k) {
+        const int64_t kc = k < i1 ? k : last;
+        o_n = A.out_anchor[kc];
+        if (C == 2) {
+            c_n = A.out_cos[kc];
+            s_n = A.out_sin[kc];
+        }
+    };
+    if (i < i1) load_out(i);
+    for (; i < i1; i += kGenThreads) {
+        const float o = o_n;
+        float gc[C];
+        gc[0] = C == 2 ? c_n : 1.f;
+        if (C == 2) gc[C - 1] = s_n;
+        load_out(i + kGenThreads);
+        const int t = (int)lower_bound_lut<kEvalLut>(si, ni, tab, lo_v, inv_w, o);
+        const float al = t > 0 ? decay_f(si[t - 1], o, A.inv_t) : 0.f;
+        const float be = t < ni ? decay_f(o, si[t], A.inv_t) : 0.f;
+        const float* row = rows + (int64_t)t * RW;
+#pragma unroll
+        for (int vi = 0; vi < kEvalVG; ++vi) {
+            if (vi < nv) {
+                float lv[C], rv[C];
+                if (C == 2) {
+                    const float4 e = *reinterpret_cast<const float4*>(row + vi * E);
+                    lv[0] = e.x;
+                    lv[C - 1] = e.y;
+                    rv[0] = e.z;
+                    rv[C - 1] = e.w;
+                } else {
+                    const float2 e = *reinterpret_cast<const float2*>(row + vi * E);
+                    lv[0] = e.x;
+                    rv[0] = e.y;
+                }
+                float acc = 0.f;
+#pragma unroll
+                for (int c = 0; c < C; ++c) acc = fmaf(gc[c], fmaf(al, lv[c], be * rv[c]), acc);
+                A.y[(v0 + vi) * A.n_out + i] = acc;
+            }
+        }
+    }
+}
+
+static size_t eval_rows_lds(int64_t ni, int C)
+{
+    return (size_t)(pad64(ni) + (ni + 1) * (C == 2 ? 36 : 20)) * 4 + (size_t)(kEvalLut + 1) * 2;
+}
+
 template <int C, bool USE_LDS>
 __global__ __launch_bounds__(kGenThreads) void lx_eval(EvalArgs A, int VG, int groups, int64_t chunk_len)
 {
@@ -576,6 +680,28 @@ __global__ __launch_bounds__(kGenThreads) void lx_eval(EvalArgs A, int VG, int g
 hipError_t eval_launch(const EvalArgs& a, hipStream_t s)
 {
     if (a.n_out <= 0 || a.batch <= 0) return hipSuccess;
+    if (a.n_in >= 1 && a.n_in <= 0xFFFF && a.lds_bytes > 0 &&
+        eval_rows_lds(a.n_in, a.channels) <= (size_t)a.lds_bytes) {
+        // groups of at most 8 vectors, as even as possible
+        const int64_t groups = (a.batch + kEvalVG - 1) / kEvalVG;
+        const int vg = (int)((a.batch + groups - 1) / groups);
+        int64_t chunks = (a.n_out + 16383) / 16384;
+        const int64_t cap = (2048 + groups - 1) / groups;
+        if (chunks > cap) chunks = cap;
+        if (chunks < 1) chunks = 1;
+        const int64_t chunk_len = (a.n_out + chunks - 1) / chunks;
+        chunks = (a.n_out + chunk_len - 1) / chunk_len;
+        const unsigned blocks = (unsigned)(chunks * groups);
+        const size_t shmem = eval_rows_lds(a.n_in, a.channels);
+        if (a.channels == 2) {
+            (void)hipFuncSetAttribute((const void*)lx_eval_rows<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+            LX_LAUNCH("eval", s, (lx_eval_rows<2><<<blocks, kGenThreads, shmem, s>>>(a, vg, (int)groups, chunk_len)));
+        } else {
+            (void)hipFuncSetAttribute((const void*)lx_eval_rows<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+            LX_LAUNCH("eval", s, (lx_eval_rows<1><<<blocks, kGenThreads, shmem, s>>>(a, vg, (int)groups, chunk_len)));
+        }
+        return hipSuccess;
+    }
     const int64_t lds_floats = a.lds_bytes / 4;
     int64_t vg = (lds_floats - pad64(a.n_in)) / (2 * (int64_t)a.channels * (a.n_in > 0 ? a.n_in : 1));
     if (vg > 16) vg = 16;
