@@ -69,30 +69,7 @@ constexpr int kBinStride = 1032;                // per-wave counter row: bins 0 
 
 __device__ __forceinline__ uint64_t match_bits11(uint32_t d) { return match_bits<11>(d); }
 
-// Interval search through a lookup table: the range [s_0, s_{n-1}] of the
-// sorted outputs is cut into kLut equal cells and tab[k] = #{s < left edge
-// of cell k} (tab[kLut] = n), so the interval of q lies in [tab[k],
-// tab[k+1]] for q's cell k, a few candidates for smooth data.  The result is
-// checked against its neighbours and a full bisection replaces it when the
-// cell arithmetic rounded q into the wrong cell: the answer is always the
-// exact #{s < q}.
-constexpr int kLut = 4096;
-
-template <int LUT = kLut>
-__device__ __forceinline__ uint32_t lower_bound_lut(const float* so, int no, const uint16_t* tab, float lo_v,
-                                                    float inv_w, float q)
-{
-    const float fk = (q - lo_v) * inv_w;
-    const int k = !(fk >= 0.f) ? 0 : (fk >= (float)(LUT - 1) ? LUT - 1 : (int)fk);
-    int lo = tab[k], hi = tab[k + 1];
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (so[mid] < q) lo = mid + 1;
-        else hi = mid;
-    }
-    if ((lo > 0 && !(so[lo - 1] < q)) || (lo < no && so[lo] < q)) lo = (int)lower_bound_f(so, no, q);
-    return (uint32_t)lo;
-}
+constexpr int kLut = 4096;  // cells of the interval lookup table (lower_bound_lut)
 
 // Layout arrays in the scratch (bytes, each region 256-byte aligned):
 //   slot  : uint16[n_in]           slot of each input inside its sub-chunk
@@ -170,7 +147,7 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_layout(BucketArgs A, Bu
     __syncthreads();  // tab complete
 #pragma unroll
     for (int j = 0; j < kSubItems; ++j)
-        tt[j] = idx[j] < A.n_in ? lower_bound_lut(so, no, tab, lo_v, inv_w, q[j]) : (uint32_t)(no + 1);
+        tt[j] = idx[j] < A.n_in ? lower_bound_lut<kLut>(so, no, tab, lo_v, inv_w, q[j]) : (uint32_t)(no + 1);
     // stable rank among equal bins: per wave, items in (j, lane) order
 #pragma unroll
     for (int j = 0; j < kSubItems; ++j) {
@@ -520,10 +497,6 @@ hipError_t bucket_launch(BucketArgs& a, hipStream_t s)
 // interval comes from a lookup table over the sorted inputs, and each
 // thread loads its next output's anchor and phase factors while it
 // evaluates the current one.
-constexpr int kEvalVG = 8;
-constexpr int kEvalLut = 2048;
-template <int C>
-constexpr int eval_row_words() { return C == 2 ? 36 : 20; }
 
 template <int C>
 __global__ __launch_bounds__(kGenThreads) void lx_eval_rows(EvalArgs A, int VG, int groups, int64_t chunk_len)
@@ -610,10 +583,6 @@ __global__ __launch_bounds__(kGenThreads) void lx_eval_rows(EvalArgs A, int VG, 
     }
 }
 
-static size_t eval_rows_lds(int64_t ni, int C)
-{
-    return (size_t)(pad64(ni) + (ni + 1) * (C == 2 ? 36 : 20)) * 4 + (size_t)(kEvalLut + 1) * 2;
-}
 
 template <int C, bool USE_LDS>
 __global__ __launch_bounds__(kGenThreads) void lx_eval(EvalArgs A, int VG, int groups, int64_t chunk_len)

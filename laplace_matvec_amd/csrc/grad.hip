@@ -393,6 +393,137 @@ hipError_t grad_sym_launch(const GradSymArgs& a, hipStream_t s)
 
 constexpr int kEvalThreads = 1024;
 
+// The same outputs with the tables of a group of up to 8 vectors in LDS
+// rows (entry (t, vector): PL_{t-1} and PR_t of every channel, one 16-byte
+// read; rows padded so different outputs' rows spread over the banks).
+// Each thread keeps kGradOuts outputs of its workgroup's chunk -- their
+// intervals t< and t<=, decays and phase factors, and the anchor and phase
+// sums -- in registers across all vector groups: the searches and decays
+// are done once per output, the weights w of each group are read once, and
+// the sums are written once at the end.
+constexpr int kGradOuts = 4;
+
+template <int C>
+__global__ __launch_bounds__(kEvalThreads) void lx_eval_grad_rows(EvalGradArgs A, int VG)
+{
+    extern __shared__ float lds[];
+    constexpr int RW = eval_row_words<C>();
+    constexpr int E = 2 * C;  // words per entry
+    const int ni = (int)A.n_in;
+    const int tid = threadIdx.x;
+    float* si = lds;                                                             // [ni]
+    float* rows = lds + pad64(ni);                                               // [ni + 1][RW]
+    uint16_t* tab = reinterpret_cast<uint16_t*>(rows + (int64_t)(ni + 1) * RW);  // [kEvalLut + 1]
+    for (int i = tid; i < ni; i += kEvalThreads) si[i] = A.s_in[i];
+    __syncthreads();
+    const float lo_v = si[0], hi_v = si[ni - 1];
+    const float width = (hi_v - lo_v) / (float)kEvalLut;
+    const float inv_w = width > 0.f ? 1.f / width : 0.f;
+    for (int k = tid; k <= kEvalLut; k += kEvalThreads)
+        tab[k] = (uint16_t)(k == kEvalLut ? ni : lower_bound_f(si, ni, lo_v + (float)k * width));
+    __syncthreads();
+
+    // this thread's outputs: i = chunk start + q * kEvalThreads + tid
+    const int64_t base = (int64_t)blockIdx.x * (kGradOuts * kEvalThreads) + tid;
+    uint32_t tt[kGradOuts];  // t< | t<= << 16 (n_in <= 65535)
+    float al[kGradOuts], be[kGradOuts], be2[kGradOuts], oc[kGradOuts], os[kGradOuts];
+    float d_a[kGradOuts], d_p[kGradOuts];
+#pragma unroll
+    for (int q = 0; q < kGradOuts; ++q) {
+        const int64_t i = base + (int64_t)q * kEvalThreads;
+        const int64_t ic = i < A.n_out ? i : A.n_out - 1;
+        const float o = A.out_anchor[ic];
+        oc[q] = 1.f;
+        os[q] = 0.f;
+        if (C == 2) {
+            oc[q] = A.out_cos[ic];
+            os[q] = A.out_sin[ic];
+        }
+        const int lt = (int)lower_bound_lut<kEvalLut>(si, ni, tab, lo_v, inv_w, o);
+        // t<= = t< unless anchors equal to o follow (ties): then bisect past them
+        const int le = (lt < ni && si[lt] == o) ? (int)upper_bound_f(si, ni, o, lt) : lt;
+        tt[q] = (uint32_t)lt | ((uint32_t)le << 16);
+        al[q] = lt > 0 ? decay_f(si[lt - 1], o, A.inv_t) : 0.f;
+        be[q] = lt < ni ? decay_f(o, si[lt], A.inv_t) : 0.f;
+        be2[q] = le < ni ? decay_f(o, si[le], A.inv_t) : 0.f;
+        d_a[q] = d_p[q] = 0.f;
+    }
+
+    const int groups = (int)((A.batch + VG - 1) / VG);
+    for (int g = 0; g < groups; ++g) {
+        const int64_t v0 = (int64_t)g * VG;
+        const int nv = (int)((A.batch - v0) < VG ? (A.batch - v0) : VG);
+        __syncthreads();  // the previous group's rows have been read
+        for (int64_t i = tid; i < (int64_t)kEvalVG * C * (ni + 1); i += kEvalThreads) {
+            const int64_t rowc = i / (ni + 1);  // vi * C + c
+            const int t = (int)(i - rowc * (ni + 1));
+            const int vi = (int)(rowc / C), c = (int)(rowc - (int64_t)vi * C);
+            const int64_t src = ((int64_t)c * A.batch + v0 + vi) * A.ld;
+            const bool have = vi < nv;
+            float* e = rows + (int64_t)t * RW + vi * E;
+            e[c] = have && t > 0 ? A.pl[src + t - 1] : 0.f;
+            e[C + c] = have && t < ni ? A.pr[src + t] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kGradOuts; ++q) {
+            const int64_t i = base + (int64_t)q * kEvalThreads;
+            if (i >= A.n_out) continue;
+            const float* r1 = rows + (int64_t)(tt[q] & 0xFFFFu) * RW;
+            const float* r2 = rows + (int64_t)(tt[q] >> 16) * RW;
+            // the group's weights, all loads in flight before their use
+            float wt[kEvalVG];
+#pragma unroll
+            for (int vi = 0; vi < kEvalVG; ++vi) wt[vi] = A.w[(v0 + (vi < nv ? vi : 0)) * A.n_out + i];
+            float acc_a = 0.f, acc_p = 0.f;
+#pragma unroll
+            for (int vi = 0; vi < kEvalVG; ++vi) {
+                if (vi < nv) {
+                    float lv[C], rv[C], rv2[C];
+                    if (C == 2) {
+                        const float4 e1 = *reinterpret_cast<const float4*>(r1 + vi * E);
+                        const float2 e2 = *reinterpret_cast<const float2*>(r2 + vi * E + C);
+                        lv[0] = e1.x;
+                        lv[C - 1] = e1.y;
+                        rv[0] = e1.z;
+                        rv[C - 1] = e1.w;
+                        rv2[0] = e2.x;
+                        rv2[C - 1] = e2.y;
+                    } else {
+                        const float2 e1 = *reinterpret_cast<const float2*>(r1 + vi * E);
+                        lv[0] = e1.x;
+                        rv[0] = e1.y;
+                        rv2[0] = r2[vi * E + C];
+                    }
+                    float sig = 0.f, kin = 0.f, pla = 0.f;
+#pragma unroll
+                    for (int c = 0; c < C; ++c) {
+                        const float k0 = fmaf(al[q], lv[c], be[q] * rv[c]);
+                        const float s0 = fmaf(al[q], lv[c], -be2[q] * rv2[c]);
+                        const float fo = c == 0 ? oc[q] : os[q];
+                        sig = fmaf(fo, s0, sig);
+                        pla = fmaf(fo, k0, pla);
+                        if (C == 2) kin = fmaf(c == 0 ? os[q] : -oc[q], k0, kin);
+                    }
+                    acc_a = fmaf(wt[vi], sig, acc_a);
+                    acc_p = fmaf(-wt[vi], kin, acc_p);
+                    if (A.y) A.y[(v0 + vi) * A.n_out + i] = pla;
+                }
+            }
+            d_a[q] = d_a[q] + A.anchor_scale * acc_a;
+            d_p[q] = d_p[q] + acc_p;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < kGradOuts; ++q) {
+        const int64_t i = base + (int64_t)q * kEvalThreads;
+        if (i < A.n_out) {
+            if (A.d_anchor) A.d_anchor[i] = d_a[q];
+            if (C == 2 && A.d_phase) A.d_phase[i] = d_p[q];
+        }
+    }
+}
+
 template <int C, bool USE_LDS>
 __global__ __launch_bounds__(kEvalThreads) void lx_eval_grad(EvalGradArgs A, int VG, int64_t chunk_len)
 {
@@ -478,6 +609,25 @@ __global__ __launch_bounds__(kEvalThreads) void lx_eval_grad(EvalGradArgs A, int
 hipError_t eval_grad_launch(const EvalGradArgs& a, hipStream_t s)
 {
     if (a.n_out <= 0 || a.batch <= 0) return hipSuccess;
+    if (a.n_in >= 1 && a.n_in <= 0xFFFF && a.lds_bytes > 0 &&
+        eval_rows_lds(a.n_in, a.channels) <= (size_t)a.lds_bytes) {
+        // groups of at most 8 vectors, as even as possible
+        const int64_t groups = (a.batch + kEvalVG - 1) / kEvalVG;
+        const int vg = (int)((a.batch + groups - 1) / groups);
+        const int64_t per = (int64_t)kGradOuts * kEvalThreads;
+        const unsigned blocks = (unsigned)((a.n_out + per - 1) / per);
+        const size_t shmem = eval_rows_lds(a.n_in, a.channels);
+        if (a.channels == 2) {
+            (void)hipFuncSetAttribute((const void*)lx_eval_grad_rows<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      (int)shmem);
+            LX_LAUNCH("eval_grad", s, (lx_eval_grad_rows<2><<<blocks, kEvalThreads, shmem, s>>>(a, vg)));
+        } else {
+            (void)hipFuncSetAttribute((const void*)lx_eval_grad_rows<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      (int)shmem);
+            LX_LAUNCH("eval_grad", s, (lx_eval_grad_rows<1><<<blocks, kEvalThreads, shmem, s>>>(a, vg)));
+        }
+        return hipSuccess;
+    }
     const int64_t lds_floats = a.lds_bytes / 4;
     int64_t vg = (lds_floats - pad64(a.n_in)) / (2 * (int64_t)a.channels * (a.n_in > 0 ? a.n_in : 1));
     if (vg > 16) vg = 16;
@@ -553,8 +703,8 @@ hipError_t eval_lr_launch(const EvalLRArgs& a, hipStream_t s)
 {
     if (a.n_out <= 0 || a.batch <= 0) return hipSuccess;
     const unsigned blocks = (unsigned)((a.n_out + 255) / 256);
-    if (a.channels == 2) LX_LAUNCH("eval_grad", s, (lx_eval_grad_lr<2><<<blocks, 256, 0, s>>>(a)));
-    else LX_LAUNCH("eval_grad", s, (lx_eval_grad_lr<1><<<blocks, 256, 0, s>>>(a)));
+    if (a.channels == 2) LX_LAUNCH("eval_grad_lr", s, (lx_eval_grad_lr<2><<<blocks, 256, 0, s>>>(a)));
+    else LX_LAUNCH("eval_grad_lr", s, (lx_eval_grad_lr<1><<<blocks, 256, 0, s>>>(a)));
     return hipSuccess;
 }
 

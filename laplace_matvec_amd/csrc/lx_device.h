@@ -377,6 +377,29 @@ __device__ __forceinline__ int64_t upper_bound_f(const float* __restrict__ s, in
     return lo;
 }
 
+// Interval search through a lookup table: the range [s_0, s_{n-1}] of the
+// sorted outputs is cut into LUT equal cells and tab[k] = #{s < left edge
+// of cell k} (tab[LUT] = n), so the interval of q lies in [tab[k],
+// tab[k+1]] for q's cell k, a few candidates for smooth data.  The result is
+// checked against its neighbours and a full bisection replaces it when the
+// cell arithmetic rounded q into the wrong cell: the answer is always the
+// exact #{s < q}.
+template <int LUT>
+__device__ __forceinline__ uint32_t lower_bound_lut(const float* so, int no, const uint16_t* tab, float lo_v,
+                                                    float inv_w, float q)
+{
+    const float fk = (q - lo_v) * inv_w;
+    const int k = !(fk >= 0.f) ? 0 : (fk >= (float)(LUT - 1) ? LUT - 1 : (int)fk);
+    int lo = tab[k], hi = tab[k + 1];
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (so[mid] < q) lo = mid + 1;
+        else hi = mid;
+    }
+    if ((lo > 0 && !(so[lo - 1] < q)) || (lo < no && so[lo] < q)) lo = (int)lower_bound_f(so, no, q);
+    return (uint32_t)lo;
+}
+
 __host__ __device__ inline int64_t pad64(int64_t x) { return (x + 63) & ~(int64_t)63; }
 
 // exp(-d / t) for a distance d >= 0 (1 at d == 0, also at t = 0).

@@ -157,6 +157,21 @@ int64_t bucket_partial_floats(const BucketArgs& a, int* groups, int* chunks);
 int64_t bucket_layout_bytes(const BucketArgs& a);
 hipError_t bucket_launch(BucketArgs& a, hipStream_t s);
 
+// Evaluation from per-interval LDS rows (lx_eval_rows, lx_eval_grad_rows):
+// groups of up to kEvalVG vectors; row t of the tables holds, per vector,
+// PL_{t-1} and PR_t of every channel (2C words), rows padded to
+// eval_row_words() so the rows of different outputs spread over the LDS
+// banks; the interval comes from a lookup table of kEvalLut cells.
+constexpr int kEvalVG = 8;
+constexpr int kEvalLut = 2048;
+template <int C>
+constexpr int eval_row_words() { return C == 2 ? 36 : 20; }
+inline size_t eval_rows_lds(int64_t ni, int C)
+{
+    const int64_t pad = (ni + 63) & ~(int64_t)63;
+    return (size_t)(pad + (ni + 1) * (C == 2 ? 36 : 20)) * 4 + (size_t)(kEvalLut + 1) * 2;
+}
+
 struct EvalArgs {
     int channels = 1;
     int64_t n_out = 0;                 // outputs, original order

@@ -267,6 +267,32 @@ def test_backward_general(gpu, n, k, phased, transpose):
     check_grads(got, ref, ["da", "db"] + (["dphi", "dpsi"] if phased else []))
 
 
+@pytest.mark.parametrize("phased", [False, True])
+def test_backward_general_vector_groups(gpu, phased):
+    """19 vectors: the evaluation runs them in groups (7, 7, 5) and sums the
+    anchor and phase gradients over the groups; ragged output count, ties
+    within and between the sides."""
+    n, k, B = 20011, 700, 19
+    say(f"[backward general groups] n={n} k={k} B={B} phased={phased}")
+    rng = np.random.default_rng(1919 + phased)
+    a = tied(n, 20.0, rng)
+    b = tied(k, 20.0, rng)
+    b[:100] = a[rng.integers(0, n, 100)]
+    phi = phases(n, rng) if phased else None
+    psi = phases(k, rng) if phased else None
+    x = rng.standard_normal((B, k)).astype(np.float32)
+    g = rng.standard_normal((B, n)).astype(np.float32)
+    with lx.laplex_plan_create(dev(a), b=dev(b), phi=None if phi is None else dev(phi),
+                               psi=None if psi is None else dev(psi)) as plan:
+        out = lx.laplex_backward(plan, dev(x), dev(g))
+        got = {key: host(v) for key, v in out.items()}
+    ref = oracle.grad_dense(a, g, x, b=b, phi=phi, psi=psi)
+    ref_dx = oracle.apply_sweep(a, g, b=b, phi=phi, psi=psi, transpose=True)
+    for v in range(B):
+        assert oracle.rel_l2(got["dx"][v], ref_dx[v]) < TOL
+    check_grads(got, ref, ["da", "db"] + (["dphi", "dpsi"] if phased else []))
+
+
 @pytest.mark.parametrize("t", [0.5, 0.0])
 def test_backward_temperature(gpu, t):
     n, k = 3000, 800
