@@ -25,6 +25,8 @@
 // Look-back state word per (tile, bin): 0 = not yet published;
 // bit31 clear, value c+1 = this tile's own count c; bit31 set = count of
 // this bin over all tiles up to and including this one (n < 2^31 fits).
+// kLookback rows before tile 0 hold an inclusive 0, so every word a
+// look-back round reads is in the array and the walk ends there.
 // Tiles wait only on tiles with a smaller ticket, which have already
 // started and publish without waiting, so every wait ends.
 #include "lx_device.h"
@@ -55,6 +57,19 @@ __global__ __launch_bounds__(256) void lx_fill_u32(uint32_t* __restrict__ p, uin
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) p[i] = v;
+}
+
+// Zeroes `head` words (histograms, bases, tickets) and four passes of
+// look-back state after them, each pass starting with kLookback rows of
+// inclusive 0 (0x80000000).
+__global__ __launch_bounds__(256) void lx_sort_clear(uint32_t* __restrict__ p, int64_t head, int64_t pass_words)
+{
+    const int64_t total = head + 4 * pass_words;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t j = i - head;
+        p[i] = (j >= 0 && j % pass_words < (int64_t)kLookback * kRadix) ? 0x80000000u : 0u;
+    }
 }
 
 hipError_t fill_u32(uint32_t* p, uint32_t v, int64_t count, hipStream_t s)
@@ -306,7 +321,12 @@ __global__ __launch_bounds__(kSortThreads, VALS ? 4 : 6) void lx_sort_pass(
     }
 
     // Decoupled look-back, kLookback predecessors per round: sum their own
-    // counts until one has published its inclusive count.
+    // counts until one has published its inclusive count.  A round is
+    // branch-free: all its loads are in flight together, then one pass of
+    // selects takes the leading run of own counts and, if the run ends at an
+    // inclusive count, that too; an unpublished word ends the run and the
+    // next round starts there.  (The rows before tile 0 read as an
+    // inclusive 0: a round that reaches them ends.)
     if (tid < kRadix) {
         uint32_t before = 0;
         if (tile > 0) {
@@ -314,28 +334,22 @@ __global__ __launch_bounds__(kSortThreads, VALS ? 4 : 6) void lx_sort_pass(
             while (true) {
                 uint32_t sv[kLookback];
 #pragma unroll
-                for (int k = 0; k < kLookback; ++k)
-                    sv[k] = (t - k >= 0) ? ld_agent(state + (t - k) * kRadix + tid) : 0x80000000u;
-                int k = 0;
-                bool done = false;
+                for (int k = 0; k < kLookback; ++k) sv[k] = ld_agent(state + (t - k) * kRadix + tid);
+                bool live = true, done = false;
+                uint32_t adv = 0;
 #pragma unroll
                 for (int q = 0; q < kLookback; ++q) {
-                    if (!done && k == q) {
-                        const uint32_t v = sv[q];
-                        if (v == 0u) {
-                            // not published yet: resume here next round
-                        } else if (v & 0x80000000u) {
-                            before += v & 0x7FFFFFFFu;
-                            done = true;
-                        } else {
-                            before += v - 1u;
-                            ++k;
-                        }
-                    }
+                    const uint32_t v = sv[q];
+                    const bool inc = live && (v & 0x80000000u) != 0u;
+                    const bool own = live && v != 0u && (v & 0x80000000u) == 0u;
+                    before += own ? v - 1u : (inc ? (v & 0x7FFFFFFFu) : 0u);
+                    adv += own ? 1u : 0u;
+                    done = done || inc;
+                    live = own;
                 }
                 if (done) break;
-                t -= k;
-                if (k == 0) __builtin_amdgcn_s_sleep(1);
+                t -= adv;
+                if (adv == 0) __builtin_amdgcn_s_sleep(1);
             }
             st_agent(state + (int64_t)tile * kRadix + tid, 0x80000000u | (before + count));
         }
@@ -402,7 +416,8 @@ __global__ __launch_bounds__(kSortThreads, VALS ? 4 : 6) void lx_sort_pass(
 //   keysA, keysB               : uint32[n] each
 //   hist, base                 : uint32[4][256] each
 //   tickets                    : uint32[4] (padded to 64)
-//   state                      : uint32[4][tiles][256]
+//   state                      : uint32[4][kLookback + tiles][256] (kLookback rows of
+//                                inclusive 0 before each pass's tile 0)
 //   pairB (with value rows)    : uint2[n]; pairA overlays keysA + keysB
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -412,7 +427,7 @@ size_t sort_scratch_bytes(int64_t n, bool with_vals)
     size_t b = 2 * align256((size_t)n * 4);
     b += 2 * align256(4 * kRadix * 4);
     b += align256(64 * 4);
-    b += align256((size_t)4 * tiles * kRadix * 4);
+    b += align256((size_t)4 * (tiles + kLookback) * kRadix * 4);
     if (with_vals) b += align256((size_t)n * 8);
     return b;
 }
@@ -450,16 +465,22 @@ hipError_t sort_launch(const float* a, int64_t n, float* sorted, const SortRecor
     uint32_t* hist = (uint32_t*)p; p += align256(4 * kRadix * 4);
     uint32_t* base = (uint32_t*)p; p += align256(4 * kRadix * 4);
     uint32_t* tickets = (uint32_t*)p; p += align256(64 * 4);
-    uint32_t* state = (uint32_t*)p; p += align256((size_t)4 * tiles * kRadix * 4);
+    uint32_t* state = (uint32_t*)p; p += align256((size_t)4 * (tiles + kLookback) * kRadix * 4);
     // key-value pairs (with value rows): keysA and keysB together hold one
     // array of n pairs, the region after the look-back state the other
     uint2* pairA = reinterpret_cast<uint2*>(keysA);
     uint2* pairB = reinterpret_cast<uint2*>(p);
 
-    // hist, base and tickets are contiguous: clear them and the state together
-    const int64_t clear_words = (int64_t)((char*)state - (char*)hist) / 4 + 4 * tiles * kRadix;
-    hipError_t e = fill_u32(hist, 0u, clear_words, s);
-    if (e != hipSuccess) return e;
+    // hist, base and tickets are contiguous with the state: one launch clears
+    // them all and writes the inclusive-0 rows before each pass's tile 0
+    const int64_t head_words = (int64_t)((char*)state - (char*)hist) / 4;
+    const int64_t pass_words = (tiles + kLookback) * kRadix;
+    {
+        const int64_t words = head_words + 4 * pass_words;
+        int64_t blocks = (words + 255) / 256;
+        if (blocks > 4096) blocks = 4096;
+        LX_LAUNCH("util_fill", s, (lx_sort_clear<<<(int)blocks, 256, 0, s>>>(hist, head_words, pass_words)));
+    }
 
     {
         int64_t blocks = (n + kHistThreads * 64 - 1) / (kHistThreads * 64);
@@ -483,7 +504,6 @@ hipError_t sort_launch(const float* a, int64_t n, float* sorted, const SortRecor
         }
     }
     const int grid = (int)tiles;
-    const int64_t st = tiles * kRadix;
     const uint32_t* kin[4] = {nullptr, keysA, keysB, keysA};
     uint32_t* kout[4] = {keysA, keysB, keysA, nullptr};
     const uint2* pin[4] = {nullptr, pairA, pairB, pairA};
@@ -494,7 +514,7 @@ hipError_t sort_launch(const float* a, int64_t n, float* sorted, const SortRecor
               (lx_sort_pass<F, L, V><<<grid, kSortThreads, 0, s>>>(                                          \
                   k == 0 ? a : nullptr, kin[k], kout[k], hv ? pin[k] : nullptr, hv ? pout[k] : nullptr,       \
                   k == 3 ? sorted : nullptr, R.rec[k], R.base[k],                                            \
-                  R.start[k], base + k * kRadix, state + k * st, tickets + k, 8 * k, n, vp[k])))
+                  R.start[k], base + k * kRadix, state + k * pass_words + kLookback * kRadix, tickets + k, 8 * k, n, vp[k])))
         if (hv) {
             if (k == 0) LX_PASS(true, false, true);
             else if (k == 3) LX_PASS(false, true, true);
