@@ -218,6 +218,32 @@ def test_general_both_directions(gpu, n, k, phased, algo):
     assert max_rel(z, oracle.apply_dense(a, w, b=b, transpose=True, **kw)) < TOL
 
 
+@pytest.mark.parametrize("phased", [False, True])
+@pytest.mark.parametrize("algo", [lx.ALGO_BUCKET, lx.ALGO_EVALUATE])
+def test_general_partial_vector_groups(gpu, phased, algo):
+    """11 vectors: the evaluation and bucketing kernels run them as groups
+    of 6 and 5 (and 8 + 3), so the last group is partial; ragged sizes and
+    outputs outside the input range on both sides."""
+    n, k, B = 30011, 777, 11
+    say(f"[general groups] n={n} k={k} B={B} phased={phased} algo={algo}")
+    rng = np.random.default_rng(4242 + phased)
+    a = (rng.standard_normal(n) * 20).astype(np.float32)
+    b = rng.uniform(-45, 45, k).astype(np.float32)
+    b[:40] = a[rng.integers(0, n, 40)]
+    kw = {}
+    if phased:
+        kw = dict(phi=rng.uniform(0, 6.3, n).astype(np.float32), psi=rng.uniform(0, 6.3, k).astype(np.float32))
+    x = rng.standard_normal((B, k)).astype(np.float32)
+    w = rng.standard_normal((B, n)).astype(np.float32)
+    dkw = {key: dev(v) for key, v in kw.items()}
+    with lx.laplex_plan_create(dev(a), b=dev(b), **dkw) as plan:
+        lx.laplex_plan_set_option(plan, lx.OPT_GENERAL_ALGO, algo)
+        y = host(lx.laplex_apply(plan, dev(x)))
+        z = host(lx.laplex_apply(plan, dev(w), transpose=True))
+    assert max_rel(y, oracle.apply_dense(a, x, b=b, **kw)) < TOL
+    assert max_rel(z, oracle.apply_dense(a, w, b=b, transpose=True, **kw)) < TOL
+
+
 @pytest.mark.parametrize("algo", [lx.ALGO_BUCKET, lx.ALGO_EVALUATE])
 def test_general_zero_temperature_permutation_bitwise(gpu, algo):
     n = 9000
