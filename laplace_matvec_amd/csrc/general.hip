@@ -12,19 +12,22 @@
 // the signed product leaves them out.
 //
 // Kernels here:
-//   lx_bucket_sorted + lx_bucket_reduce : u, v when the sorted output side
-//                      is small (up to 1024 anchors): per workgroup, stable
-//                      counting sort of input sub-chunks by interval and
-//                      register accumulation by an owner thread per anchor;
+//   lx_bucket_layout + lx_bucket_sorted + lx_bucket_reduce : u, v when the
+//                      sorted output side is small (up to 1024 anchors):
+//                      once per call, a stable counting sort of input
+//                      sub-chunks by interval with the factors in slot
+//                      order; then per group of vectors, register
+//                      accumulation by an owner thread per anchor; the
 //                      per-workgroup partials summed in a fixed order;
 //   lx_bucket_global : u, v with device-wide float atomics, any size;
-//   lx_eval          : the transposed reading of the same identity: with
-//                      the scan run over the sorted INPUT side (PL = prefix,
-//                      PR = suffix, both inclusive), an output at anchor o
-//                      with t = #{s_j < o} is
+//   lx_eval_rows / lx_eval : the transposed reading of the same identity:
+//                      with the scan run over the sorted INPUT side (PL =
+//                      prefix, PR = suffix, both inclusive), an output at
+//                      anchor o with t = #{s_j < o} is
 //                        exp(-(o - s_{t-1})) PL_{t-1} + exp(-(s_t - o)) PR_t,
 //                      evaluated for every output in its original order (no
-//                      sort or scatter of the output side).
+//                      sort or scatter of the output side); lx_eval_rows
+//                      when the tables of 8 vectors fit in LDS.
 // The cos/sin split of a phased operator (cos(p - q) = cos p cos q +
 // sin p sin q) gives two channels: inputs scaled by cos q_j and sin q_j,
 // outputs combined with cos p_i and sin p_i.
