@@ -107,21 +107,26 @@ __device__ __forceinline__ Aff<T> compose(Aff<T> p, Aff<T> q)
 // (row_bcast:15) gives the rows in ROW_MASK lane 15 of the row below them,
 // 0x143 (row_bcast:31) lane 31; 0x138 (wave_shr:1) reads lane - 1 and 0x130
 // (wave_shl:1) lane + 1 across the whole wave.  Lanes without a source, or
-// outside ROW_MASK, get 0; callers ignore them.
+// outside ROW_MASK, get `old`.
 template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ double dpp_move(double x)
+__device__ __forceinline__ double dpp_move(double x, double old)
 {
     const uint64_t b = (uint64_t)__double_as_longlong(x);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, 0xF, false);
-    const uint32_t hi =
-        (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, 0xF, false);
+    const uint64_t o = (uint64_t)__double_as_longlong(old);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)o, (int)(uint32_t)b, CTRL, ROW_MASK,
+                                                              0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(o >> 32), (int)(uint32_t)(b >> 32),
+                                                              CTRL, ROW_MASK, 0xF, false);
     return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// A composite moved by DPP; lanes without a source get the identity map, so
+// composing with the result leaves them unchanged (1*m = m, 0*m + v = v
+// exactly) and no lane needs a select.
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ Aff<double> dpp_move(Aff<double> x)
 {
-    return Aff<double>{dpp_move<CTRL, ROW_MASK>(x.m), dpp_move<CTRL, ROW_MASK>(x.v)};
+    return Aff<double>{dpp_move<CTRL, ROW_MASK>(x.m, 1.0), dpp_move<CTRL, ROW_MASK>(x.v, 0.0)};
 }
 
 // The value of lane L (a constant), in scalar registers.
@@ -140,27 +145,21 @@ __device__ __forceinline__ Aff<double> read_lane(Aff<double> x, int l)
 // Inclusive scan over the lanes of a wave in ascending lane order.  All
 // lanes of the wave must be active.  Float64 composites: distances 1, 2, 4,
 // 8 inside each row of 16 lanes by DPP, then each row takes the composite
-// of all rows below it (row broadcasts of lanes 15 and 31).  Other types:
-// shuffles at distances 1 .. 32.
+// of all rows below it (row broadcasts of lanes 15 and 31); lanes with
+// nothing to take compose with the identity.  Other types: shuffles at
+// distances 1 .. 32.
 template <class T>
 __device__ __forceinline__ Aff<T> wave_scan_up(Aff<T> x)
 {
-    const int lane = lane_id();
     if constexpr (sizeof(T) == 8) {
-        Aff<double> y;
-        y = dpp_move<0x111>(x);
-        if ((lane & 15) >= 1) x = compose(y, x);
-        y = dpp_move<0x112>(x);
-        if ((lane & 15) >= 2) x = compose(y, x);
-        y = dpp_move<0x114>(x);
-        if ((lane & 15) >= 4) x = compose(y, x);
-        y = dpp_move<0x118>(x);
-        if ((lane & 15) >= 8) x = compose(y, x);
-        y = dpp_move<0x142, 0xA>(x);  // rows 1, 3 <- lane 15 of rows 0, 2
-        if (lane & 16) x = compose(y, x);
-        y = dpp_move<0x143, 0xC>(x);  // rows 2, 3 <- lane 31 (rows 0 and 1)
-        if (lane & 32) x = compose(y, x);
+        x = compose(dpp_move<0x111>(x), x);
+        x = compose(dpp_move<0x112>(x), x);
+        x = compose(dpp_move<0x114>(x), x);
+        x = compose(dpp_move<0x118>(x), x);
+        x = compose(dpp_move<0x142, 0xA>(x), x);  // rows 1, 3 <- lane 15 of rows 0, 2
+        x = compose(dpp_move<0x143, 0xC>(x), x);  // rows 2, 3 <- lane 31 (rows 0 and 1)
     } else {
+        const int lane = lane_id();
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
             const T m = __shfl_up(x.m, d);
@@ -180,20 +179,16 @@ __device__ __forceinline__ Aff<T> wave_scan_down(Aff<T> x)
 {
     const int lane = lane_id();
     if constexpr (sizeof(T) == 8) {
-        Aff<double> y;
-        y = dpp_move<0x101>(x);
-        if ((lane & 15) + 1 < 16) x = compose(y, x);
-        y = dpp_move<0x102>(x);
-        if ((lane & 15) + 2 < 16) x = compose(y, x);
-        y = dpp_move<0x104>(x);
-        if ((lane & 15) + 4 < 16) x = compose(y, x);
-        y = dpp_move<0x108>(x);
-        if ((lane & 15) + 8 < 16) x = compose(y, x);
+        x = compose(dpp_move<0x101>(x), x);
+        x = compose(dpp_move<0x102>(x), x);
+        x = compose(dpp_move<0x104>(x), x);
+        x = compose(dpp_move<0x108>(x), x);
         const Aff<double> r1 = read_lane(x, 16), r2 = read_lane(x, 32), r3 = read_lane(x, 48);
         const Aff<double> r32 = compose(r3, r2);
         const int row = lane >> 4;
-        const Aff<double> above = row == 2 ? r3 : (row == 1 ? r32 : compose(r32, r1));
-        if (row < 3) x = compose(above, x);
+        const Aff<double> above =
+            row == 3 ? aff_identity<double>() : (row == 2 ? r3 : (row == 1 ? r32 : compose(r32, r1)));
+        x = compose(above, x);
     } else {
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
@@ -210,20 +205,24 @@ __device__ __forceinline__ Aff<T> wave_scan_down(Aff<T> x)
 template <class T>
 __device__ __forceinline__ Aff<T> wave_shift_up(Aff<T> inc)
 {
-    Aff<T> ex;
-    if constexpr (sizeof(T) == 8) ex = dpp_move<0x138>(inc);
-    else ex = Aff<T>{__shfl_up(inc.m, 1), __shfl_up(inc.v, 1)};
-    if (lane_id() == 0) ex = aff_identity<T>();
-    return ex;
+    if constexpr (sizeof(T) == 8) {
+        return dpp_move<0x138>(inc);
+    } else {
+        Aff<T> ex{__shfl_up(inc.m, 1), __shfl_up(inc.v, 1)};
+        if (lane_id() == 0) ex = aff_identity<T>();
+        return ex;
+    }
 }
 template <class T>
 __device__ __forceinline__ Aff<T> wave_shift_down(Aff<T> inc)
 {
-    Aff<T> ex;
-    if constexpr (sizeof(T) == 8) ex = dpp_move<0x130>(inc);
-    else ex = Aff<T>{__shfl_down(inc.m, 1), __shfl_down(inc.v, 1)};
-    if (lane_id() == kWave - 1) ex = aff_identity<T>();
-    return ex;
+    if constexpr (sizeof(T) == 8) {
+        return dpp_move<0x130>(inc);
+    } else {
+        Aff<T> ex{__shfl_down(inc.m, 1), __shfl_down(inc.v, 1)};
+        if (lane_id() == kWave - 1) ex = aff_identity<T>();
+        return ex;
+    }
 }
 
 // Block-wide exclusive scans of one Aff per thread, ascending (up) or
