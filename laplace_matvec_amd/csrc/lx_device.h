@@ -122,11 +122,26 @@ __device__ __forceinline__ double dpp_move(double x, double old)
 
 // A composite moved by DPP; lanes without a source get the identity map, so
 // composing with the result leaves them unchanged (1*m = m, 0*m + v = v
-// exactly) and no lane needs a select.
+// exactly) and no lane needs a select.  With every row enabled, the three
+// zero words of the identity (both words of v, the low word of m = 1.0)
+// come from the hardware's zero for a lane without a source (bound_ctrl),
+// so only the high word of m needs an initialised old value.
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ Aff<double> dpp_move(Aff<double> x)
 {
-    return Aff<double>{dpp_move<CTRL, ROW_MASK>(x.m, 1.0), dpp_move<CTRL, ROW_MASK>(x.v, 0.0)};
+    if constexpr (ROW_MASK == 0xF) {
+        const uint64_t bm = (uint64_t)__double_as_longlong(x.m);
+        const uint64_t bv = (uint64_t)__double_as_longlong(x.v);
+        const uint32_t mlo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)bm, CTRL, 0xF, 0xF, true);
+        const uint32_t mhi =
+            (uint32_t)__builtin_amdgcn_update_dpp(0x3FF00000, (int)(uint32_t)(bm >> 32), CTRL, 0xF, 0xF, false);
+        const uint32_t vlo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)bv, CTRL, 0xF, 0xF, true);
+        const uint32_t vhi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(bv >> 32), CTRL, 0xF, 0xF, true);
+        return Aff<double>{__longlong_as_double((long long)(((uint64_t)mhi << 32) | mlo)),
+                           __longlong_as_double((long long)(((uint64_t)vhi << 32) | vlo))};
+    } else {
+        return Aff<double>{dpp_move<CTRL, ROW_MASK>(x.m, 1.0), dpp_move<CTRL, ROW_MASK>(x.v, 0.0)};
+    }
 }
 
 // The value of lane L (a constant), in scalar registers.
