@@ -325,18 +325,33 @@ __device__ __forceinline__ Aff<T> block_exscan_down_lean(Aff<T> x, Aff<T>* sh)
     return compose(pre, ex);
 }
 
+// Inclusive sum of uint32 over the lanes of a wave in ascending lane order,
+// by DPP (distances 1, 2, 4, 8 inside rows of 16, then the row broadcasts
+// of lanes 15 and 31).  The identity is 0, which is what a lane without a
+// DPP source reads (bound_ctrl), and what the rows left out of a broadcast
+// keep.  All lanes of the wave must be active.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, ROW_MASK == 0xF);
+}
+__device__ __forceinline__ uint32_t wave_incsum_u32(uint32_t x)
+{
+    x += dpp_u32<0x111>(x);
+    x += dpp_u32<0x112>(x);
+    x += dpp_u32<0x114>(x);
+    x += dpp_u32<0x118>(x);
+    x += dpp_u32<0x142, 0xA>(x);
+    x += dpp_u32<0x143, 0xC>(x);
+    return x;
+}
 // Block-wide exclusive sum of uint32 over NW waves.
 template <int NW>
 __device__ __forceinline__ uint32_t block_exsum_u32(uint32_t x, uint32_t* sh, uint32_t& total)
 {
     const int lane = lane_id();
     const int w = (int)threadIdx.x / kWave;
-    uint32_t inc = x;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const uint32_t y = __shfl_up(inc, d);
-        if (lane >= d) inc += y;
-    }
+    const uint32_t inc = wave_incsum_u32(x);
     if (lane == kWave - 1) sh[w] = inc;
     __syncthreads();
     uint32_t pre = 0, tot = 0;
