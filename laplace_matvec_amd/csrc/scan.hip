@@ -83,37 +83,61 @@ __device__ __forceinline__ void load_values(const ScanArgs& A, int64_t vec, int6
     }
 }
 
-template <int C, int MODE, bool RANDOM>
+// Vectors per scan workgroup: the decays of a tile are computed once and
+// serve every vector of the group.
+constexpr int kScanVB = 8;
+
+template <int C, int MODE, bool RANDOM, int VB>
 __global__ __launch_bounds__(kScanThreads) void lx_scan_reduce(ScanArgs A)
 {
-    __shared__ Aff<double> sh[kScanWaves];
-    const int64_t vec = blockIdx.x / A.tiles;
-    const int64_t tile = blockIdx.x - vec * A.tiles;
+    // wave totals of every (vector, channel) row, both directions; one
+    // barrier for the whole group, then one thread per row and direction
+    // folds the waves
+    __shared__ Aff<double> sh[VB * C][kScanWaves][2];
+    const int64_t vg = blockIdx.x / A.tiles;
+    const int64_t tile = blockIdx.x - vg * A.tiles;
+    const int64_t v0 = vg * VB;
+    const int nv = VB == 1 ? 1 : (int)(A.batch - v0 < VB ? A.batch - v0 : VB);
     const int64_t r0 = tile * kScanTile + (int64_t)threadIdx.x * kScanItems;
+    const int lane = lane_id();
+    const int w = (int)threadIdx.x / kWave;
 
     double e[kScanItems + 1];
     load_decays<kScanItems>(A.s, r0, A.n, A.inv_t, e);
-    float fv[C][kScanItems], bv[C][kScanItems];
-    load_values<C, MODE, RANDOM, true>(A, vec, r0, fv, bv);
-
+#pragma unroll 1
+    for (int vi = 0; vi < nv; ++vi) {
+        const int64_t vec = v0 + vi;
+        float fv[C][kScanItems], bv[C][kScanItems];
+        load_values<C, MODE, RANDOM, true>(A, vec, r0, fv, bv);
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-        Aff<double> f = aff_identity<double>();
+        for (int c = 0; c < C; ++c) {
+            Aff<double> f = aff_identity<double>();
 #pragma unroll
-        for (int i = 0; i < kScanItems; ++i) f = compose(f, Aff<double>{e[i], (double)fv[c][i]});
-        Aff<double> b = aff_identity<double>();
+            for (int i = 0; i < kScanItems; ++i) f = compose(f, Aff<double>{e[i], (double)fv[c][i]});
+            Aff<double> b = aff_identity<double>();
 #pragma unroll
-        for (int i = kScanItems - 1; i >= 0; --i) b = compose(b, Aff<double>{e[i + 1], (double)bv[c][i]});
-        Aff<double> ft, bt;
-        (void)block_exscan_up<double, kScanWaves>(f, sh, ft);
-        (void)block_exscan_down<double, kScanWaves>(b, sh, bt);
-        if (threadIdx.x == 0) {
-            double* ag = A.agg + ((((int64_t)c * A.batch + vec) * A.tiles) + tile) * 4;
-            ag[0] = ft.m;
-            ag[1] = ft.v;
-            ag[2] = bt.m;
-            ag[3] = bt.v;
+            for (int i = kScanItems - 1; i >= 0; --i) b = compose(b, Aff<double>{e[i + 1], (double)bv[c][i]});
+            const Aff<double> fi = wave_scan_up(f);
+            const Aff<double> bi = wave_scan_down(b);
+            if (lane == kWave - 1) sh[vi * C + c][w][0] = fi;
+            if (lane == 0) sh[vi * C + c][w][1] = bi;
         }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < nv * C * 2) {
+        const int row = (int)threadIdx.x / 2, dir = (int)threadIdx.x & 1;
+        const int vi = row / C, c = row - vi * C;
+        Aff<double> acc = aff_identity<double>();
+        if (dir == 0) {
+#pragma unroll
+            for (int i = 0; i < kScanWaves; ++i) acc = compose(acc, sh[row][i][0]);
+        } else {
+#pragma unroll
+            for (int i = kScanWaves - 1; i >= 0; --i) acc = compose(acc, sh[row][i][1]);
+        }
+        double* ag = A.agg + ((((int64_t)c * A.batch + v0 + vi) * A.tiles) + tile) * 4;
+        ag[2 * dir] = acc.m;
+        ag[2 * dir + 1] = acc.v;
     }
 }
 
@@ -190,76 +214,111 @@ __global__ __launch_bounds__(kCarryThreads) void lx_scan_carry_tiles(const doubl
     }
 }
 
-template <int C, int MODE, bool RANDOM>
+// Exclusive block scans of one forward and one backward row with one
+// barrier: wave scans, wave totals in LDS, then each wave folds the waves
+// before (after) it.  `sh` holds two buffers used in turns (`parity`), so
+// the next call can write without a second barrier.
+__device__ __forceinline__ void block_exscan2(Aff<double> f, Aff<double> b, Aff<double>* sh, int parity,
+                                              Aff<double>& xf, Aff<double>& xb)
+{
+    const int lane = lane_id();
+    const int w = (int)threadIdx.x / kWave;
+    Aff<double>* buf = sh + parity * (kScanWaves * 2);
+    const Aff<double> fi = wave_scan_up(f);
+    const Aff<double> bi = wave_scan_down(b);
+    const Aff<double> ef = wave_shift_up(fi);
+    const Aff<double> eb = wave_shift_down(bi);
+    if (lane == kWave - 1) buf[w * 2] = fi;
+    if (lane == 0) buf[w * 2 + 1] = bi;
+    __syncthreads();
+    Aff<double> pf = aff_identity<double>(), pb = aff_identity<double>();
+#pragma unroll
+    for (int i = 0; i < kScanWaves; ++i)
+        if (i < w) pf = compose(pf, buf[i * 2]);
+#pragma unroll
+    for (int i = kScanWaves - 1; i >= 0; --i)
+        if (i > w) pb = compose(pb, buf[i * 2 + 1]);
+    xf = compose(pf, ef);
+    xb = compose(pb, eb);
+}
+
+template <int C, int MODE, bool RANDOM, int VB>
 __global__ __launch_bounds__(kScanThreads) void lx_scan_apply(ScanArgs A)
 {
-    __shared__ Aff<double> sh[kScanWaves];
-    const int64_t vec = blockIdx.x / A.tiles;
-    const int64_t tile = blockIdx.x - vec * A.tiles;
+    __shared__ Aff<double> sh[2 * kScanWaves * 2];
+    int parity = 0;
+    const int64_t vg = blockIdx.x / A.tiles;
+    const int64_t tile = blockIdx.x - vg * A.tiles;
+    const int64_t v0 = vg * VB;
+    const int nv = VB == 1 ? 1 : (int)(A.batch - v0 < VB ? A.batch - v0 : VB);
     const int64_t n = A.n;
     const int64_t r0 = tile * kScanTile + (int64_t)threadIdx.x * kScanItems;
 
     double e[kScanItems + 1];
     load_decays<kScanItems>(A.s, r0, n, A.inv_t, e);
-    float fv[C][kScanItems], bv[C][kScanItems];
-    // the reduce step already stored x by rank: read it back
-    load_values<C, MODE, false, false>(A, vec, r0, fv, bv);
+#pragma unroll 1
+    for (int vi = 0; vi < nv; ++vi) {
+        const int64_t vec = v0 + vi;
+        float fv[C][kScanItems], bv[C][kScanItems];
+        // the reduce step already stored x by rank: read it back
+        load_values<C, MODE, false, false>(A, vec, r0, fv, bv);
 
-    float out[kScanItems];
+        float out[kScanItems];
 #pragma unroll
-    for (int i = 0; i < kScanItems; ++i) out[i] = 0.f;
+        for (int i = 0; i < kScanItems; ++i) out[i] = 0.f;
 
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-        Aff<double> f = aff_identity<double>();
+        for (int c = 0; c < C; ++c) {
+            Aff<double> f = aff_identity<double>();
 #pragma unroll
-        for (int i = 0; i < kScanItems; ++i) f = compose(f, Aff<double>{e[i], (double)fv[c][i]});
-        Aff<double> b = aff_identity<double>();
+            for (int i = 0; i < kScanItems; ++i) f = compose(f, Aff<double>{e[i], (double)fv[c][i]});
+            Aff<double> b = aff_identity<double>();
 #pragma unroll
-        for (int i = kScanItems - 1; i >= 0; --i) b = compose(b, Aff<double>{e[i + 1], (double)bv[c][i]});
-        Aff<double> tot;
-        const Aff<double> fx = block_exscan_up<double, kScanWaves>(f, sh, tot);
-        const Aff<double> bx = block_exscan_down<double, kScanWaves>(b, sh, tot);
-        const double* cr = A.carry + ((((int64_t)c * A.batch + vec) * A.tiles) + tile) * 2;
-        double L = fx.m * cr[0] + fx.v;
-        double U = bx.m * cr[1] + bx.v;
-        double Lr[kScanItems];
+            for (int i = kScanItems - 1; i >= 0; --i) b = compose(b, Aff<double>{e[i + 1], (double)bv[c][i]});
+            Aff<double> fx, bx;
+            block_exscan2(f, b, sh, parity, fx, bx);
+            parity ^= 1;
+            const double* cr = A.carry + ((((int64_t)c * A.batch + vec) * A.tiles) + tile) * 2;
+            double L = fx.m * cr[0] + fx.v;
+            double U = bx.m * cr[1] + bx.v;
+            double Lr[kScanItems];
 #pragma unroll
-        for (int i = 0; i < kScanItems; ++i) {
-            L = e[i] * L + (double)fv[c][i];
-            Lr[i] = L;
-        }
-        if (MODE == kScanPLPR || MODE == kScanUVLR) {
-            float pl[kScanItems], pr[kScanItems];
-#pragma unroll
-            for (int i = kScanItems - 1; i >= 0; --i) {
-                U = e[i + 1] * U + (double)bv[c][i];
-                pl[i] = (float)Lr[i];
-                pr[i] = (float)U;
+            for (int i = 0; i < kScanItems; ++i) {
+                L = e[i] * L + (double)fv[c][i];
+                Lr[i] = L;
             }
-            store_run<kScanItems>(A.pl + row_off(A, c, vec), r0, n, pl);
-            store_run<kScanItems>(A.pr + row_off(A, c, vec), r0, n, pr);
-        } else {
-            float g[kScanItems];
-            if (C == 2) load_run<kScanItems>(c == 0 ? A.out_c : A.out_s, r0, n, g);
+            if (MODE == kScanPLPR || MODE == kScanUVLR) {
+                float pl[kScanItems], pr[kScanItems];
 #pragma unroll
-            for (int i = kScanItems - 1; i >= 0; --i) {
-                U = e[i + 1] * U + (double)bv[c][i];
-                const double y = (MODE == kScanSym) ? Lr[i] + U - (double)fv[c][i] : Lr[i] + U;
-                out[i] = (C == 2) ? fmaf(g[i], (float)y, out[i]) : (float)y;
+                for (int i = kScanItems - 1; i >= 0; --i) {
+                    U = e[i + 1] * U + (double)bv[c][i];
+                    pl[i] = (float)Lr[i];
+                    pr[i] = (float)U;
+                }
+                store_run<kScanItems>(A.pl + row_off(A, c, vec), r0, n, pl);
+                store_run<kScanItems>(A.pr + row_off(A, c, vec), r0, n, pr);
+            } else {
+                float g[kScanItems];
+                if (C == 2) load_run<kScanItems>(c == 0 ? A.out_c : A.out_s, r0, n, g);
+#pragma unroll
+                for (int i = kScanItems - 1; i >= 0; --i) {
+                    U = e[i + 1] * U + (double)bv[c][i];
+                    const double y = (MODE == kScanSym) ? Lr[i] + U - (double)fv[c][i] : Lr[i] + U;
+                    out[i] = (C == 2) ? fmaf(g[i], (float)y, out[i]) : (float)y;
+                }
             }
         }
-    }
-    if (MODE != kScanPLPR && MODE != kScanUVLR) {
-        if (RANDOM) {
-            uint32_t idx[kScanItems];
-            load_run<kScanItems>(A.perm, r0, n, idx);
-            float* yv = A.y + vec * n;
+        if (MODE != kScanPLPR && MODE != kScanUVLR) {
+            if (RANDOM) {
+                uint32_t idx[kScanItems];
+                load_run<kScanItems>(A.perm, r0, n, idx);
+                float* yv = A.y + vec * n;
 #pragma unroll
-            for (int i = 0; i < kScanItems; ++i)
-                if (r0 + i < n) yv[idx[i]] = out[i];
-        } else {
-            store_run<kScanItems>(A.ys + vec * A.ld, r0, n, out);
+                for (int i = 0; i < kScanItems; ++i)
+                    if (r0 + i < n) yv[idx[i]] = out[i];
+            } else {
+                store_run<kScanItems>(A.ys + vec * A.ld, r0, n, out);
+            }
         }
     }
 }
@@ -274,16 +333,16 @@ hipError_t scan_carry_launch(const double* agg, double* gagg, double* carry, int
     return hipSuccess;
 }
 
-template <int C, int MODE, bool RANDOM>
+template <int C, int MODE, bool RANDOM, int VB>
 static hipError_t scan_launch_t(const ScanArgs& a, hipStream_t s)
 {
-    const int64_t blocks = a.tiles * a.batch;
+    const int64_t blocks = a.tiles * ((a.batch + VB - 1) / VB);
     LX_LAUNCH(MODE == kScanUV || MODE == kScanUVLR ? "scan_reduce_uv" : (RANDOM ? "scan_reduce_gather" : "scan_reduce"), s,
-              (lx_scan_reduce<C, MODE, RANDOM><<<(unsigned)blocks, kScanThreads, 0, s>>>(a)));
+              (lx_scan_reduce<C, MODE, RANDOM, VB><<<(unsigned)blocks, kScanThreads, 0, s>>>(a)));
     const hipError_t e = scan_carry_launch(a.agg, a.gagg, a.carry, a.tiles, (int64_t)a.channels * a.batch, s);
     if (e != hipSuccess) return e;
     LX_LAUNCH(MODE == kScanPLPR || MODE == kScanUVLR ? "scan_apply_tables" : (RANDOM ? "scan_apply_scatter" : "scan_apply"), s,
-              (lx_scan_apply<C, MODE, RANDOM><<<(unsigned)blocks, kScanThreads, 0, s>>>(a)));
+              (lx_scan_apply<C, MODE, RANDOM, VB><<<(unsigned)blocks, kScanThreads, 0, s>>>(a)));
     return hipSuccess;
 }
 
@@ -292,7 +351,11 @@ hipError_t scan_launch(const ScanArgs& a, hipStream_t s)
     if (a.n <= 0 || a.batch <= 0) return hipSuccess;
     if (a.tiles * a.batch > 0x7FFFFFFFll) return hipErrorInvalidValue;
     const bool two = a.channels == 2;
-#define LX_SCAN(M, R) (two ? scan_launch_t<2, M, R>(a, s) : scan_launch_t<1, M, R>(a, s))
+    // one vector: no vector loop, the leaner kernel keeps more waves resident
+    const bool one = a.batch == 1;
+#define LX_SCAN(M, R)                                                                            \
+    (one ? (two ? scan_launch_t<2, M, R, 1>(a, s) : scan_launch_t<1, M, R, 1>(a, s))              \
+         : (two ? scan_launch_t<2, M, R, kScanVB>(a, s) : scan_launch_t<1, M, R, kScanVB>(a, s)))
     switch (a.mode) {
         case kScanSym: return a.random ? LX_SCAN(kScanSym, true) : LX_SCAN(kScanSym, false);
         case kScanUV: return a.random ? LX_SCAN(kScanUV, true) : LX_SCAN(kScanUV, false);
