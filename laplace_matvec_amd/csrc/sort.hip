@@ -678,17 +678,129 @@ __global__ __launch_bounds__(kSortThreads, 6) void lx_replay(const T* __restrict
     }
 }
 
-// Forward replay of two neighbouring tiles per workgroup.  For each bin the
-// runs of tiles t and t+1 are adjacent in the output (t+1's run starts where
-// t's ends), so dealing the two tiles' slots out together -- bin by bin,
-// t's slots first -- turns each pair of runs into one run twice as long and
-// removes the partly written cache line at their seam.  (Forward replays
-// write their runs scattered; with 4-byte elements most of a run's lines
-// are partly written.)  In merged order, slot m of bin b goes to global
-// position mbase_b + m with mbase_b = base_b(t) - start_b(t+1).
+// Replay of two neighbouring tiles per workgroup.  For each bin the runs of
+// tiles t and t+1 are adjacent in the sorted-side array (t+1's run starts
+// where t's ends), so dealing the two tiles' slots out together -- bin by
+// bin, t's slots first -- turns each pair of runs into one run twice as
+// long: half as many partly covered cache lines at the seams, and about
+// half as many distinct lines per wave access.  In merged order, slot m of
+// bin b sits at global position mbase_b + m with
+// mbase_b = base_b(t) - start_b(t+1).
 constexpr int kPairThreads = 2 * kSortThreads;          // 1024: one half per tile
 constexpr int kPairItems = 2 * kSortTile / kPairThreads;  // 16 merged slots per thread
 
+// Shared memory of a pair replay: first the maps (per-tile bin of each slot;
+// merged source and bin of each merged slot), then the two tiles' data, in
+// the same 64 KB.
+struct PairShared {
+    __align__(16) uint32_t words[2 * kSortTile];
+    uint32_t start[2][kRadix + 1];
+    uint32_t mbase[kRadix];
+    uint32_t red[2 * kSortWaves];
+};
+
+// Builds the merged order of tiles t0 and t0 + 1 (ntile of them exist) and
+// returns, for merged slot m = q * kPairThreads + tid, its tile-pair
+// position src = tile << 13 | position (two per word in srcp) and its global
+// position dst (0xFFFFFFFF past the pair's slots).  A slot past the pair
+// (one tile only) gets src = m, a position of the absent second tile.  Slots
+// whose dst is n or more hold the padding of the last tile: every pass sorts
+// the padding (maximal keys, after every real element of the last tile)
+// behind all real elements, so their tile positions lie past the tile's
+// valid range as well.  Ends with a barrier after which `words` is free for
+// data.
+__device__ __forceinline__ void pair_maps(PairShared& S, const uint16_t* __restrict__ rec,
+                                          const uint32_t* __restrict__ tab_base,
+                                          const uint16_t* __restrict__ tab_start, int64_t t0, int ntile,
+                                          uint32_t (&srcp)[kPairItems / 2], uint32_t (&dst)[kPairItems])
+{
+    uint8_t* sbin = reinterpret_cast<uint8_t*>(S.words);               // [2][kSortTile]
+    uint16_t* msrc = reinterpret_cast<uint16_t*>(sbin + 2 * kSortTile);  // [2 kSortTile]
+    uint8_t* mbin = reinterpret_cast<uint8_t*>(msrc + 2 * kSortTile);    // [2 kSortTile]
+    static_assert(2 * kSortTile + 4 * kSortTile + 2 * kSortTile <= (int)sizeof(S.words), "map layout");
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int h = tid / kSortThreads;  // tile of the pair this thread maps
+    const int ht = tid % kSortThreads;
+    const int wh = ht / kWave;         // wave within the half
+
+    // this thread's slots of its own tile: records (tile positions)
+    uint32_t pos[kReplayItems];
+    if (h < ntile) {
+#pragma unroll
+        for (int q = 0; q < kReplayItems; ++q) pos[q] = rec[(t0 + h) * kSortTile + q * kSortThreads + ht];
+    }
+    reinterpret_cast<uint4*>(sbin)[tid] = make_uint4(0u, 0u, 0u, 0u);  // 1024 x 16 B = both tiles' bin maps
+    if (ht < kRadix) {
+        const bool have = h < ntile;
+        S.start[h][ht] = have ? tab_start[(t0 + h) * kRadix + ht] : 0u;
+        if (ht == 0) S.start[h][kRadix] = have ? (uint32_t)kSortTile : 0u;
+    }
+    __syncthreads();
+    if (ht < kRadix && h < ntile) {
+        const uint32_t st = S.start[h][ht], nx = S.start[h][ht + 1];
+        if (nx > st) sbin[h * kSortTile + st] = (uint8_t)ht;  // first slot of a non-empty bin
+        if (h == 0) S.mbase[ht] = tab_base[t0 * kRadix + ht] - S.start[1][ht];
+    }
+    __syncthreads();
+    {
+        // inclusive prefix max over each tile's slots; thread ht of half h
+        // scans slots 16 ht .. 16 ht + 15 of tile h
+        uint4 raw = reinterpret_cast<const uint4*>(sbin + h * kSortTile)[ht];
+        uint32_t word[4] = {raw.x, raw.y, raw.z, raw.w};
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) m = max(m, (word[k >> 2] >> (8 * (k & 3))) & 0xFFu);
+        uint32_t inc = m;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const uint32_t o = __shfl_up(inc, d);
+            if (lane >= d) inc = max(inc, o);
+        }
+        if (lane == kWave - 1) S.red[h * kSortWaves + wh] = inc;
+        uint32_t ex = __shfl_up(inc, 1);
+        if (lane == 0) ex = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kSortWaves; ++i)
+            if (i < wh) ex = max(ex, S.red[h * kSortWaves + i]);
+        uint32_t run = ex;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const uint32_t sh = 8 * (k & 3);
+            run = max(run, (word[k >> 2] >> sh) & 0xFFu);
+            word[k >> 2] = (word[k >> 2] & ~(0xFFu << sh)) | (run << sh);
+        }
+        reinterpret_cast<uint4*>(sbin + h * kSortTile)[ht] = make_uint4(word[0], word[1], word[2], word[3]);
+    }
+    __syncthreads();
+    // merged slot of each of this thread's slots: slot i of bin b of tile 0
+    // -> i + start_b(1); of tile 1 -> i + start_{b+1}(0)
+    if (h < ntile) {
+#pragma unroll
+        for (int q = 0; q < kReplayItems; ++q) {
+            const uint32_t i = (uint32_t)(q * kSortThreads + ht);
+            const uint32_t b = sbin[h * kSortTile + i];
+            const uint32_t m = i + (h == 0 ? S.start[1][b] : S.start[0][b + 1]);
+            msrc[m] = (uint16_t)(pos[q] | ((uint32_t)h << 13));
+            mbin[m] = (uint8_t)b;
+        }
+    }
+    __syncthreads();
+    const uint32_t total = (uint32_t)(ntile * kSortTile);
+#pragma unroll
+    for (int q = 0; q < kPairItems; ++q) {
+        const uint32_t m = (uint32_t)(q * kPairThreads + tid);
+        const uint32_t sq = m < total ? msrc[m] : m;  // past the pair: the absent tile's own slot
+        if (q % 2 == 0) srcp[q / 2] = sq;
+        else srcp[q / 2] |= sq << 16;
+        dst[q] = m < total ? S.mbase[mbin[m]] + m : 0xFFFFFFFFu;
+    }
+    __syncthreads();  // the maps are dead: the tiles' data takes over their bytes
+}
+
+// Forward: the two tiles' data are read whole into LDS, each merged slot is
+// written to its global position (a scattered run per bin).
 template <typename T, bool IOTA>
 __global__ __launch_bounds__(kPairThreads, 8) void lx_replay_fwd2(const T* __restrict__ in, int64_t in_ld,
                                                               T* __restrict__ out, int64_t out_ld,
@@ -698,23 +810,11 @@ __global__ __launch_bounds__(kPairThreads, 8) void lx_replay_fwd2(const T* __res
                                                               int64_t tiles, int64_t batch)
 {
     static_assert(sizeof(T) == 4, "32-bit elements");
-    // First the maps (per-tile bin of each slot; merged source and bin of
-    // each merged slot), then the two tiles' data, in the same 64 KB.
-    __shared__ __align__(16) uint32_t words[2 * kSortTile];
-    uint8_t* sbin = reinterpret_cast<uint8_t*>(words);           // [2][kSortTile]
-    uint16_t* msrc = reinterpret_cast<uint16_t*>(sbin + 2 * kSortTile);  // [2 kSortTile]: tile << 13 | position
-    uint8_t* mbin = reinterpret_cast<uint8_t*>(msrc + 2 * kSortTile);    // [2 kSortTile]
-    T* buf = reinterpret_cast<T*>(words);                        // [2][kSortTile]
-    __shared__ uint32_t s_start[2][kRadix + 1];
-    __shared__ uint32_t s_mbase[kRadix];
-    __shared__ uint32_t sred[2 * kSortWaves];
-    static_assert(2 * kSortTile + 4 * kSortTile + 2 * kSortTile <= (int)sizeof(words), "map layout");
-
+    __shared__ PairShared S;
+    T* buf = reinterpret_cast<T*>(S.words);  // [2][kSortTile], after the maps
     const int tid = threadIdx.x;
-    const int lane = lane_id();
-    const int h = tid / kSortThreads;  // tile of the pair this thread maps
+    const int h = tid / kSortThreads;
     const int ht = tid % kSortThreads;
-    const int wh = ht / kWave;         // wave within the half
     const int64_t pairs = (tiles + 1) / 2;
     const int64_t t0 = 2 * xcd_tile(blockIdx.x, pairs);
     const int ntile = t0 + 1 < tiles ? 2 : 1;
@@ -738,81 +838,8 @@ __global__ __launch_bounds__(kPairThreads, 8) void lx_replay_fwd2(const T* __res
             else pre[q] = __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(rs, off * 4, 0, 0));
         }
     }
-
-    // this thread's slots of its own tile: records (tile positions)
-    uint32_t pos[kReplayItems];
-    if (h < ntile) {
-#pragma unroll
-        for (int q = 0; q < kReplayItems; ++q) pos[q] = rec[(t0 + h) * kSortTile + q * kSortThreads + ht];
-    }
-    reinterpret_cast<uint4*>(sbin)[tid] = make_uint4(0u, 0u, 0u, 0u);  // 1024 x 16 B = both tiles' bin maps
-    if (ht < kRadix) {
-        const bool have = h < ntile;
-        s_start[h][ht] = have ? tab_start[(t0 + h) * kRadix + ht] : 0u;
-        if (ht == 0) s_start[h][kRadix] = have ? (uint32_t)kSortTile : 0u;
-    }
-    __syncthreads();
-    if (ht < kRadix && h < ntile) {
-        const uint32_t st = s_start[h][ht], nx = s_start[h][ht + 1];
-        if (nx > st) sbin[h * kSortTile + st] = (uint8_t)ht;  // first slot of a non-empty bin
-        if (h == 0) s_mbase[ht] = tab_base[t0 * kRadix + ht] - s_start[1][ht];
-    }
-    __syncthreads();
-    {
-        // inclusive prefix max over each tile's slots; thread ht of half h
-        // scans slots 16 ht .. 16 ht + 15 of tile h
-        uint4 raw = reinterpret_cast<const uint4*>(sbin + h * kSortTile)[ht];
-        uint32_t word[4] = {raw.x, raw.y, raw.z, raw.w};
-        uint32_t m = 0;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) m = max(m, (word[k >> 2] >> (8 * (k & 3))) & 0xFFu);
-        uint32_t inc = m;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const uint32_t o = __shfl_up(inc, d);
-            if (lane >= d) inc = max(inc, o);
-        }
-        if (lane == kWave - 1) sred[h * kSortWaves + wh] = inc;
-        uint32_t ex = __shfl_up(inc, 1);
-        if (lane == 0) ex = 0;
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < kSortWaves; ++i)
-            if (i < wh) ex = max(ex, sred[h * kSortWaves + i]);
-        uint32_t run = ex;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const uint32_t sh = 8 * (k & 3);
-            run = max(run, (word[k >> 2] >> sh) & 0xFFu);
-            word[k >> 2] = (word[k >> 2] & ~(0xFFu << sh)) | (run << sh);
-        }
-        reinterpret_cast<uint4*>(sbin + h * kSortTile)[ht] = make_uint4(word[0], word[1], word[2], word[3]);
-    }
-    __syncthreads();
-    // merged slot of each of this thread's slots: slot i of bin b of tile 0
-    // -> i + start_b(1); of tile 1 -> i + start_{b+1}(0)
-    if (h < ntile) {
-#pragma unroll
-        for (int q = 0; q < kReplayItems; ++q) {
-            const uint32_t i = (uint32_t)(q * kSortThreads + ht);
-            const uint32_t b = sbin[h * kSortTile + i];
-            const uint32_t m = i + (h == 0 ? s_start[1][b] : s_start[0][b + 1]);
-            msrc[m] = (uint16_t)(pos[q] | ((uint32_t)h << 13));
-            mbin[m] = (uint8_t)b;
-        }
-    }
-    __syncthreads();
     uint32_t srcp[kPairItems / 2], dst[kPairItems];  // sources two per word
-    const uint32_t total = (uint32_t)(ntile * kSortTile);
-#pragma unroll
-    for (int q = 0; q < kPairItems; ++q) {
-        const uint32_t m = (uint32_t)(q * kPairThreads + tid);
-        const uint32_t sq = m < total ? msrc[m] : 0u;
-        if (q % 2 == 0) srcp[q / 2] = sq;
-        else srcp[q / 2] |= sq << 16;
-        dst[q] = m < total ? s_mbase[mbin[m]] + m : 0xFFFFFFFFu;
-    }
-    __syncthreads();  // the maps are dead: the tiles' data takes over their bytes
+    pair_maps(S, rec, tab_base, tab_start, t0, ntile, srcp, dst);
     for (int64_t v = 0; v < batch; ++v) {
         const T* iv = in + v * in_ld;
         T* ov = out + v * out_ld;
@@ -842,7 +869,70 @@ __global__ __launch_bounds__(kPairThreads, 8) void lx_replay_fwd2(const T* __res
 #pragma unroll
         for (int q = 0; q < kPairItems; ++q) {
             const uint32_t sq = (srcp[q / 2] >> (16 * (q % 2))) & 0xFFFFu;
-            if (dst[q] < (uint32_t)n) ov[dst[q]] = buf[(sq >> 13) * kSortTile + (sq & 0x1FFFu)];
+            if (dst[q] < (uint32_t)n) ov[dst[q]] = buf[sq];  // sq = tile * kSortTile + position
+        }
+        __syncthreads();
+    }
+}
+
+// Backward: each merged slot is read from its global position (one run per
+// bin), placed in LDS at its tile position, and the two tiles, which are
+// neighbours in the original order, are written out as one block.
+template <typename T>
+__global__ __launch_bounds__(kPairThreads, 8) void lx_replay_bwd2(const T* __restrict__ in, int64_t in_ld,
+                                                              T* __restrict__ out, int64_t out_ld,
+                                                              const uint16_t* __restrict__ rec,
+                                                              const uint32_t* __restrict__ tab_base,
+                                                              const uint16_t* __restrict__ tab_start, int64_t n,
+                                                              int64_t tiles, int64_t batch)
+{
+    static_assert(sizeof(T) == 4, "32-bit elements");
+    __shared__ PairShared S;
+    T* buf = reinterpret_cast<T*>(S.words);  // [2][kSortTile], after the maps
+    const int tid = threadIdx.x;
+    const int64_t pairs = (tiles + 1) / 2;
+    const int64_t t0 = 2 * xcd_tile(blockIdx.x, pairs);
+    const int ntile = t0 + 1 < tiles ? 2 : 1;
+    uint32_t srcp[kPairItems / 2], dst[kPairItems];
+    pair_maps(S, rec, tab_base, tab_start, t0, ntile, srcp, dst);
+    const int64_t p0 = t0 * kSortTile;
+    const int64_t valid = n - p0 < 2 * kSortTile ? n - p0 : 2 * kSortTile;
+    for (int64_t v = 0; v < batch; ++v) {
+        const T* iv = in + v * in_ld;
+        T* ov = out + v * out_ld;
+        // rounds of eight gathers, all of a round in flight before any is
+        // stored; a slot past the pair or past n reads a valid element and
+        // leaves it in a part of buf that is never stored
+        constexpr int kHalf = kPairItems / 2;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            T val[kHalf];
+#pragma unroll
+            for (int q = 0; q < kHalf; ++q) {
+                const uint32_t d = dst[r * kHalf + q];
+                // a 32-bit byte offset from a uniform base (n < 2^30 + 1 fits)
+                const uint32_t off = (d < (uint32_t)n ? d : (uint32_t)(n - 1)) * (uint32_t)sizeof(T);
+                val[q] = *reinterpret_cast<const T*>(reinterpret_cast<const char*>(iv) + off);
+            }
+#pragma unroll
+            for (int q = 0; q < kHalf; ++q) {
+                const int k = r * kHalf + q;
+                buf[(srcp[k / 2] >> (16 * (k % 2))) & 0xFFFFu] = val[q];
+            }
+        }
+        __syncthreads();
+        if (valid == 2 * kSortTile && ((uintptr_t)(ov + p0) & 15) == 0) {
+            // whole aligned pair: four 16-byte stores per thread, lanes contiguous
+            uint4* o4 = reinterpret_cast<uint4*>(ov + p0);
+#pragma unroll
+            for (int q = 0; q < 2 * kSortTile / 4 / kPairThreads; ++q)
+                o4[q * kPairThreads + tid] = reinterpret_cast<const uint4*>(buf)[q * kPairThreads + tid];
+        } else {
+#pragma unroll
+            for (int q = 0; q < kPairItems; ++q) {
+                const int j = q * kPairThreads + tid;
+                if (j < valid) ov[p0 + j] = buf[j];
+            }
         }
         __syncthreads();
     }
@@ -861,6 +951,10 @@ hipError_t replay_launch(const SortRecords& R, int pass, bool forward, const flo
         LX_LAUNCH("replay_forward", s,
                   (lx_replay<float, true, false><<<grid, kSortThreads, 0, s>>>(
                       in, in_ld, out, out_ld, R.rec[pass], R.base[pass], R.start[pass], R.n, batch)));
+    else if (R.tiles >= 2)
+        LX_LAUNCH("replay_backward", s,
+                  (lx_replay_bwd2<float><<<(unsigned)((R.tiles + 1) / 2), kPairThreads, 0, s>>>(
+                      in, in_ld, out, out_ld, R.rec[pass], R.base[pass], R.start[pass], R.n, R.tiles, batch)));
     else
         LX_LAUNCH("replay_backward", s,
                   (lx_replay<float, false, false><<<grid, kSortThreads, 0, s>>>(
