@@ -371,9 +371,28 @@ __device__ __forceinline__ uint32_t block_exsum_u32(uint32_t x, uint32_t* sh, ui
 // in float64, and float64 factors keep long chains of equal gaps (common
 // where many anchors sit on one float32 grid) free of the bias a repeated
 // float32 rounding of exp(-gap) would accumulate.
+// exp(x) for x <= 0.  Neighbouring sorted anchors are usually close, so x is
+// usually tiny: for |x| < 2^-7 the Taylor polynomial of degree 7 leaves a
+// truncation error below x^8 / 8! < 2^-71 and costs 7 FMAs; larger |x| (and
+// x = -inf for t = 0) take the library exp.
+__device__ __forceinline__ double exp_nonpos(double x)
+{
+    if (x > -0x1p-7) {
+        double p = 1.0 / 5040.0;
+        p = fma(p, x, 1.0 / 720.0);
+        p = fma(p, x, 1.0 / 120.0);
+        p = fma(p, x, 1.0 / 24.0);
+        p = fma(p, x, 1.0 / 6.0);
+        p = fma(p, x, 0.5);
+        p = fma(p, x, 1.0);
+        return fma(p, x, 1.0);
+    }
+    return exp(x);
+}
+
 __device__ __forceinline__ double decay(float lo, float hi, double inv_t)
 {
-    return lo == hi ? 1.0 : exp(((double)lo - (double)hi) * inv_t);
+    return lo == hi ? 1.0 : exp_nonpos(((double)lo - (double)hi) * inv_t);
 }
 
 // exp(-(hi - lo) / t) in float32 for anchors lo <= hi, it = 1 / t.
