@@ -30,6 +30,14 @@
  *     LAPLEX_ERR_INVALID_ARGUMENT without touching the device.
  *   - Outputs are overwritten, never accumulated into.
  *   - Inputs are borrowed only for the duration of the call.
+ *
+ * Environment (read once per process):
+ *   LAPLEX_REPLAY_MIN  sides of at least this many anchors (default 2^20)
+ *                      move x into sorted order and y back by replaying the
+ *                      sort's per-pass records (streaming passes); shorter
+ *                      sides gather and scatter through the permutation.
+ *                      Results agree to rounding (the summation order can
+ *                      differ); the permutation is the same.
  */
 #ifndef LAPLEX_H
 #define LAPLEX_H
