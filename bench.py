@@ -19,8 +19,6 @@ training step (forward product plus its backward pass) instead.
 from __future__ import annotations
 
 import argparse
-import glob
-import hashlib
 import json
 import os
 import sys
@@ -50,17 +48,44 @@ def parse():
     return p.parse_args()
 
 
-# --------------------------------------------------------------- byte model
-# Algorithmic bytes per launch of each kernel (what the algorithm must move,
-# not what the counters see), for a sorted side of n anchors, B vectors and
-# C phase channels.  Radix passes: 4 B key in, 4 B key out, 2 B replay record
-# per key, plus a 6 B x 256 table per 8192-key tile.
+# --------------------------------------------------------------- byte models
+# Two byte counts per launch of each kernel, for a sorted side of n anchors,
+# B vectors and C phase channels:
+#
+#  * survey bytes: the hot-path scope table's per-element figures (the bytes
+#    the method's steps move in a plain design: a radix pass reads and
+#    writes key + index, 12 B for the first pass and 16 B for each later
+#    one; the scan reads s and x twice and writes y once; the gather and the
+#    scatter each move an index, the value in and the value out).  The
+#    roofline fraction is quoted on these.
+#  * design bytes: what this design's kernels must move: radix passes carry
+#    x as a value row and write replay records (2 B per key plus a 6 B x 256
+#    table per 8192-key tile) instead of an index; the four backward replays
+#    read the records again.
 
 TILE_TABLE = 6.0 * 256 / 8192
+SURVEY_SORT_PASS = (12.0 + 16.0 + 16.0 + 16.0) / 4  # average over the four launches of one sort
+
+
+def survey_bytes(kernel: str, n: int, batch: int = 1, channels: int = 1) -> float | None:
+    factors = 8.0 if channels == 2 else 0.0
+    per = {
+        "sort_hist": 4.0,
+        "sort_pass": SURVEY_SORT_PASS,
+        # one gather (index, value in, value out) and one scatter, each
+        # spread over the four replays that carry it out
+        "replay_forward": (4.0 + 8.0 * batch) / 4,
+        "replay_backward": (4.0 + 8.0 * batch) / 4,
+        "scan_reduce": 4.0 + factors + 4.0 * batch,
+        "scan_apply": 4.0 + 2 * factors + 8.0 * batch,
+        "scan_reduce_gather": 8.0 + factors + 8.0 * batch,
+        "scan_apply_scatter": 8.0 + 2 * factors + 8.0 * batch,
+    }.get(kernel)
+    return None if per is None else per * n
 
 
 def model_bytes(kernel: str, n: int, batch: int = 1, channels: int = 1, vals: int = 0) -> float | None:
-    """vals: value rows carried by each radix pass (read and written)."""
+    """Design bytes; vals: value rows carried by each radix pass (read and written)."""
     factors = 8.0 if channels == 2 else 0.0
     per = {
         "sort_hist": 4.0,
@@ -79,64 +104,42 @@ def model_bytes(kernel: str, n: int, batch: int = 1, channels: int = 1, vals: in
     return None if per is None else per * n
 
 
+SYM_STEP = {"sort_hist": 1, "sort_pass": 4, "scan_reduce": 1, "scan_apply": 1, "replay_backward": 4}
+
+
+def survey_step_bytes(n: int, batch: int) -> float:
+    """Whole symmetric step by the scope table: sort 68, gather 4 + 8B,
+    scan 8 + 12B, scatter 4 + 8B bytes per element (112 at B = 1)."""
+    return (68.0 + (4.0 + 8.0 * batch) + (8.0 + 12.0 * batch) + (4.0 + 8.0 * batch)) * n
+
+
 def model_step_bytes(n: int, batch: int) -> float:
-    """Whole symmetric step (plan_create_apply on the replay path: the rows
-    of x travel with the keys through the four radix passes)."""
-    launches = {"sort_hist": 1, "sort_pass": 4, "scan_reduce": 1, "scan_apply": 1, "replay_backward": 4}
-    return sum(c * model_bytes(k, n, batch, vals=batch) for k, c in launches.items())
+    """Whole symmetric step by design bytes (plan_create_apply on the replay
+    path: the rows of x travel with the keys through the four radix passes)."""
+    return sum(c * model_bytes(k, n, batch, vals=batch) for k, c in SYM_STEP.items())
 
 
-def counter_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if
-    their recorded source hash still matches the kernel source."""
-    for path in glob.glob(os.path.join(ROOT, "profiles", "*counters*.txt")):
-        kv = {}
-        for line in open(path):
-            if "=" in line and not line.startswith("#"):
-                k, v = line.split("=", 1)
-                kv[k.strip()] = v.strip()
-        if kv.get("kernel") != kernel or kv.get("workload") != workload:
-            continue
-        src = os.path.join(ROOT, "laplace_matvec_amd", "csrc", kv.get("source", ""))
-        if not os.path.exists(src):
-            continue
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-        if sha != kv.get("source_sha"):
-            return None
-        try:
-            return float(kv["hbm_bytes_per_launch"])
-        except (KeyError, ValueError):
-            return None
-    return None
+# Kernel labels of each phase of the path.
+PHASES = {
+    "sort": ("util_fill", "sort_hist", "sort_scan_hist", "sort_pass", "perm_replay"),
+    "scan": ("scan_reduce", "scan_carry", "scan_apply", "scan_reduce_gather", "scan_apply_scatter",
+             "scan_reduce_uv", "scan_apply_tables"),
+    "gather_scatter": ("replay_forward", "replay_backward"),
+}
 
 
-def counter_step_bytes(workload: str):
-    """HBM bytes of one whole step from the committed rocprofv3 counter
-    record (every kernel of the step, calibrated FETCH_SIZE + WRITE_SIZE),
-    if the hashes of all the kernel sources it names still match."""
-    for path in glob.glob(os.path.join(ROOT, "profiles", "*counters*.txt")):
-        kv = {}
-        for line in open(path):
-            if "=" in line and not line.startswith("#"):
-                k, v = line.split("=", 1)
-                kv[k.strip()] = v.strip()
-        if kv.get("kernel") != "step" or kv.get("workload") != workload:
-            continue
-        srcs = kv.get("source", "").split(",")
-        shas = kv.get("source_sha", "").split(",")
-        if len(srcs) != len(shas):
-            return None
-        for src, want in zip(srcs, shas):
-            path_src = os.path.join(ROOT, "laplace_matvec_amd", "csrc", src)
-            if not os.path.exists(path_src):
-                return None
-            if hashlib.sha256(open(path_src, "rb").read()).hexdigest()[:16] != want:
-                return None
-        try:
-            return float(kv["hbm_bytes_per_step"])
-        except (KeyError, ValueError):
-            return None
-    return None
+def gram_bytes(kernel: str, n: int, k: int, weight_sets: int = 1) -> float | None:
+    """Gram: the M write (4 B per entry), b and D read once (8 B per column
+    anchor), the sorted rows (4 B each)."""
+    return {"gram_tile": 4.0 * n * n, "gram_bins": 8.0 * k + 4.0 * n,
+            "gram_scan": (8.0 * 3 * weight_sets + 4.0) * n}.get(kernel)
+
+
+def counter_record(workload: str):
+    """The committed rocprofv3 counter record of a workload, if it was taken
+    from the current library sources (else None)."""
+    from laplace_matvec_amd import counters
+    return counters.find_record(workload, ROOT)
 
 
 def cpu_baseline(sample: int):
@@ -270,32 +273,64 @@ def main():
         per = cnt / args.steps
         kernels[name] = {"launches_per_step": per, "avg_ms": tot / cnt, "ms_per_step": tot / args.steps}
     dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"]) if kernels else None
+    rec = counter_record(W.name)
+    rec_labels = rec["labels"] if rec else {}
     roof = None
     if dominant:
-        ab = model_bytes(dominant, n, batch, vals=batch if W.kind == "sym" else 0)
         avg_s = kernels[dominant]["avg_ms"] / 1e3
+        if W.kind == "gram":
+            ab = gram_bytes(dominant, n, W.k)
+            design = ab
+        else:
+            ab = survey_bytes(dominant, n, batch)
+            design = model_bytes(dominant, n, batch, vals=batch if W.kind == "sym" else 0)
         if ab is not None:
             ach = ab / avg_s / 1e9
+            traffic = rec_labels.get(dominant, (None, None))[1]
             roof = {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
-                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
-                    "traffic": counter_traffic(dominant, W.name),
-                    "algorithmic_bytes_per_launch": ab, "avg_launch_ms": kernels[dominant]["avg_ms"]}
-    # whole-step model bandwidth (symmetric end to end: 4 + 60 sort + 32 apply bytes/elem at B=1)
+                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                    "algorithmic_bytes_per_launch": ab, "avg_launch_ms": kernels[dominant]["avg_ms"],
+                    "design_bytes_per_launch": design,
+                    "design_frac": None if design is None else round(design / avg_s / 1e9 / PEAK_HBM_GBPS, 4),
+                    "counter_record": rec["path"] if rec else None}
     extra = {}
+    # per phase: time in this run, survey / design bytes, and what the counters saw
+    phases = {}
+    for ph, labels in PHASES.items():
+        ms_ph = sum(kernels[k]["ms_per_step"] for k in labels if k in kernels)
+        if ms_ph == 0:
+            continue
+        d = {"ms_per_step": round(ms_ph, 4)}
+        sb = [survey_bytes(k, n, batch) * kernels[k]["launches_per_step"] for k in labels
+              if k in kernels and survey_bytes(k, n, batch) is not None]
+        if W.kind == "sym" and sb:
+            d["survey_gbps"] = round(sum(sb) / (ms_ph / 1e3) / 1e9, 1)
+        cb = [rec_labels[k][0] * rec_labels[k][1] for k in labels if k in kernels and k in rec_labels]
+        if rec and cb:
+            d["counter_bytes_per_step"] = sum(cb)
+            d["counter_gbps"] = round(sum(cb) / (ms_ph / 1e3) / 1e9, 1)
+            d["counter_frac"] = round(sum(cb) / (ms_ph / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
+        phases[ph] = d
+    if phases:
+        extra["phases"] = phases
     if W.kind == "sym" and not args.backward:
+        sv = survey_step_bytes(n, batch)
+        extra["survey_bytes_per_step"] = sv
+        extra["survey_frac_end_to_end"] = round(sv / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
         model = model_step_bytes(n, batch)
-        extra["model_bytes_per_step"] = model
-        extra["model_gbps_end_to_end"] = round(model / (ms / 1e3) / 1e9, 1)
-        extra["model_frac_end_to_end"] = round(model / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
+        extra["design_bytes_per_step"] = model
+        extra["design_frac_end_to_end"] = round(model / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
         # bytes any implementation must move: read a and x, write y
         comp = (4.0 + 8.0 * batch) * n
         extra["compulsory_bytes_per_step"] = comp
         extra["compulsory_gbps_end_to_end"] = round(comp / (ms / 1e3) / 1e9, 1)
-        # what the HBM counters saw for a whole step (committed record), over this run's step time
-        cb = counter_step_bytes(W.name)
-        extra["counter_bytes_per_step"] = cb
-        extra["counter_gbps_end_to_end"] = None if cb is None else round(cb / (ms / 1e3) / 1e9, 1)
-        extra["counter_frac_end_to_end"] = None if cb is None else round(cb / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
+    if rec:
+        # what the HBM counters saw for a whole step (committed record taken
+        # from these sources), over this run's step time
+        cbs = float(rec["step_bytes"])
+        extra["counter_bytes_per_step"] = cbs
+        extra["counter_gbps_end_to_end"] = round(cbs / (ms / 1e3) / 1e9, 1)
+        extra["counter_frac_end_to_end"] = round(cbs / (ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)
     out = {
         "metric": (METRIC if cfg == 5 else f"LAPLEX {W.kind} elements/s ({W.name})") if not args.backward
         else f"LAPLEX training step (forward + backward) elements/s ({W.name})",

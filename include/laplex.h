@@ -69,9 +69,11 @@ typedef enum {
  *   (summary §2.2: "after sorting the anchors")
  *
  *   out    host pointer; receives the plan, or NULL on any error.
- *   a      device, float32[n], the row anchors.  1 <= n <= 2^31 - 1.
+ *   a      device, float32[n], the row anchors.  1 <= n <= 2^30.
  *   b      device, float32[k], the column anchors, or NULL for a symmetric
- *          plan (b := a; then k must be 0 or n).  1 <= k <= 2^31 - 1.
+ *          plan (b := a; then k must be 0 or n).  1 <= k <= 2^30.
+ *          (Longer sides give INVALID_ARGUMENT: element offsets are formed
+ *          as 32-bit byte offsets.)
  *   phi    device, float32[n] row phases, and
  *   psi    device, float32[k] (float32[n] if symmetric) column phases;
  *          both NULL (unphased) or both non-NULL (phased operator).

@@ -5,9 +5,10 @@
 // algebra, general case and Gram); see include/laplex.h for the contract.
 //
 // Every argument check runs before the first HIP call, so invalid calls are
-// rejected on any host, GPU or not.  Device memory comes from a pool owned
-// by the library (stream-ordered allocation, memory kept for reuse), so
-// repeated plans and growing workspaces do not pay for fresh allocations.
+// rejected on any host, GPU or not.  Device memory comes from the library's
+// caching allocator below (freed blocks kept per device and handed out
+// again, each ordered after its last use by an event), so repeated plans and
+// growing workspaces do not pay for fresh allocations.
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
@@ -25,7 +26,10 @@ namespace {
 
 thread_local std::string g_last_error;
 
-constexpr int64_t kMaxLen = 0x7FFFFFFFll;  // permutations are uint32
+// Longest anchor side.  Permutations are uint32, and the backward replay
+// forms its gather offsets as 32-bit byte offsets from a uniform base, so
+// every element index times 4 must fit in 32 bits: n <= 2^30.
+constexpr int64_t kMaxLen = (int64_t)1 << 30;
 
 laplex_status fail(laplex_status st, const std::string& msg)
 {
@@ -441,10 +445,10 @@ laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, cons
     if (out) *out = nullptr;
     if (!out) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "out is NULL");
     if (!a) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "a is NULL");
-    if (n < 1 || n > kMaxLen) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "n must be in [1, 2^31-1]");
+    if (n < 1 || n > kMaxLen) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "n must be in [1, 2^30]");
     const bool sym = b == nullptr;
     if (sym && k != 0 && k != n) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "symmetric plan: k must be 0 or n");
-    if (!sym && (k < 1 || k > kMaxLen)) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "k must be in [1, 2^31-1]");
+    if (!sym && (k < 1 || k > kMaxLen)) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "k must be in [1, 2^30]");
     if ((phi == nullptr) != (psi == nullptr))
         return fail(LAPLEX_ERR_INVALID_ARGUMENT, "phi and psi: give both or neither");
     if (sym) k = n;

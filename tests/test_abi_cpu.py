@@ -52,9 +52,12 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: checks run first
     (None, 10, None, 0, None, None),                 # a NULL
     (FAKE, 0, None, 0, None, None),                  # n < 1
     (FAKE, 1 << 31, None, 0, None, None),            # n too large for uint32 permutations
+    (FAKE, (1 << 30) + 1, None, 0, None, None),      # n past 2^30 (32-bit byte offsets)
     (FAKE, 10, None, 5, None, None),                 # symmetric with k != n
     (FAKE, 10, FAKE, 0, None, None),                 # general with k < 1
     (FAKE, 10, FAKE, 1 << 31, None, None),           # k too large
+    (FAKE, 10, FAKE, (1 << 30) + 1, None, None),     # k past 2^30
+    (FAKE, (1 << 30) + 1, FAKE, 10, None, None),     # general plan, n past 2^30
     (FAKE, 10, None, 0, FAKE, None),                 # phi without psi
     (FAKE, 10, None, 0, None, FAKE),                 # psi without phi
 ])
@@ -84,6 +87,9 @@ def test_apply_and_gram_reject_bad_arguments():
         lx.ERR_INVALID_ARGUMENT  # x and y overlap
     assert lib.laplex_plan_create_apply(ctypes.byref(h), FAKE, 10, None, None, FAKE, ctypes.c_void_p(0x9000), 0,
                                         None) == lx.ERR_INVALID_ARGUMENT
+    big = (1 << 30) + 1  # past the longest side
+    assert lib.laplex_plan_create_apply(ctypes.byref(h), FAKE, big, None, None, ctypes.c_void_p(1 << 44),
+                                        ctypes.c_void_p(1 << 45), 1, None) == lx.ERR_INVALID_ARGUMENT
     assert lib.laplex_backward(None, FAKE, FAKE, 1, 0, FAKE, None, None, None, None, None) == \
         lx.ERR_INVALID_ARGUMENT
     for s in range(7):
