@@ -764,7 +764,40 @@ laplex_status laplex_plan_set_temperature(laplex_plan p, double t)
     return LAPLEX_OK;
 }
 
-laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batch, int transpose, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Where an apply takes its workspace: the plan's own (grown on demand), or
+// a fixed region that must already be large enough (no allocation).
+struct WsSource {
+    void* fixed = nullptr;
+    size_t fixed_bytes = 0;
+};
+
+laplex_status take_ws(laplex_plan p, size_t need, hipStream_t s, const WsSource& src, void** base)
+{
+    if (src.fixed) {
+        if (need > src.fixed_bytes)
+            return fail(LAPLEX_ERR_INVALID_ARGUMENT, "this apply needs " + std::to_string(need) +
+                                                         " bytes of scratch; the fixed scratch holds " +
+                                                         std::to_string(src.fixed_bytes));
+        *base = src.fixed;
+        return LAPLEX_OK;
+    }
+    LX_TRY(ensure_ws(p, need, s), "workspace");
+    *base = p->ws;
+    return LAPLEX_OK;
+}
+
+#define LX_WS(need, base)                                           \
+    do {                                                            \
+        const laplex_status lx_w_ = take_ws(p, (need), s, src, &(base)); \
+        if (lx_w_ != LAPLEX_OK) return lx_w_;                       \
+    } while (0)
+
+laplex_status apply_impl(laplex_plan p, const float* x, float* y, int64_t batch, int transpose, void* stream,
+                         const WsSource& src)
 {
     if (!p) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "plan is NULL");
     if (!x || !y) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "x or y is NULL");
@@ -783,9 +816,13 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
     if (p->sym) {
         const int64_t n = p->n;
         const bool replay = n >= replay_min();
-        if (!replay) LX_TRY(ensure_perm(p, 0, s), "permutation");
-        LX_TRY(ensure_ws(p, scan_ws_bytes(n, batch, ch, replay ? 2 : 1, 0), s), "workspace");
-        Carve cv(p->ws);
+        if (!replay && !p->pa) {
+            if (src.fixed) return fail(LAPLEX_ERR_UNSUPPORTED, "the plan has no permutation yet");
+            LX_TRY(ensure_perm(p, 0, s), "permutation");
+        }
+        void* wsb = nullptr;
+        LX_WS(scan_ws_bytes(n, batch, ch, replay ? 2 : 1, 0), wsb);
+        Carve cv(wsb);
         lx::ScanArgs A;
         A.mode = lx::kScanSym;
         scan_common(A, cv, n, batch, ch);
@@ -849,8 +886,9 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
     if (algo == LAPLEX_ALGO_AUTO) algo = ni <= no ? LAPLEX_ALGO_EVALUATE : LAPLEX_ALGO_BUCKET;
 
     if (algo == LAPLEX_ALGO_EVALUATE) {
-        LX_TRY(ensure_ws(p, scan_ws_bytes(ni, batch, ch, 1, 2), s), "workspace");
-        Carve cv(p->ws);
+        void* wsb = nullptr;
+        LX_WS(scan_ws_bytes(ni, batch, ch, 1, 2), wsb);
+        Carve cv(wsb);
         lx::ScanArgs A;
         A.mode = lx::kScanPLPR;
         A.random = true;
@@ -905,11 +943,15 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
     Bk.ld = pad64(no);
     Bk.lds_bytes = p->lds_bytes;
     Bk.partial_floats = lx::bucket_partial_floats(Bk, nullptr, nullptr);
-    const size_t layout_bytes = Bk.partial_floats ? (size_t)lx::bucket_layout_bytes(Bk) : 0;
-    const size_t need = scan_ws_bytes(no, batch, ch, 0, 2) + align256((size_t)Bk.partial_floats * 4) +
-                        align256(layout_bytes);
-    LX_TRY(ensure_ws(p, need, s), "workspace");
-    Carve cv(p->ws);
+    // a short output side bins in LDS; a long one merges the sorted sides
+    const bool merge = Bk.partial_floats == 0;
+    const size_t layout_bytes = merge ? 0 : (size_t)lx::bucket_layout_bytes(Bk);
+    const size_t need = scan_ws_bytes(no, batch, ch, 0, 2) +
+                        (merge ? lx::merge_ws_bytes(ni, no, batch, ch)
+                               : align256((size_t)Bk.partial_floats * 4) + align256(layout_bytes));
+    void* wsb = nullptr;
+    LX_WS(need, wsb);
+    Carve cv(wsb);
     lx::ScanArgs A;
     A.mode = lx::kScanUV;
     A.random = true;
@@ -926,15 +968,52 @@ laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batc
         A.out_c = c_o;
         A.out_s = sn_o;
     }
-    Bk.u = u;
-    Bk.v = v;
-    Bk.partial = Bk.partial_floats ? cv.take<float>((size_t)Bk.partial_floats) : nullptr;
-    Bk.layout = layout_bytes ? (void*)cv.take<char>(layout_bytes) : nullptr;
-    LX_TRY(lx::bucket_launch(Bk, s), "bucket inputs");
+    if (merge) {
+        lx::MergeArgs M;
+        M.channels = ch;
+        M.n_out = no;
+        M.n_in = ni;
+        M.batch = batch;
+        M.inv_t = p->inv_t;
+        M.s_out = s_o;
+        M.s_in = s_i;
+        M.perm_in = p_i;
+        if (p->phased) {
+            M.in_c = c_i;
+            M.in_s = sn_i;
+        }
+        M.x = x;
+        M.ld = A.ld;
+        M.u = u;
+        M.v = v;
+        const int64_t tiles = lx::merge_tiles(ni, no);
+        M.split = cv.take<uint2>((size_t)tiles + 1);
+        M.head = cv.take<double>((size_t)ch * batch * tiles * 2);
+        M.tail = cv.take<double>((size_t)ch * batch * tiles * 2);
+        LX_TRY(lx::merge_launch(M, s), "merge inputs");
+    } else {
+        Bk.u = u;
+        Bk.v = v;
+        Bk.partial = cv.take<float>((size_t)Bk.partial_floats);
+        Bk.layout = (void*)cv.take<char>(layout_bytes);
+        LX_TRY(lx::bucket_launch(Bk, s), "bucket inputs");
+    }
     LX_TRY(lx::scan_launch(A, s), "scan over the output side");
-    (void)p_i;
     return LAPLEX_OK;
 }
+
+#undef LX_WS
+
+}  // namespace
+
+extern "C" {
+
+laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batch, int transpose, void* stream)
+{
+    return apply_impl(p, x, y, batch, transpose, stream, WsSource{});
+}
+
+}  // extern "C"
 
 namespace {
 
@@ -1086,6 +1165,8 @@ laplex_status grad_general_side(laplex_plan p, const GradSide& G, const float* V
 }
 
 }  // namespace
+
+extern "C" {
 
 laplex_status laplex_backward(laplex_plan p, const float* x, const float* g, int64_t batch, int transpose,
                               float* dx, float* da, float* db, float* dphi, float* dpsi, void* stream)

@@ -19,7 +19,7 @@
 //                      order; then per group of vectors, register
 //                      accumulation by an owner thread per anchor; the
 //                      per-workgroup partials summed in a fixed order;
-//   lx_bucket_global : u, v with device-wide float atomics, any size;
+//   (a long sorted output side takes the merge-path bucketing of merge.hip);
 //   lx_eval_rows / lx_eval : the transposed reading of the same identity:
 //                      with the scan run over the sorted INPUT side (PL =
 //                      prefix, PR = suffix, both inclusive), an output at
@@ -368,33 +368,6 @@ __global__ __launch_bounds__(256) void lx_bucket_reduce(const float* __restrict_
     }
 }
 
-template <int C>
-__global__ __launch_bounds__(256) void lx_bucket_global(BucketArgs A)
-{
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t no = A.n_out;
-    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < A.n_in; j += stride) {
-        const float q = A.in_anchor[j];
-        const int64_t t = lower_bound_f(A.s_out, no, q);
-        const float al = t < no ? decay_f(q, A.s_out[t], A.inv_t) : 0.f;
-        const float be = t > 0 ? decay_f(A.s_out[t - 1], q, A.inv_t) : 0.f;
-        float f[C];
-        f[0] = C == 2 ? A.in_cos[j] : 1.f;
-        if (C == 2) f[C - 1] = A.in_sin[j];
-        for (int64_t vv = 0; vv < A.batch; ++vv) {
-            const float xv = A.x[vv * A.n_in + j];
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                const float val = f[c] * xv;
-                const int64_t row = ((int64_t)c * A.batch + vv) * A.ld;
-                if (t < no) atomicAdd(A.u + row + t, al * val);
-                if (t > 0) atomicAdd(A.v + row + t - 1, be * val);
-                if (A.ties && t < no && A.s_out[t] == q) atomicAdd(A.tie + row + t, val);
-            }
-        }
-    }
-}
-
 static void bucket_shape(const BucketArgs& a, int* vg, int* groups, int* chunks, int64_t* chunk_len)
 {
     const bool fits = a.n_out <= kGenThreads && a.lds_bytes > 0 &&
@@ -472,22 +445,8 @@ hipError_t bucket_launch(BucketArgs& a, hipStream_t s)
                                                                  a.n_out, a.ld, a.u, a.v, a.tie)));
         return hipSuccess;
     }
-    // global path: clear u, v (and the tie sums), then accumulate with device atomics
-    const int64_t words = (int64_t)a.channels * a.batch * a.ld;
-    hipError_t e = fill_u32((uint32_t*)a.u, 0u, words, s);
-    if (e != hipSuccess) return e;
-    e = fill_u32((uint32_t*)a.v, 0u, words, s);
-    if (e != hipSuccess) return e;
-    if (ties) {
-        e = fill_u32((uint32_t*)a.tie, 0u, words, s);
-        if (e != hipSuccess) return e;
-    }
-    if (a.n_in <= 0) return hipSuccess;
-    int64_t blocks = (a.n_in + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    if (two) LX_LAUNCH("bucket_global", s, (lx_bucket_global<2><<<(unsigned)blocks, 256, 0, s>>>(a)));
-    else LX_LAUNCH("bucket_global", s, (lx_bucket_global<1><<<(unsigned)blocks, 256, 0, s>>>(a)));
-    return hipSuccess;
+    // not the LDS-binned shape: the caller runs merge-path bucketing instead
+    return hipErrorInvalidValue;
 }
 
 // ------------------------------------------------------------- evaluation

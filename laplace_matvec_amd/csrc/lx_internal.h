@@ -146,16 +146,44 @@ struct BucketArgs {
     float* partial = nullptr;        // scratch for the LDS-binned path
     int64_t partial_floats = 0;
     void* layout = nullptr;          // scratch for the LDS-binned path: bucket_layout_bytes()
-    int lds_bytes = 0;               // LDS budget per workgroup (0: global path)
+    int lds_bytes = 0;               // LDS budget per workgroup
 };
-// Scratch floats the LDS-binned bucketing needs for these sizes (0 if it is
-// not used and the global-atomics path runs instead).
+// Scratch floats the LDS-binned bucketing needs for these sizes
+// (0 if the shape does not fit that path: then merge-path bucketing runs)
 int64_t bucket_partial_floats(const BucketArgs& a, int* groups, int* chunks);
 // Bytes of the per-call input layout of the LDS-binned path (slots of the
 // inputs, interval starts per sub-chunk, anchors and phase factors in slot
 // order), 256-byte aligned.
 int64_t bucket_layout_bytes(const BucketArgs& a);
 hipError_t bucket_launch(BucketArgs& a, hipStream_t s);
+
+// Merge-path bucketing (merge.hip) for a long sorted output side: the
+// sorted input side and the sorted outputs merged (an input before an
+// output of equal value), tiles of the merged sequence per workgroup,
+// segmented float64 sums of each interval's run of inputs into u, v.
+struct MergeArgs {
+    int channels = 1;
+    int64_t n_out = 0;                // sorted output side
+    int64_t n_in = 0;                 // sorted input side
+    int64_t batch = 0;
+    double inv_t = 1.0;               // 1 / temperature (+inf: equality routing)
+    const float* s_out = nullptr;     // sorted output anchors [n_out]
+    const float* s_in = nullptr;      // sorted input anchors [n_in]
+    const uint32_t* perm_in = nullptr;  // input rank -> original index
+    const float* in_c = nullptr;      // cos / sin of the input phases by input rank (phased)
+    const float* in_s = nullptr;
+    const float* x = nullptr;         // [batch][n_in], original order
+    int64_t ld = 0;                   // row stride of u, v
+    float* u = nullptr;               // [channels][batch][ld] by output rank (overwritten)
+    float* v = nullptr;
+    uint2* split = nullptr;           // [tiles + 1] scratch: (inputs, outputs) before each tile
+    double* head = nullptr;           // [channels][batch][tiles][2] scratch
+    double* tail = nullptr;           // [channels][batch][tiles][2] scratch
+    int64_t tiles = 0;                // set by merge_launch
+};
+int64_t merge_tiles(int64_t n_in, int64_t n_out);
+size_t merge_ws_bytes(int64_t n_in, int64_t n_out, int64_t batch, int channels);
+hipError_t merge_launch(MergeArgs& a, hipStream_t s);
 
 // Evaluation from per-interval LDS rows (lx_eval_rows, lx_eval_grad_rows):
 // groups of up to kEvalVG vectors; row t of the tables holds, per vector,
