@@ -128,6 +128,26 @@ laplex_status laplex_apply(laplex_plan plan, const float* x, float* y, int64_t b
                            int transpose, void* stream);
 
 /*
+ * laplex_apply_noalloc -- laplex_apply without any device allocation.
+ *   For callers that cannot allocate: code under HIP graph capture, tight
+ *   serving loops, harnesses that forbid hipMalloc.
+ *
+ *   Arguments, results and errors as laplex_apply (bit for bit the same
+ *   y), but the workspace is a fixed scratch array inside the library, one
+ *   copy per GPU of LAPLEX_NOALLOC_SCRATCH_BYTES, held until the process
+ *   ends, instead of the plan's growing workspace; no hipMalloc, hipFree or
+ *   allocating library call is made.  A call whose workspace would exceed
+ *   the array returns LAPLEX_ERR_INVALID_ARGUMENT (laplex_last_error says
+ *   how much it needs); roughly, a symmetric plan takes batch * n up to
+ *   about 7.5 million (2^20 <= n) or 15 million (shorter n).  Every call on
+ *   one GPU shares that GPU's array: calls that overlap in time on one GPU
+ *   (other streams or threads) race and must be ordered by the caller.
+ */
+#define LAPLEX_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+laplex_status laplex_apply_noalloc(laplex_plan plan, const float* x, float* y, int64_t batch,
+                                   int transpose, void* stream);
+
+/*
  * laplex_gram -- weighted Gram matrix M = A diag(D) A^T with A = K (n x k).
  *   (summary §2.2, Gram operators: O(n^2 + k log n), not O(n^2 k))
  *

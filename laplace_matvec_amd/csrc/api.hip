@@ -1004,6 +1004,34 @@ laplex_status apply_impl(laplex_plan p, const float* x, float* y, int64_t batch,
 
 #undef LX_WS
 
+// ------------------------------------------------------ allocation-free apply
+//
+// laplex_apply_noalloc takes its workspace from this file-scope array, one
+// copy per device, kept until the process ends.  Host code reaches it only
+// through the device address hipGetSymbolAddress returns (looked up once per
+// device, with that device current); the array's own name is a host-side
+// stand-in.  Kernels never need it cleared: every word a kernel reads was
+// written earlier in the same call.
+constexpr size_t kNoAllocBytes = LAPLEX_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device; null until looked up
+
+hipError_t noalloc_scratch(int dev, void** out)
+{
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1011,6 +1039,17 @@ extern "C" {
 laplex_status laplex_apply(laplex_plan p, const float* x, float* y, int64_t batch, int transpose, void* stream)
 {
     return apply_impl(p, x, y, batch, transpose, stream, WsSource{});
+}
+
+laplex_status laplex_apply_noalloc(laplex_plan p, const float* x, float* y, int64_t batch, int transpose,
+                                   void* stream)
+{
+    if (!p) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "plan is NULL");
+    DeviceGuard g(p->device);
+    WsSource src;
+    LX_TRY(noalloc_scratch(p->device, &src.fixed), "scratch address");
+    src.fixed_bytes = kNoAllocBytes;
+    return apply_impl(p, x, y, batch, transpose, stream, src);
 }
 
 }  // extern "C"

@@ -33,6 +33,7 @@ SIGNATURES = {
     "laplex_plan_create": (_I32, [ctypes.POINTER(_VP), _VP, _I64, _VP, _I64, _VP, _VP, _VP]),
     "laplex_plan_create_apply": (_I32, [ctypes.POINTER(_VP), _VP, _I64, _VP, _VP, _VP, _VP, _I64, _VP]),
     "laplex_apply": (_I32, [_VP, _VP, _VP, _I64, _I32, _VP]),
+    "laplex_apply_noalloc": (_I32, [_VP, _VP, _VP, _I64, _I32, _VP]),
     "laplex_gram": (_I32, [_VP, _VP, _VP, _VP]),
     "laplex_plan_destroy": (_I32, [_VP]),
     "laplex_plan_perm": (_I32, [_VP, _I32, ctypes.POINTER(_VP)]),
@@ -181,6 +182,20 @@ def laplex_apply(plan: Plan, x, y=None, transpose: bool = False, stream=None):
         raise ValueError("y has the wrong size")
     _check(load().laplex_apply(plan.handle, _ptr(x), _ptr(y), batch, int(bool(transpose)), _stream(stream)),
            "laplex_apply")
+    return y
+
+
+def laplex_apply_noalloc(plan: Plan, x, y, transpose: bool = False, stream=None):
+    """laplex_apply into a caller-provided y, with the library's fixed
+    scratch instead of any allocation (see include/laplex.h)."""
+    x = _dev_f32(x, "x")
+    y = _dev_f32(y, "y")
+    n_in, n_out = (plan.n, plan.k) if transpose else (plan.k, plan.n)
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    if x.shape[-1] != n_in or x.dim() > 2 or y.numel() != batch * n_out:
+        raise ValueError(f"x must be [batch][{n_in}] and y [batch][{n_out}]")
+    _check(load().laplex_apply_noalloc(plan.handle, _ptr(x), _ptr(y), batch, int(bool(transpose)),
+                                       _stream(stream)), "laplex_apply_noalloc")
     return y
 
 
