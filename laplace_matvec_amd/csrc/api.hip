@@ -66,10 +66,15 @@ inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 // on s at the free; whoever takes it next orders its stream after that
 // event, so reuse across streams is safe.  When the driver is out of
 // memory, the cached blocks are released and the allocation is retried.
+// One event recorded at a free, shared by the blocks freed together.
+struct FreeEvent {
+    hipEvent_t ev;
+    int refs;
+};
 struct CachedBlock {
     void* ptr;
     size_t bytes;
-    hipEvent_t freed;  // recorded at the free (null: idle already)
+    FreeEvent* freed;  // recorded at the free (null: idle already)
 };
 struct DeviceCache {
     std::mutex mu;
@@ -93,13 +98,22 @@ size_t round_block(size_t bytes)
     return (bytes + q - 1) / q * q;
 }
 
+// Caller holds c.mu.  Drops one block's reference to its free event.
+void drop_event(DeviceCache& c, FreeEvent* f)
+{
+    if (f && --f->refs == 0) {
+        c.events.push_back(f->ev);
+        delete f;
+    }
+}
+
 // Caller holds c.mu.  Waits for the idle blocks' frees and returns them.
 void release_idle(DeviceCache& c)
 {
     for (CachedBlock& b : c.idle) {
         if (b.freed) {
-            (void)hipEventSynchronize(b.freed);
-            c.events.push_back(b.freed);
+            (void)hipEventSynchronize(b.freed->ev);
+            drop_event(c, b.freed);
         }
         (void)hipFree(b.ptr);
     }
@@ -121,8 +135,8 @@ hipError_t dev_alloc(void** ptr, size_t bytes, int dev, hipStream_t s)
         CachedBlock b = c.idle[best];
         c.idle.erase(c.idle.begin() + best);
         if (b.freed) {
-            (void)hipStreamWaitEvent(s, b.freed, 0);
-            c.events.push_back(b.freed);
+            (void)hipStreamWaitEvent(s, b.freed->ev, 0);
+            drop_event(c, b.freed);
         }
         c.live.emplace_back(b.ptr, b.bytes);
         *ptr = b.ptr;
@@ -142,32 +156,53 @@ hipError_t dev_alloc(void** ptr, size_t bytes, int dev, hipStream_t s)
     return hipSuccess;
 }
 
-void dev_free(void* ptr, int dev, hipStream_t s)
+// Returns blocks to the cache.  Their last uses are ordered on stream s:
+// one event recorded there now orders whoever takes any of them next.
+// With `idle` the caller has already waited for them (no event).
+void dev_free_many(void* const* ptrs, size_t count, int dev, hipStream_t s, bool idle = false)
 {
-    if (!ptr) return;
     DeviceCache& c = cache_for(dev);
     std::lock_guard<std::mutex> lk(c.mu);
-    for (size_t i = 0; i < c.live.size(); ++i) {
-        if (c.live[i].first != ptr) continue;
-        const size_t bytes = c.live[i].second;
-        c.live[i] = c.live.back();
-        c.live.pop_back();
+    FreeEvent* fe = nullptr;
+    if (!idle) {
         hipEvent_t ev = nullptr;
         if (!c.events.empty()) {
             ev = c.events.back();
             c.events.pop_back();
         } else if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+            (void)hipGetLastError();
             ev = nullptr;
         }
         if (ev && hipEventRecord(ev, s) != hipSuccess) {
             (void)hipGetLastError();
-            (void)hipStreamSynchronize(s);
             c.events.push_back(ev);
             ev = nullptr;
         }
-        c.idle.push_back(CachedBlock{ptr, bytes, ev});
-        return;
+        if (ev) fe = new FreeEvent{ev, 0};
+        else (void)hipStreamSynchronize(s);  // no event: wait here instead
     }
+    for (size_t k = 0; k < count; ++k) {
+        void* ptr = ptrs[k];
+        if (!ptr) continue;
+        for (size_t i = 0; i < c.live.size(); ++i) {
+            if (c.live[i].first != ptr) continue;
+            const size_t bytes = c.live[i].second;
+            c.live[i] = c.live.back();
+            c.live.pop_back();
+            if (fe) ++fe->refs;
+            c.idle.push_back(CachedBlock{ptr, bytes, fe});
+            break;
+        }
+    }
+    if (fe && fe->refs == 0) {
+        c.events.push_back(fe->ev);
+        delete fe;
+    }
+}
+
+void dev_free(void* ptr, int dev, hipStream_t s)
+{
+    if (ptr) dev_free_many(&ptr, 1, dev, s);
 }
 
 // ------------------------------------------------------------- profiling
@@ -262,6 +297,9 @@ struct laplex_plan_s {
     void* ws = nullptr;
     size_t ws_bytes = 0;
     std::vector<void*> owned;
+    // the stream the plan's work was ordered on (multi: more than one)
+    hipStream_t stream = nullptr;
+    bool stream_known = false, multi_stream = false;
 };
 
 namespace {
@@ -286,14 +324,31 @@ hipError_t plan_alloc(laplex_plan p, void** out, size_t bytes, hipStream_t s)
     return e;
 }
 
+void note_stream(laplex_plan p, hipStream_t s)
+{
+    if (!p->stream_known) {
+        p->stream = s;
+        p->stream_known = true;
+    } else if (p->stream != s) {
+        p->multi_stream = true;
+    }
+}
+
 void plan_release(laplex_plan p)
 {
     if (!p) return;
-    // every stream may still use the plan's memory: wait for the device, then
-    // the blocks go back to the cache already idle
-    (void)hipDeviceSynchronize();
-    for (void* q : p->owned) dev_free(q, p->device, nullptr);
-    if (p->ws) dev_free(p->ws, p->device, nullptr);
+    std::vector<void*> blocks = p->owned;
+    if (p->ws) blocks.push_back(p->ws);
+    if (p->stream_known && !p->multi_stream) {
+        // all of the plan's work was ordered on one stream: the blocks go
+        // back to the cache behind one event on it, nothing waits here
+        dev_free_many(blocks.data(), blocks.size(), p->device, p->stream);
+    } else {
+        // several streams may still use the plan's memory: wait for the
+        // device, then the blocks go back to the cache already idle
+        (void)hipDeviceSynchronize();
+        dev_free_many(blocks.data(), blocks.size(), p->device, nullptr, true);
+    }
     delete p;
 }
 
@@ -457,6 +512,7 @@ laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, cons
 
     hipStream_t s = (hipStream_t)stream;
     laplex_plan p = new laplex_plan_s();
+    note_stream(p, s);
     p->n = n;
     p->k = k;
     p->sym = sym;
@@ -499,6 +555,9 @@ laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, cons
             LX_PLAN_TRY(plan_alloc(p, (void**)&p->spsi, (size_t)n * 4, s), "alloc phases");
         }
         const bool with_y = x != nullptr && batch <= 8;
+        // the kernel that computes y also copies x for a later backward
+        float* keep = nullptr;
+        if (with_y) LX_PLAN_TRY(plan_alloc(p, (void**)&keep, (size_t)(batch * n) * 4, s), "alloc kept x");
         lx::SmallSymArgs S;
         S.n = n;
         S.batch = with_y ? (int)batch : 0;
@@ -507,6 +566,7 @@ laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, cons
         S.phi = phi;
         S.psi = psi;
         S.x = with_y ? x : nullptr;
+        S.x_keep = keep;
         S.y = with_y ? y : nullptr;
         S.sa = p->sa;
         S.perm = p->pa;
@@ -520,12 +580,12 @@ laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, cons
         LX_PLAN_TRY(hipStreamSynchronize(s), "synchronize");
         if (host_flag & 1u) return bail(fail(LAPLEX_ERR_NONFINITE_ANCHOR, "NaN or Inf among anchors or phases"));
         if (x) {
-            // x in its original order is kept for a later backward
+            // x in its original order is kept for a later backward (copied
+            // by the plan kernel when it computed y)
             laplex_status st2 = with_y ? LAPLEX_OK : laplex_apply(p, x, y, batch, 0, stream);
-            float* keep = nullptr;
-            if (st2 == LAPLEX_OK)
+            if (!with_y && st2 == LAPLEX_OK)
                 st2 = from_hip(plan_alloc(p, (void**)&keep, (size_t)(batch * n) * 4, s), "alloc kept x");
-            if (st2 == LAPLEX_OK)
+            if (!with_y && st2 == LAPLEX_OK)
                 st2 = from_hip(hipMemcpyAsync(keep, x, (size_t)(batch * n) * 4, hipMemcpyDeviceToDevice, s), "copy x");
             p->kept_x = keep;
             p->kept_by_rank = false;
@@ -721,6 +781,7 @@ laplex_status laplex_plan_perm(laplex_plan p, int side, const uint32_t** perm_de
 {
     if (!p || !perm_dev || (side != 0 && side != 1)) return fail(LAPLEX_ERR_INVALID_ARGUMENT, "bad plan_perm arguments");
     DeviceGuard g(p->device);
+    note_stream(p, nullptr);
     LX_TRY(ensure_perm(p, side, nullptr), "permutation");
     LX_TRY(hipStreamSynchronize(nullptr), "synchronize");
     *perm_dev = side == 0 ? p->pa : p->pb;
@@ -811,6 +872,7 @@ laplex_status apply_impl(laplex_plan p, const float* x, float* y, int64_t batch,
         return fail(LAPLEX_ERR_INVALID_ARGUMENT, "x and y overlap");
     DeviceGuard g(p->device);
     hipStream_t s = (hipStream_t)stream;
+    note_stream(p, s);
     const int ch = p->phased ? 2 : 1;
 
     if (p->sym) {
@@ -1246,6 +1308,7 @@ laplex_status laplex_backward(laplex_plan p, const float* x, const float* g, int
     if (!dx && !da && !db && !dphi && !dpsi) return LAPLEX_OK;
     DeviceGuard guard(p->device);
     hipStream_t s = (hipStream_t)stream;
+    note_stream(p, s);
     const int ch = p->phased ? 2 : 1;
     // row side u, column side w of F = sum <u, K w>
     const float* u = transpose ? x : g;
@@ -1367,9 +1430,10 @@ laplex_status laplex_gram(laplex_plan p, const float* D, float* M, void* stream)
         return fail(LAPLEX_ERR_INVALID_ARGUMENT, "D and M overlap");
     DeviceGuard g(p->device);
     hipStream_t s = (hipStream_t)stream;
+    note_stream(p, s);
     LX_TRY(ensure_perm(p, 0, s), "permutation of a");
     LX_TRY(ensure_perm(p, 1, s), "permutation of b");
-    LX_TRY(ensure_ws(p, lx::gram_scratch_bytes(p->n, p->phased ? 3 : 1), s), "workspace");
+    LX_TRY(ensure_ws(p, lx::gram_scratch_bytes(p->n, p->k, p->phased ? 3 : 1), s), "workspace");
     lx::GramArgs G;
     G.n = p->n;
     G.k = p->k;

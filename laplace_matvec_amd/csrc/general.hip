@@ -213,6 +213,9 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, Bu
 {
     extern __shared__ float lds[];
     const int no = (int)A.n_out;  // <= kGenThreads
+    // intervals 0 .. no: thread t owns interval t; interval no has no thread
+    // of its own when no == kGenThreads and goes to thread 0
+    const bool last_extra = no == kGenThreads && threadIdx.x == 0;
     float4* xs = reinterpret_cast<float4*>(lds);                // [kSub][2]: 8 vectors by slot
     float4* cs = xs + 2 * kSub;                                 // [kSub]: factors by slot
     uint8_t* ts = reinterpret_cast<uint8_t*>(cs + kSub);        // [kSub]: tie flags by slot (TIES)
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, Bu
     float xin[kSubItems][kBucketVG];
     float cfn[kSubItems][4];
     uint8_t tfn[TIES ? kSubItems : 1];
-    uint16_t sln[kSubItems], stn[3];
+    uint16_t sln[kSubItems], stn[4];
     auto load_sub = [&](int64_t base) {
         const int64_t sub = base / kSub;
 #pragma unroll
@@ -269,8 +272,11 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, Bu
             if (TIES) tfn[j] = L.tie[base + p];
         }
         const uint16_t* st = L.start + sub * L.stride;
-#pragma unroll
-        for (int k = 0; k < 3; ++k) stn[k] = st[tid + k < no + 2 ? tid + k : 0];
+        stn[0] = st[tid < no + 2 ? tid : 0];
+        stn[1] = st[tid + 1 < no + 2 ? tid + 1 : 0];
+        // thread 0 also owns interval no when no == kGenThreads (no thread no)
+        stn[2] = st[last_extra ? no : 0];
+        stn[3] = st[last_extra ? no + 1 : 0];
     };
     if (j0 < j1) load_sub(j0);
     for (int64_t sub0 = j0; sub0 < j1; sub0 += kSub) {
@@ -289,18 +295,22 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, Bu
             cs[p] = make_float4(cfn[j][0], cfn[j][1], cfn[j][2], cfn[j][3]);
             if (TIES) ts[p] = tfn[TIES ? j : 0];
         }
-        const uint32_t s0 = stn[0], s1 = stn[1], s2 = stn[2];
+        const uint32_t s0 = stn[0], s1 = stn[1], e0 = stn[2], e1 = stn[3];
         __syncthreads();
         if (sub0 + kSub < j1) load_sub(sub0 + kSub);
-        if (tid < no) {
-            for (uint32_t sl = s0; sl < s1; ++sl) {  // interval tid: alpha parts -> u_tid
-                const float2 f = *reinterpret_cast<const float2*>(&cs[sl].x);
+        // interval tid: every slot read once, its alpha part into u_tid and
+        // its beta part into v_{tid-1} (interval 0 has no beta part)
+        if (tid <= no) {
+            for (uint32_t sl = s0; sl < s1; ++sl) {
+                const float4 f = cs[sl];
                 const float4 xa = xs[2 * sl], xb = xs[2 * sl + 1];
                 const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
                 for (int vi = 0; vi < kBucketVG; ++vi) {
                     au[vi][0] = fmaf(f.x, xv[vi], au[vi][0]);
                     if (C == 2) au[vi][C - 1] = fmaf(f.y, xv[vi], au[vi][C - 1]);
+                    av[vi][0] = fmaf(f.z, xv[vi], av[vi][0]);
+                    if (C == 2) av[vi][C - 1] = fmaf(f.w, xv[vi], av[vi][C - 1]);
                 }
                 if (TIES) {  // a tie's alpha is exactly 1: its factors are the phase's cos, sin
                     const float tw = ts[sl] ? 1.f : 0.f;
@@ -311,32 +321,37 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, Bu
                     }
                 }
             }
-            for (uint32_t sl = s1; sl < s2; ++sl) {  // interval tid+1: beta parts -> v_tid
-                const float2 f = *reinterpret_cast<const float2*>(&cs[sl].z);
-                const float4 xa = xs[2 * sl], xb = xs[2 * sl + 1];
-                const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+        }
+        // interval no when no == kGenThreads: its beta parts are v_{no-1},
+        // kept by thread 0 (whose own interval 0 has none)
+        for (uint32_t sl = e0; sl < e1; ++sl) {
+            const float2 f = *reinterpret_cast<const float2*>(&cs[sl].z);
+            const float4 xa = xs[2 * sl], xb = xs[2 * sl + 1];
+            const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
-                for (int vi = 0; vi < kBucketVG; ++vi) {
-                    av[vi][0] = fmaf(f.x, xv[vi], av[vi][0]);
-                    if (C == 2) av[vi][C - 1] = fmaf(f.y, xv[vi], av[vi][C - 1]);
-                }
+            for (int vi = 0; vi < kBucketVG; ++vi) {
+                av[vi][0] = fmaf(f.x, xv[vi], av[vi][0]);
+                if (C == 2) av[vi][C - 1] = fmaf(f.y, xv[vi], av[vi][C - 1]);
             }
         }
     }
     // partial layout [chunk][batch][C][P][no], P = 2 (u, v) or 3 (u, v, tie)
     constexpr int P = TIES ? 3 : 2;
-    if (tid < no) {
+    // this thread's v index: v_{tid-1}, or v_{no-1} for thread 0 when it
+    // kept interval no
+    const int vt = tid > 0 ? tid - 1 : (last_extra ? no - 1 : -1);
 #pragma unroll
-        for (int vi = 0; vi < kBucketVG; ++vi)
+    for (int vi = 0; vi < kBucketVG; ++vi)
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
-                if (vi >= nv) continue;
-                float* pp = A.partial + ((chunk * A.batch + v0 + vi) * C + c) * P * no;
+        for (int c = 0; c < C; ++c) {
+            if (vi >= nv) continue;
+            float* pp = A.partial + ((chunk * A.batch + v0 + vi) * C + c) * P * no;
+            if (tid < no) {
                 pp[tid] = au[vi][c];
-                pp[no + tid] = av[vi][c];
                 if (TIES) pp[2 * no + tid] = at[TIES ? vi : 0][c];
             }
-    }
+            if (vt >= 0 && vt < no) pp[no + vt] = av[vi][c];
+        }
 }
 
 static size_t bucket_sorted_lds(int64_t no, int C, bool ties)

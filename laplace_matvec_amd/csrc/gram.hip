@@ -24,33 +24,24 @@
 // such Grams with weights D cos^2 psi, D cos psi sin psi, D sin^2 psi,
 // combined per entry with cos/sin of phi_i and phi_j.
 //
-//   lx_gram_bins : one workgroup per interval; its b-range in the sorted b
-//                  by bisection (k log n in total), fixed-order reduction.
-//   lx_gram_scan : one workgroup, the three scans, stats in original order.
+//   lx_gram_bins : per tile of the merged order of the sorted b and the
+//                  sorted a (b before an equal a, tiles of equal length found
+//                  by merge-path search), each interval's run of b summed
+//                  (sigma, p, q per weight set) by a segmented scan in
+//                  float64, a fixed order; the decay between neighbouring a
+//                  once per a; the tiles' first intervals left as records;
+//   lx_gram_scan : one workgroup: the tile records completed by a segmented
+//                  scan over the tiles, then S, P, Q over the intervals,
+//                  written as stats by original index;
 //   lx_gram_tile : 64 x 64 tiles of M in the original order, O(1) per entry.
 #include "lx_device.h"
 #include "lx_internal.h"
+#include "lx_merge.h"
 
 namespace lx {
 
-constexpr int kBinThreads = 256;
 constexpr int kGramScanThreads = 1024;
 constexpr int kGT = 64;  // tile edge
-
-__device__ __forceinline__ double block_sum_d(double x, double* sh)
-{
-    const int lane = lane_id();
-    const int w = (int)threadIdx.x / kWave;
-#pragma unroll
-    for (int d = kWave / 2; d > 0; d >>= 1) x += __shfl_down(x, d);
-    if (lane == 0) sh[w] = x;
-    __syncthreads();
-    double t = 0.0;
-#pragma unroll
-    for (int i = 0; i < kBinThreads / kWave; ++i) t += sh[i];
-    __syncthreads();
-    return t;
-}
 
 // Weight sets: one (D) for the plain operator; three for a phased one,
 // D cos^2 psi, D cos psi sin psi and D sin^2 psi, since
@@ -60,132 +51,424 @@ __device__ __forceinline__ double block_sum_d(double x, double* sh)
 template <int NW>
 constexpr int gram_stride() { return 1 + 3 * NW + (NW == 3 ? 2 : 0); }
 
-template <int NW>
-__global__ __launch_bounds__(kBinThreads) void lx_gram_bins(GramArgs A, double* __restrict__ sigma,
-                                                           double* __restrict__ p, double* __restrict__ q)
+// Scratch (doubles, 256-byte aligned regions):
+//   sigma [NW][n+1], p [NW][n], q [NW][n], mdec [n] (e^{-2(s_r - s_{r-1})/t}),
+//   st [n][SW] (stats by original index), head/tail [3 NW][tiles],
+//   split uint2 [tiles + 1]
+struct GramScratch {
+    double *sigma, *p, *q, *mdec, *st, *head, *tail;
+    uint2* split;
+    int64_t tiles;
+};
+
+static inline size_t al256g(size_t b) { return (b + 255) & ~(size_t)255; }
+
+static GramScratch gram_scratch_at(void* base, int64_t n, int64_t k, int nw)
 {
-    __shared__ double sh[kBinThreads / kWave];
-    const int64_t n = A.n, k = A.k;
-    const int64_t r = blockIdx.x;  // interval (s_{r-1}, s_r], r = 0..n
-    const int64_t lo = r == 0 ? 0 : upper_bound_f(A.sb, k, A.sa[r - 1]);
-    const int64_t hi = r == n ? k : upper_bound_f(A.sb, k, A.sa[r]);
-    const double right = r < n ? (double)A.sa[r] : 0.0;
-    const double left = r > 0 ? (double)A.sa[r - 1] : 0.0;
-    double sg[NW], pp[NW], qq[NW];
-#pragma unroll
-    for (int w = 0; w < NW; ++w) sg[w] = pp[w] = qq[w] = 0.0;
-    for (int64_t j = lo + threadIdx.x; j < hi; j += kBinThreads) {
-        const double d = (double)A.D[A.pb[j]];
-        double wt[NW];
-        if (NW == 3) {
-            const double c = A.cpsi_r[j], sn = A.spsi_r[j];
-            wt[0] = d * c * c;
-            wt[NW > 1 ? 1 : 0] = d * c * sn;
-            wt[NW - 1] = d * sn * sn;
-        } else {
-            wt[0] = d;
-        }
-        const double b = (double)A.sb[j];
-        const double er = r < n ? decay_dist(2.0 * (right - b), A.inv_t) : 0.0;
-        const double el = r > 0 ? decay_dist(2.0 * (b - left), A.inv_t) : 0.0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            sg[w] += wt[w];
-            pp[w] += wt[w] * er;
-            qq[w] += wt[w] * el;
-        }
-    }
+    const int sw = 1 + 3 * nw + (nw == 3 ? 2 : 0);
+    GramScratch g;
+    g.tiles = (n + k + kMergeTile - 1) / kMergeTile;
+    char* c = (char*)base;
+    g.sigma = (double*)c; c += al256g((size_t)nw * (n + 1) * 8);
+    g.p = (double*)c; c += al256g((size_t)nw * n * 8);
+    g.q = (double*)c; c += al256g((size_t)nw * n * 8);
+    g.mdec = (double*)c; c += al256g((size_t)n * 8);
+    g.st = (double*)c; c += al256g((size_t)n * sw * 8);
+    g.head = (double*)c; c += al256g((size_t)3 * nw * g.tiles * 8);
+    g.tail = (double*)c; c += al256g((size_t)3 * nw * g.tiles * 8);
+    g.split = (uint2*)c;
+    return g;
+}
+
+size_t gram_scratch_bytes(int64_t n, int64_t k, int nw)
+{
+    const int sw = 1 + 3 * nw + (nw == 3 ? 2 : 0);
+    const int64_t tiles = (n + k + kMergeTile - 1) / kMergeTile;
+    return al256g((size_t)nw * (n + 1) * 8) + 2 * al256g((size_t)nw * n * 8) + al256g((size_t)n * 8) +
+           al256g((size_t)n * sw * 8) + 2 * al256g((size_t)3 * nw * tiles * 8) + al256g((size_t)(tiles + 1) * 8);
+}
+
+// The split (b before it, a before it) of the merged order at tile
+// boundary t: b (sorted) goes before an equal a.
+__device__ __forceinline__ uint2 gram_split_at(const GramArgs& A, int64_t t)
+{
+    const int64_t total = A.n + A.k;
+    const int64_t d = t * kMergeTile < total ? t * kMergeTile : total;
+    const int64_t i = merge_search(A.sb, A.k, A.sa, A.n, d);
+    return make_uint2((uint32_t)i, (uint32_t)(d - i));
+}
+
+// Writes the sums of interval t (closed by anchor a_t; t = n: the run above
+// every anchor): sigma_t, p_t (t < n), q_{t-1} (t > 0).
+template <int NW>
+__device__ __forceinline__ void gram_put(const GramScratch& G, int64_t n, int64_t t, const double* v)
+{
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        const double a1 = block_sum_d(sg[w], sh);
-        const double a2 = block_sum_d(pp[w], sh);
-        const double a3 = block_sum_d(qq[w], sh);
-        if (threadIdx.x == 0) {
-            sigma[w * (n + 1) + r] = a1;
-            if (r < n) p[w * n + r] = a2;
-            if (r > 0) q[w * n + r - 1] = a3;
-        }
+        G.sigma[w * (n + 1) + t] = v[3 * w];
+        if (t < n) G.p[w * n + t] = v[3 * w + 1];
+        if (t > 0) G.q[w * n + t - 1] = v[3 * w + 2];
     }
 }
 
 template <int NW>
-__global__ __launch_bounds__(kGramScanThreads) void lx_gram_scan(GramArgs A, const double* __restrict__ sigma,
-                                                                const double* __restrict__ p,
-                                                                const double* __restrict__ q,
-                                                                double* __restrict__ st)
+__global__ __launch_bounds__(kMergeThreads) void lx_gram_bins(GramArgs A, GramScratch G)
+{
+    constexpr int K = 3 * NW;  // per weight set: sigma, p, q
+    __shared__ float s_b[kMergeTile];
+    __shared__ float s_a[kMergeTile];
+    __shared__ Aff<double> sh[2 * K * kMergeWaves];
+    const int tid = threadIdx.x;
+    const int64_t tile = blockIdx.x;
+    const int64_t n = A.n;
+    const double it2 = 2.0 * A.inv_t;  // e^{-2 d / t}
+    __shared__ uint2 s_split[2];
+    // this tile's boundaries (recorded for the carry step)
+    if (tid < 2) {
+        const uint2 sp = gram_split_at(A, tile + tid);
+        s_split[tid] = sp;
+        if (tid == 0) G.split[tile] = sp;
+        if (tid == 1 && tile + 1 == G.tiles) G.split[tile + 1] = sp;
+    }
+    __syncthreads();
+    const uint2 b0 = s_split[0], b1 = s_split[1];
+    const int64_t j0 = b0.x, r0 = b0.y;
+    const int nb = (int)(b1.x - b0.x), na = (int)(b1.y - b0.y);
+    const int len = nb + na;
+    for (int j = tid; j < nb; j += kMergeThreads) s_b[j] = A.sb[j0 + j];
+    for (int j = tid; j < na; j += kMergeThreads) s_a[j] = A.sa[r0 + j];
+    const float left_sent = r0 > 0 ? A.sa[r0 - 1] : 0.f;
+    const float right_sent = r0 + na < n ? A.sa[r0 + na] : 0.f;
+    __syncthreads();
+
+    const int dk = tid * kMergeItems < len ? tid * kMergeItems : len;
+    int ib = (int)merge_search(s_b, nb, s_a, na, dk);
+    int ia = dk - ib;
+    double al[kMergeItems], be[kMergeItems];
+    uint32_t idx[kMergeItems];  // b: its rank in sorted b; a: its rank t
+    uint32_t is_b = 0, is_a = 0;
+#pragma unroll
+    for (int j = 0; j < kMergeItems; ++j) {
+        al[j] = be[j] = 0.0;
+        idx[j] = 0;
+        if (dk + j >= len) continue;
+        const bool take_b = ib < nb && (ia >= na || s_b[ib] <= s_a[ia]);
+        const int64_t t = r0 + ia;  // anchors a before this item
+        if (take_b) {
+            const float bv = s_b[ib];
+            const float right = ia < na ? s_a[ia] : right_sent;
+            const float left = ia > 0 ? s_a[ia - 1] : left_sent;
+            al[j] = t < n ? decay(bv, right, it2) : 0.0;
+            be[j] = t > 0 ? decay(left, bv, it2) : 0.0;
+            idx[j] = (uint32_t)(j0 + ib);
+            is_b |= 1u << j;
+            ++ib;
+        } else {
+            const float right = s_a[ia];
+            const float left = ia > 0 ? s_a[ia - 1] : left_sent;
+            G.mdec[t] = t > 0 ? decay(left, right, it2) : 0.0;  // each a once
+            idx[j] = (uint32_t)t;
+            is_a |= 1u << j;
+            ++ia;
+        }
+    }
+    // the weights of this thread's b (D through the permutation of b)
+    double wv[kMergeItems][NW];
+#pragma unroll
+    for (int j = 0; j < kMergeItems; ++j) {
+        const uint32_t r = (is_b >> j) & 1u ? idx[j] : 0u;
+        const double d = (double)A.D[A.pb[r]];
+        if (NW == 3) {
+            const double c = A.cpsi_r[r], sn = A.spsi_r[r];
+            wv[j][0] = d * c * c;
+            wv[j][NW > 1 ? 1 : 0] = d * c * sn;
+            wv[j][NW - 1] = d * sn * sn;
+        } else {
+            wv[j][0] = d;
+        }
+    }
+    double run[K], head[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) run[k] = head[k] = 0.0;
+    const uint32_t first_j = is_a ? (uint32_t)__builtin_ctz(is_a) : 0u;
+#pragma unroll
+    for (int j = 0; j < kMergeItems; ++j) {
+        if ((is_b >> j) & 1u) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                run[3 * w] += wv[j][w];
+                run[3 * w + 1] = fma(al[j], wv[j][w], run[3 * w + 1]);
+                run[3 * w + 2] = fma(be[j], wv[j][w], run[3 * w + 2]);
+            }
+        } else if ((is_a >> j) & 1u) {
+            if ((uint32_t)j == first_j) {
+#pragma unroll
+                for (int k = 0; k < K; ++k) head[k] = run[k];
+            } else {
+                gram_put<NW>(G, n, idx[j], run);
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) run[k] = 0.0;
+        }
+    }
+    double mex, vex[K], vtot[K];
+    block_segscan<K>(is_a ? 0.0 : 1.0, run, sh, 0, mex, vex, vtot);
+    if (is_a) {
+        double tot[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) tot[k] = vex[k] + head[k];
+        if (mex != 0.0) {
+            // the tile's first anchor: earlier tiles may add to its interval
+#pragma unroll
+            for (int k = 0; k < K; ++k) G.head[k * G.tiles + tile] = tot[k];
+        } else {
+            gram_put<NW>(G, n, idx[first_j], tot);
+        }
+    }
+    if (tid == 0) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) G.tail[k * G.tiles + tile] = vtot[k];
+    }
+}
+
+// One workgroup: first the tiles' first intervals are completed (for each
+// of the 3 NW sums, a segmented scan over the tiles in chunks per thread,
+// thread 0 writing the run above the last anchor: sigma_n and q_{n-1}),
+// then S, P and Q over the intervals, written as stats by original index.
+// Each thread takes rounds of kGramRun consecutive ranks with every load of
+// a round issued before any is used.
+constexpr int kGramRun = 8;
+
+template <int NW>
+__global__ __launch_bounds__(kGramScanThreads) void lx_gram_scan(GramArgs A, GramScratch G)
 {
     __shared__ Aff<double> sh[kGramScanThreads / kWave];
     constexpr int SW = gram_stride<NW>();
-    const int64_t n = A.n;
-    const float* s = A.sa;
-    const int64_t per = (n + kGramScanThreads - 1) / kGramScanThreads;
-    int64_t r0 = (int64_t)threadIdx.x * per;
-    if (r0 > n) r0 = n;
-    int64_t r1 = r0 + per;
-    if (r1 > n) r1 = n;
-    for (int64_t r = r0; r < r1; ++r) {
-        double* o = st + (int64_t)A.pa[r] * SW;
-        o[0] = (double)s[r];
-        if (NW == 3) {
-            o[SW - 2] = A.cphi_r[r];
-            o[SW - 1] = A.sphi_r[r];
+    const int tid = threadIdx.x;
+    const int64_t n = A.n, T = G.tiles;
+
+    // ---- tile carries
+    {
+        const int64_t per = (T + kGramScanThreads - 1) / kGramScanThreads;
+        int64_t t0 = (int64_t)tid * per;
+        if (t0 > T) t0 = T;
+        int64_t t1 = t0 + per;
+        if (t1 > T) t1 = T;
+#pragma unroll 1
+        for (int k = 0; k < 3 * NW; ++k) {
+            const int w = k / 3, kind = k % 3;
+            const double* hd = G.head + k * T;
+            const double* tl = G.tail + k * T;
+            Aff<double> f = aff_identity<double>();
+            for (int64_t t = t0; t < t1; ++t)
+                f = compose(f, Aff<double>{G.split[t + 1].y > G.split[t].y ? 0.0 : 1.0, tl[t]});
+            Aff<double> tot;
+            double c = block_exscan_up<double, kGramScanThreads / kWave>(f, sh, tot).v;
+            for (int64_t t = t0; t < t1; ++t) {
+                const uint32_t r = G.split[t].y;
+                if (G.split[t + 1].y > r) {
+                    const double v = c + hd[t];
+                    if (kind == 0) G.sigma[w * (n + 1) + r] = v;
+                    else if (kind == 1) G.p[w * n + r] = v;
+                    else if (r > 0) G.q[w * n + r - 1] = v;
+                    c = tl[t];
+                } else {
+                    c += tl[t];
+                }
+            }
+            if (tid == 0) {
+                if (kind == 0) G.sigma[w * (n + 1) + n] = tot.v;
+                else if (kind == 2) G.q[w * n + n - 1] = tot.v;
+            }
         }
     }
+    __syncthreads();  // global writes above are read below by other threads
+    __threadfence_block();
+
+    // ---- scans over the intervals, in rounds of kGramScanThreads * kGramRun ranks
+    constexpr int64_t kRound = (int64_t)kGramScanThreads * kGramRun;
+    const float* s = A.sa;
+    double* st = G.st;
 #pragma unroll 1
     for (int w = 0; w < NW; ++w) {
-        const double* sg = sigma + w * (n + 1);
-        const double* pw = p + w * n;
-        const double* qw = q + w * n;
-        // forward: S (multiplier 1) and P (multiplier e^{-2 gap}); rank 0 starts both
-        Aff<double> S = aff_identity<double>(), P = aff_identity<double>();
-        for (int64_t r = r0; r < r1; ++r) {
-            const double m = r > 0 ? decay_dist(2.0 * ((double)s[r] - (double)s[r - 1]), A.inv_t) : 0.0;
-            S = compose(S, Aff<double>{1.0, sg[r]});
-            P = compose(P, Aff<double>{m, pw[r]});
+        const double* sg = G.sigma + w * (n + 1);
+        const double* pw = G.p + w * n;
+        const double* qw = G.q + w * n;
+        double carS = 0.0, carP = 0.0;
+#pragma unroll 1
+        for (int64_t base = 0; base < n; base += kRound) {
+            const int64_t r0 = base + (int64_t)tid * kGramRun;
+            double vs[kGramRun], vp[kGramRun], m[kGramRun];
+#pragma unroll
+            for (int i = 0; i < kGramRun; ++i) {
+                const int64_t r = r0 + i;
+                const bool ok = r < n;
+                vs[i] = ok ? sg[r] : 0.0;
+                vp[i] = ok ? pw[r] : 0.0;
+                m[i] = ok ? G.mdec[r] : 1.0;
+            }
+            Aff<double> S = aff_identity<double>(), P = aff_identity<double>();
+#pragma unroll
+            for (int i = 0; i < kGramRun; ++i) {
+                S = compose(S, Aff<double>{1.0, vs[i]});
+                P = compose(P, Aff<double>{m[i], vp[i]});
+            }
+            Aff<double> totS, totP;
+            const Aff<double> xS = block_exscan_up<double, kGramScanThreads / kWave>(S, sh, totS);
+            const Aff<double> xP = block_exscan_up<double, kGramScanThreads / kWave>(P, sh, totP);
+            double runS = xS.m * carS + xS.v, runP = xP.m * carP + xP.v;
+            carS = totS.m * carS + totS.v;
+            carP = totP.m * carP + totP.v;
+#pragma unroll
+            for (int i = 0; i < kGramRun; ++i) {
+                const int64_t r = r0 + i;
+                runS += vs[i];
+                runP = m[i] * runP + vp[i];
+                if (r < n) {
+                    double* o = st + (int64_t)A.pa[r] * SW;
+                    o[1 + 3 * w] = runP;
+                    o[2 + 3 * w] = runS;
+                    if (w == 0) {
+                        o[0] = (double)s[r];
+                        if (NW == 3) {
+                            o[SW - 2] = A.cphi_r[r];
+                            o[SW - 1] = A.sphi_r[r];
+                        }
+                    }
+                }
+            }
         }
-        Aff<double> tot;
-        double runS = block_exscan_up<double, kGramScanThreads / kWave>(S, sh, tot).v;
-        double runP = block_exscan_up<double, kGramScanThreads / kWave>(P, sh, tot).v;
-        for (int64_t r = r0; r < r1; ++r) {
-            const double m = r > 0 ? decay_dist(2.0 * ((double)s[r] - (double)s[r - 1]), A.inv_t) : 0.0;
-            runS += sg[r];
-            runP = m * runP + pw[r];
-            double* o = st + (int64_t)A.pa[r] * SW + 1 + 3 * w;
-            o[0] = runP;
-            o[1] = runS;
-        }
-        Aff<double> Q = aff_identity<double>();
-        for (int64_t r = r1 - 1; r >= r0; --r) {
-            const double m = r + 1 < n ? decay_dist(2.0 * ((double)s[r + 1] - (double)s[r]), A.inv_t) : 0.0;
-            Q = compose(Q, Aff<double>{m, qw[r]});
-        }
-        double runQ = block_exscan_down<double, kGramScanThreads / kWave>(Q, sh, tot).v;
-        for (int64_t r = r1 - 1; r >= r0; --r) {
-            const double m = r + 1 < n ? decay_dist(2.0 * ((double)s[r + 1] - (double)s[r]), A.inv_t) : 0.0;
-            runQ = m * runQ + qw[r];
-            st[(int64_t)A.pa[r] * SW + 3 + 3 * w] = runQ;
+        // backward: Q_r = e^{-2 (s_{r+1} - s_r)} Q_{r+1} + q_r, rounds from the top
+        double carQ = 0.0;
+        const int64_t rounds = (n + kRound - 1) / kRound;
+#pragma unroll 1
+        for (int64_t rd = rounds - 1; rd >= 0; --rd) {
+            const int64_t r0 = rd * kRound + (int64_t)tid * kGramRun;
+            double vq[kGramRun], m1[kGramRun];
+#pragma unroll
+            for (int i = 0; i < kGramRun; ++i) {
+                const int64_t r = r0 + i;
+                vq[i] = r < n ? qw[r] : 0.0;
+                m1[i] = r + 1 < n ? G.mdec[r + 1] : (r + 1 == n ? 0.0 : 1.0);
+            }
+            Aff<double> Q = aff_identity<double>();
+#pragma unroll
+            for (int i = kGramRun - 1; i >= 0; --i) Q = compose(Q, Aff<double>{m1[i], vq[i]});
+            Aff<double> totQ;
+            const Aff<double> xQ = block_exscan_down<double, kGramScanThreads / kWave>(Q, sh, totQ);
+            double runQ = xQ.m * carQ + xQ.v;
+            carQ = totQ.m * carQ + totQ.v;
+#pragma unroll
+            for (int i = kGramRun - 1; i >= 0; --i) {
+                const int64_t r = r0 + i;
+                runQ = m1[i] * runQ + vq[i];
+                if (r < n) st[(int64_t)A.pa[r] * SW + 3 + 3 * w] = runQ;
+            }
         }
     }
 }
 
+// Tiles of M, 64 x 64 entries in the original order.  Thread (column jj,
+// row group) computes column jj of 16 rows and stores a wave's 64 columns
+// of one row at once.  With lo / hi the entry's smaller / larger anchor,
+//   M = e^{-(hi - lo)/t} (P_lo + (S_hi - S_lo) + Q_hi)
+// (weight sets combined with the cos/sin of phi when phased).  When the
+// tile's anchors span at most 600 t, the decay is split around the tile's
+// centre c into per-anchor factors, e^{-(hi - lo)/t} = E+_lo E-_hi with
+// E+ = e^{(a - c)/t} and E- = e^{-(a - c)/t}: one exp per anchor instead of
+// one per entry.  (The sum keeps S_hi - S_lo as one difference, exact for
+// equal anchors, so small entries next to a large S keep their precision.)
+// Otherwise, and at t = 0, each entry takes its own decay.
 template <int NW>
 __global__ __launch_bounds__(256) void lx_gram_tile(const double* __restrict__ st, int64_t n, double inv_t,
                                                    float* __restrict__ M)
 {
     constexpr int SW = gram_stride<NW>();
+    constexpr int FW = SW + 2;  // a, E+, E-, then the stats after a: (P, S, Q) per set, (cos, sin)
     __shared__ double rs[kGT][SW];
     __shared__ double cs[kGT][SW];
+    __shared__ double fr[2][kGT][FW];  // [rows, columns][anchor][term]
+    __shared__ float sred[4][2];
+    const int tid = threadIdx.x;
     const int64_t i0 = (int64_t)blockIdx.y * kGT, j0 = (int64_t)blockIdx.x * kGT;
-    for (int t = threadIdx.x; t < kGT * SW; t += 256) {
+    for (int t = tid; t < kGT * SW; t += 256) {
         const int e = t / SW, f = t % SW;
         rs[e][f] = (i0 + e < n) ? st[(i0 + e) * SW + f] : 0.0;
         cs[e][f] = (j0 + e < n) ? st[(j0 + e) * SW + f] : 0.0;
     }
     __syncthreads();
-    const int jj = threadIdx.x % kGT;
+    // the tile's anchor range (valid rows and columns only), for the centre
+    {
+        float mn = INFINITY, mx = -INFINITY;
+        if (tid < 2 * kGT) {
+            const int e = tid % kGT;
+            const bool row = tid < kGT;
+            if ((row ? i0 : j0) + e < n) {
+                const float v = (float)(row ? rs[e][0] : cs[e][0]);
+                mn = mx = v;
+            }
+        }
+        for (int d = 32; d > 0; d >>= 1) {
+            mn = fminf(mn, __shfl_xor(mn, d));
+            mx = fmaxf(mx, __shfl_xor(mx, d));
+        }
+        if (lane_id() == 0) {
+            sred[tid / kWave][0] = mn;
+            sred[tid / kWave][1] = mx;
+        }
+    }
+    __syncthreads();
+    const double lo_a = fmin(sred[0][0], sred[1][0]), hi_a = fmax(sred[0][1], sred[1][1]);
+    const double centre = 0.5 * (lo_a + hi_a);
+    // factors only when every |a - c|/t stays far from overflow (and t > 0)
+    const bool factored = inv_t <= 1.0e300 && (hi_a - lo_a) * inv_t <= 600.0;
+    const int jj = tid % kGT;
     const int64_t j = j0 + jj;
+    if (factored) {
+        if (tid < 2 * kGT) {
+            const int e = tid % kGT, side = tid / kGT;
+            const double* x = side == 0 ? rs[e] : cs[e];
+            double* f = fr[side][e];
+            const double xe = (x[0] - centre) * inv_t;
+            f[0] = x[0];
+            f[1] = exp(xe);
+            f[2] = exp(-xe);
+#pragma unroll
+            for (int q = 1; q < SW; ++q) f[2 + q] = x[q];
+        }
+        __syncthreads();
+        double cf[FW];
+#pragma unroll
+        for (int q = 0; q < FW; ++q) cf[q] = fr[1][jj][q];
 #pragma unroll 4
-    for (int ii = threadIdx.x / kGT; ii < kGT; ii += 256 / kGT) {
+        for (int ii = tid / kGT; ii < kGT; ii += 256 / kGT) {
+            const int64_t i = i0 + ii;
+            const double* rf = fr[0][ii];  // the same row for the whole wave: broadcast reads
+            const bool row_first = rf[0] <= cf[0];
+            // stats of lo and hi: P, S, Q of weight set w at 3 + 3 w .. 5 + 3 w
+            double g[NW];
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const double p_lo = row_first ? rf[3 + 3 * w] : cf[3 + 3 * w];
+                const double s_lo = row_first ? rf[4 + 3 * w] : cf[4 + 3 * w];
+                const double s_hi = row_first ? cf[4 + 3 * w] : rf[4 + 3 * w];
+                const double q_hi = row_first ? cf[5 + 3 * w] : rf[5 + 3 * w];
+                g[w] = p_lo + (s_hi - s_lo) + q_hi;
+            }
+            const double dec = row_first ? rf[1] * cf[2] : cf[1] * rf[2];
+            double val;
+            if (NW == 3) {
+                const double ci = rf[FW - 2], si = rf[FW - 1], cj = cf[FW - 2], sj = cf[FW - 1];
+                val = ci * cj * g[0] + (ci * sj + si * cj) * g[NW > 1 ? 1 : 0] + si * sj * g[NW - 1];
+            } else {
+                val = g[0];
+            }
+            if (i < n && j < n) M[i * n + j] = (float)(dec * val);
+        }
+        return;
+    }
+#pragma unroll 4
+    for (int ii = tid / kGT; ii < kGT; ii += 256 / kGT) {
         const int64_t i = i0 + ii;
         if (i < n && j < n) {
             // lo: the smaller anchor (equal anchors carry equal stats)
@@ -207,30 +490,20 @@ __global__ __launch_bounds__(256) void lx_gram_tile(const double* __restrict__ s
     }
 }
 
-size_t gram_scratch_bytes(int64_t n, int nw)
-{
-    const int sw = 1 + 3 * nw + (nw == 3 ? 2 : 0);
-    return (size_t)(nw * ((n + 1) + 2 * n) + sw * n + 64) * 8;
-}
-
 template <int NW>
 static hipError_t gram_launch_t(const GramArgs& a, hipStream_t s)
 {
-    const int64_t n = a.n;
-    double* sigma = a.stats;
-    double* p = sigma + NW * (n + 1);
-    double* q = p + NW * n;
-    double* st = q + NW * n;
-    LX_LAUNCH("gram_bins", s, (lx_gram_bins<NW><<<(unsigned)(n + 1), kBinThreads, 0, s>>>(a, sigma, p, q)));
-    LX_LAUNCH("gram_scan", s, (lx_gram_scan<NW><<<1, kGramScanThreads, 0, s>>>(a, sigma, p, q, st)));
-    const unsigned nb = (unsigned)((n + kGT - 1) / kGT);
-    LX_LAUNCH("gram_tile", s, (lx_gram_tile<NW><<<dim3(nb, nb), 256, 0, s>>>(st, n, a.inv_t, a.M)));
+    const GramScratch G = gram_scratch_at(a.stats, a.n, a.k, NW);
+    LX_LAUNCH("gram_bins", s, (lx_gram_bins<NW><<<(unsigned)G.tiles, kMergeThreads, 0, s>>>(a, G)));
+    LX_LAUNCH("gram_scan", s, (lx_gram_scan<NW><<<1, kGramScanThreads, 0, s>>>(a, G)));
+    const unsigned nb = (unsigned)((a.n + kGT - 1) / kGT);
+    LX_LAUNCH("gram_tile", s, (lx_gram_tile<NW><<<dim3(nb, nb), 256, 0, s>>>(G.st, a.n, a.inv_t, a.M)));
     return hipSuccess;
 }
 
 hipError_t gram_launch(const GramArgs& a, hipStream_t s)
 {
-    if (a.n <= 0) return hipSuccess;
+    if (a.n <= 0 || a.k <= 0) return hipSuccess;
     return a.cpsi_r ? gram_launch_t<3>(a, s) : gram_launch_t<1>(a, s);
 }
 

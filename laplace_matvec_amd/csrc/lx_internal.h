@@ -307,6 +307,7 @@ struct SmallSymArgs {
     const float* phi = nullptr;            // phases (both or neither), original order
     const float* psi = nullptr;
     const float* x = nullptr;              // [batch][n], or null: plan only
+    float* x_keep = nullptr;               // [batch][n] copy of x (original order), or null
     float* y = nullptr;                    // [batch][n]
     float* sa = nullptr;                   // sorted anchors [n]
     uint32_t* perm = nullptr;              // rank -> original index [n]
@@ -334,7 +335,7 @@ struct GramArgs {
     double* stats = nullptr;        // scratch: see gram.hip
     float* M = nullptr;             // [n][n]
 };
-size_t gram_scratch_bytes(int64_t n, int weight_sets);
+size_t gram_scratch_bytes(int64_t n, int64_t k, int weight_sets);
 hipError_t gram_launch(const GramArgs& a, hipStream_t s);
 
 }  // namespace lx

@@ -30,14 +30,11 @@
 // Every u_t and v_t is written exactly once; nothing needs clearing first.
 #include "lx_device.h"
 #include "lx_internal.h"
+#include "lx_merge.h"
 
 namespace lx {
 
-constexpr int kMergeThreads = 256;
-constexpr int kMergeWaves = kMergeThreads / kWave;
-constexpr int kMergeItems = 8;
-constexpr int kMergeTile = kMergeThreads * kMergeItems;  // merged items per tile
-constexpr int kMergeVG = 8;                              // vectors per workgroup (max)
+constexpr int kMergeVG = 8;  // vectors per workgroup (max)
 
 int64_t merge_tiles(int64_t n_in, int64_t n_out) { return (n_in + n_out + kMergeTile - 1) / kMergeTile; }
 
@@ -49,21 +46,6 @@ size_t merge_ws_bytes(int64_t n_in, int64_t n_out, int64_t batch, int channels)
     return al256m((size_t)(tiles + 1) * sizeof(uint2)) + 2 * al256m((size_t)channels * batch * tiles * 2 * 8);
 }
 
-// Inputs among the first d merged items: the least i with input i not
-// before output d - i - 1 (input i goes first iff s_in[i] <= s_out[d-i-1]).
-__device__ __forceinline__ int64_t merge_search(const float* __restrict__ si, int64_t ni, const float* __restrict__ so,
-                                                int64_t no, int64_t d)
-{
-    int64_t lo = d > no ? d - no : 0;
-    int64_t hi = d < ni ? d : ni;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (si[mid] <= so[d - mid - 1]) lo = mid + 1;
-        else hi = mid;
-    }
-    return lo;
-}
-
 __global__ __launch_bounds__(256) void lx_merge_split(MergeArgs A)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -72,44 +54,6 @@ __global__ __launch_bounds__(256) void lx_merge_split(MergeArgs A)
     const int64_t d = k * kMergeTile < total ? k * kMergeTile : total;
     const int64_t i = merge_search(A.s_in, A.n_in, A.s_out, A.n_out, d);
     A.split[k] = make_uint2((uint32_t)i, (uint32_t)(d - i));
-}
-
-// Exclusive segmented scan of K values per thread across the workgroup, in
-// thread order: a thread holding an output (m = 0) restarts the sum.  The
-// elements are the affine maps t -> m t + v (m 0 or 1, exact), so the wave
-// scans of the float64 composites serve.  Returns through vex the sum
-// entering this thread, through mex 1 if no earlier thread holds an output,
-// through vtot the sum after the workgroup's last output (or of everything).
-// sh: [2][K][kMergeWaves], used in turns by `parity`.
-template <int K>
-__device__ __forceinline__ void block_segscan(double m, const double (&v)[K], Aff<double>* sh, int parity, double& mex,
-                                              double (&vex)[K], double (&vtot)[K])
-{
-    const int lane = lane_id();
-    const int w = (int)threadIdx.x / kWave;
-    Aff<double>* buf = sh + parity * (K * kMergeWaves);
-    Aff<double> ex[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const Aff<double> inc = wave_scan_up(Aff<double>{m, v[k]});
-        ex[k] = wave_shift_up(inc);
-        if (lane == kWave - 1) buf[k * kMergeWaves + w] = inc;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        Aff<double> pre = aff_identity<double>(), tot = aff_identity<double>();
-#pragma unroll
-        for (int i = 0; i < kMergeWaves; ++i) {
-            const Aff<double> a = buf[k * kMergeWaves + i];
-            if (i < w) pre = compose(pre, a);
-            tot = compose(tot, a);
-        }
-        const Aff<double> r = compose(pre, ex[k]);
-        vex[k] = r.v;
-        if (k == 0) mex = r.m;
-        vtot[k] = tot.v;
-    }
 }
 
 template <int C>

@@ -137,6 +137,9 @@ __global__ __launch_bounds__(kSmallThreads) void lx_small_sym(SmallSymArgs A)
     }
     if (__any(bad) && lane == 0) atomicOr(A.flag, 1u);
     if (A.x == nullptr) return;  // uniform: a plan without a product
+    // the plan's own copy of x (original order) for a later backward
+    if (A.x_keep)
+        for (int64_t i = tid; i < (int64_t)A.batch * n; i += kSmallThreads) A.x_keep[i] = A.x[i];
 
     // decays between neighbouring ranks; 0 before rank 0 and from rank n on
     double e[kSmallItems + 1];
