@@ -272,6 +272,9 @@ struct laplex_plan_s {
     // permutations (rank -> original index), made from the records on demand
     uint32_t* pa = nullptr;
     uint32_t* pb = nullptr;
+    // Gram: first sorted-b position of every interval of the sorted a, made
+    // on the first gram call
+    uint32_t* gbound = nullptr;
     // copies in original order (general only)
     float* a0 = nullptr;
     float* b0 = nullptr;
@@ -1433,6 +1436,12 @@ laplex_status laplex_gram(laplex_plan p, const float* D, float* M, void* stream)
     note_stream(p, s);
     LX_TRY(ensure_perm(p, 0, s), "permutation of a");
     LX_TRY(ensure_perm(p, 1, s), "permutation of b");
+    if (!p->gbound) {
+        void* gb = nullptr;
+        LX_TRY(plan_alloc(p, &gb, (size_t)(p->n + 2) * 4, s), "alloc gram bounds");
+        LX_TRY(lx::gram_bounds_launch(p->sa, p->n, p->sb, p->k, (uint32_t*)gb, s), "gram bounds");
+        p->gbound = (uint32_t*)gb;
+    }
     LX_TRY(ensure_ws(p, lx::gram_scratch_bytes(p->n, p->k, p->phased ? 3 : 1), s), "workspace");
     lx::GramArgs G;
     G.n = p->n;
@@ -1443,6 +1452,7 @@ laplex_status laplex_gram(laplex_plan p, const float* D, float* M, void* stream)
     G.sb = p->sb;
     G.pb = p->pb;
     G.D = D;
+    G.bound = p->gbound;
     if (p->phased) {
         G.cphi_r = p->cphi;
         G.sphi_r = p->sphi;

@@ -24,23 +24,20 @@
 // such Grams with weights D cos^2 psi, D cos psi sin psi, D sin^2 psi,
 // combined per entry with cos/sin of phi_i and phi_j.
 //
-//   lx_gram_bins : per tile of the merged order of the sorted b and the
-//                  sorted a (b before an equal a, tiles of equal length found
-//                  by merge-path search), each interval's run of b summed
-//                  (sigma, p, q per weight set) by a segmented scan in
-//                  float64, a fixed order; the decay between neighbouring a
-//                  once per a; the tiles' first intervals left as records;
-//   lx_gram_scan : one workgroup: the tile records completed by a segmented
-//                  scan over the tiles, then S, P, Q over the intervals,
-//                  written as stats by original index;
-//   lx_gram_tile : 64 x 64 tiles of M in the original order, O(1) per entry.
+//   lx_gram_bounds : once per plan, the first sorted-b position of every
+//                    interval (bisection of each a over the sorted b);
+//   lx_gram_bins   : one workgroup per interval: its run of sorted b summed
+//                    (sigma, p, q per weight set) in float64 and a fixed
+//                    order, and the decay between the interval's two a;
+//   lx_gram_scan   : one workgroup: S, P, Q over the intervals, written as
+//                    stats by original index;
+//   lx_gram_tile   : 64 x 64 tiles of M in the original order, O(1) per entry.
 #include "lx_device.h"
 #include "lx_internal.h"
-#include "lx_merge.h"
 
 namespace lx {
 
-constexpr int kGramScanThreads = 1024;
+constexpr int kGramScanThreads = 256;
 constexpr int kGT = 64;  // tile edge
 
 // Weight sets: one (D) for the plain operator; three for a phased one,
@@ -53,191 +50,145 @@ constexpr int gram_stride() { return 1 + 3 * NW + (NW == 3 ? 2 : 0); }
 
 // Scratch (doubles, 256-byte aligned regions):
 //   sigma [NW][n+1], p [NW][n], q [NW][n], mdec [n] (e^{-2(s_r - s_{r-1})/t}),
-//   st [n][SW] (stats by original index), head/tail [3 NW][tiles],
-//   split uint2 [tiles + 1]
+//   st [n][SW] (stats by original index)
 struct GramScratch {
-    double *sigma, *p, *q, *mdec, *st, *head, *tail;
-    uint2* split;
-    int64_t tiles;
+    double *sigma, *p, *q, *mdec, *st;
 };
 
 static inline size_t al256g(size_t b) { return (b + 255) & ~(size_t)255; }
 
-static GramScratch gram_scratch_at(void* base, int64_t n, int64_t k, int nw)
+static GramScratch gram_scratch_at(void* base, int64_t n, int nw)
 {
-    const int sw = 1 + 3 * nw + (nw == 3 ? 2 : 0);
     GramScratch g;
-    g.tiles = (n + k + kMergeTile - 1) / kMergeTile;
     char* c = (char*)base;
     g.sigma = (double*)c; c += al256g((size_t)nw * (n + 1) * 8);
     g.p = (double*)c; c += al256g((size_t)nw * n * 8);
     g.q = (double*)c; c += al256g((size_t)nw * n * 8);
     g.mdec = (double*)c; c += al256g((size_t)n * 8);
-    g.st = (double*)c; c += al256g((size_t)n * sw * 8);
-    g.head = (double*)c; c += al256g((size_t)3 * nw * g.tiles * 8);
-    g.tail = (double*)c; c += al256g((size_t)3 * nw * g.tiles * 8);
-    g.split = (uint2*)c;
+    g.st = (double*)c;
     return g;
 }
 
 size_t gram_scratch_bytes(int64_t n, int64_t k, int nw)
 {
+    (void)k;
     const int sw = 1 + 3 * nw + (nw == 3 ? 2 : 0);
-    const int64_t tiles = (n + k + kMergeTile - 1) / kMergeTile;
     return al256g((size_t)nw * (n + 1) * 8) + 2 * al256g((size_t)nw * n * 8) + al256g((size_t)n * 8) +
-           al256g((size_t)n * sw * 8) + 2 * al256g((size_t)3 * nw * tiles * 8) + al256g((size_t)(tiles + 1) * 8);
+           al256g((size_t)n * sw * 8);
 }
 
-// The split (b before it, a before it) of the merged order at tile
-// boundary t: b (sorted) goes before an equal a.
-__device__ __forceinline__ uint2 gram_split_at(const GramArgs& A, int64_t t)
+// bound[r] = #{l : b_l <= s_{r-1}} for r = 1 .. n, bound[0] = 0,
+// bound[n+1] = k: interval r (b in (s_{r-1}, s_r]) is sorted b [bound[r], bound[r+1]).
+__global__ __launch_bounds__(256) void lx_gram_bounds(const float* __restrict__ sa, int64_t n,
+                                                     const float* __restrict__ sb, int64_t k,
+                                                     uint32_t* __restrict__ bound)
 {
-    const int64_t total = A.n + A.k;
-    const int64_t d = t * kMergeTile < total ? t * kMergeTile : total;
-    const int64_t i = merge_search(A.sb, A.k, A.sa, A.n, d);
-    return make_uint2((uint32_t)i, (uint32_t)(d - i));
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r > n + 1) return;
+    bound[r] = (uint32_t)(r == 0 ? 0 : (r == n + 1 ? k : upper_bound_f(sb, k, sa[r - 1])));
 }
 
-// Writes the sums of interval t (closed by anchor a_t; t = n: the run above
-// every anchor): sigma_t, p_t (t < n), q_{t-1} (t > 0).
-template <int NW>
-__device__ __forceinline__ void gram_put(const GramScratch& G, int64_t n, int64_t t, const double* v)
+hipError_t gram_bounds_launch(const float* sa, int64_t n, const float* sb, int64_t k, uint32_t* bound, hipStream_t s)
 {
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        G.sigma[w * (n + 1) + t] = v[3 * w];
-        if (t < n) G.p[w * n + t] = v[3 * w + 1];
-        if (t > 0) G.q[w * n + t - 1] = v[3 * w + 2];
-    }
+    if (n <= 0 || k <= 0) return hipSuccess;
+    LX_LAUNCH("gram_bounds", s, (lx_gram_bounds<<<(unsigned)((n + 2 + 255) / 256), 256, 0, s>>>(sa, n, sb, k, bound)));
+    return hipSuccess;
 }
 
+// Interval r: thread tid takes sorted b positions lo + tid, lo + tid + 256,
+// ... in rounds of kBinLoads with every load of a round in flight before any
+// is used; the per-thread sums are folded over the workgroup in a fixed
+// order (wave shuffles, then the waves in order).
+constexpr int kBinThreads = 256;
+constexpr int kBinLoads = 4;
+
 template <int NW>
-__global__ __launch_bounds__(kMergeThreads) void lx_gram_bins(GramArgs A, GramScratch G)
+__global__ __launch_bounds__(kBinThreads) void lx_gram_bins(GramArgs A, GramScratch G)
 {
     constexpr int K = 3 * NW;  // per weight set: sigma, p, q
-    __shared__ float s_b[kMergeTile];
-    __shared__ float s_a[kMergeTile];
-    __shared__ Aff<double> sh[2 * K * kMergeWaves];
+    __shared__ double red[kBinThreads / kWave][K];
     const int tid = threadIdx.x;
-    const int64_t tile = blockIdx.x;
     const int64_t n = A.n;
+    const int64_t r = blockIdx.x;  // 0 .. n
     const double it2 = 2.0 * A.inv_t;  // e^{-2 d / t}
-    __shared__ uint2 s_split[2];
-    // this tile's boundaries (recorded for the carry step)
-    if (tid < 2) {
-        const uint2 sp = gram_split_at(A, tile + tid);
-        s_split[tid] = sp;
-        if (tid == 0) G.split[tile] = sp;
-        if (tid == 1 && tile + 1 == G.tiles) G.split[tile + 1] = sp;
-    }
-    __syncthreads();
-    const uint2 b0 = s_split[0], b1 = s_split[1];
-    const int64_t j0 = b0.x, r0 = b0.y;
-    const int nb = (int)(b1.x - b0.x), na = (int)(b1.y - b0.y);
-    const int len = nb + na;
-    for (int j = tid; j < nb; j += kMergeThreads) s_b[j] = A.sb[j0 + j];
-    for (int j = tid; j < na; j += kMergeThreads) s_a[j] = A.sa[r0 + j];
-    const float left_sent = r0 > 0 ? A.sa[r0 - 1] : 0.f;
-    const float right_sent = r0 + na < n ? A.sa[r0 + na] : 0.f;
-    __syncthreads();
-
-    const int dk = tid * kMergeItems < len ? tid * kMergeItems : len;
-    int ib = (int)merge_search(s_b, nb, s_a, na, dk);
-    int ia = dk - ib;
-    double al[kMergeItems], be[kMergeItems];
-    uint32_t idx[kMergeItems];  // b: its rank in sorted b; a: its rank t
-    uint32_t is_b = 0, is_a = 0;
+    const int64_t lo = A.bound[r], hi = A.bound[r + 1];
+    const float right = r < n ? A.sa[r] : 0.f;
+    const float left = r > 0 ? A.sa[r - 1] : 0.f;
+    double acc[K];
 #pragma unroll
-    for (int j = 0; j < kMergeItems; ++j) {
-        al[j] = be[j] = 0.0;
-        idx[j] = 0;
-        if (dk + j >= len) continue;
-        const bool take_b = ib < nb && (ia >= na || s_b[ib] <= s_a[ia]);
-        const int64_t t = r0 + ia;  // anchors a before this item
-        if (take_b) {
-            const float bv = s_b[ib];
-            const float right = ia < na ? s_a[ia] : right_sent;
-            const float left = ia > 0 ? s_a[ia - 1] : left_sent;
-            al[j] = t < n ? decay(bv, right, it2) : 0.0;
-            be[j] = t > 0 ? decay(left, bv, it2) : 0.0;
-            idx[j] = (uint32_t)(j0 + ib);
-            is_b |= 1u << j;
-            ++ib;
-        } else {
-            const float right = s_a[ia];
-            const float left = ia > 0 ? s_a[ia - 1] : left_sent;
-            G.mdec[t] = t > 0 ? decay(left, right, it2) : 0.0;  // each a once
-            idx[j] = (uint32_t)t;
-            is_a |= 1u << j;
-            ++ia;
+    for (int q = 0; q < K; ++q) acc[q] = 0.0;
+    for (int64_t j0 = lo + tid; j0 < hi; j0 += (int64_t)kBinThreads * kBinLoads) {
+        uint32_t src[kBinLoads];
+        float bv[kBinLoads], cc[kBinLoads], ss[kBinLoads];
+#pragma unroll
+        for (int u = 0; u < kBinLoads; ++u) {
+            const int64_t j = j0 + (int64_t)u * kBinThreads;
+            const int64_t jc = j < hi ? j : lo;  // a valid position; its terms are not used
+            src[u] = A.pb[jc];
+            bv[u] = A.sb[jc];
+            cc[u] = NW == 3 ? A.cpsi_r[jc] : 1.f;
+            ss[u] = NW == 3 ? A.spsi_r[jc] : 0.f;
         }
-    }
-    // the weights of this thread's b (D through the permutation of b)
-    double wv[kMergeItems][NW];
+        float dv[kBinLoads];
 #pragma unroll
-    for (int j = 0; j < kMergeItems; ++j) {
-        const uint32_t r = (is_b >> j) & 1u ? idx[j] : 0u;
-        const double d = (double)A.D[A.pb[r]];
-        if (NW == 3) {
-            const double c = A.cpsi_r[r], sn = A.spsi_r[r];
-            wv[j][0] = d * c * c;
-            wv[j][NW > 1 ? 1 : 0] = d * c * sn;
-            wv[j][NW - 1] = d * sn * sn;
-        } else {
-            wv[j][0] = d;
-        }
-    }
-    double run[K], head[K];
+        for (int u = 0; u < kBinLoads; ++u) dv[u] = A.D[src[u]];
 #pragma unroll
-    for (int k = 0; k < K; ++k) run[k] = head[k] = 0.0;
-    const uint32_t first_j = is_a ? (uint32_t)__builtin_ctz(is_a) : 0u;
-#pragma unroll
-    for (int j = 0; j < kMergeItems; ++j) {
-        if ((is_b >> j) & 1u) {
+        for (int u = 0; u < kBinLoads; ++u) {
+            if (j0 + (int64_t)u * kBinThreads >= hi) continue;
+            const double d = (double)dv[u];
+            double wt[NW];
+            if (NW == 3) {
+                const double c = cc[u], sn = ss[u];
+                wt[0] = d * c * c;
+                wt[NW > 1 ? 1 : 0] = d * c * sn;
+                wt[NW - 1] = d * sn * sn;
+            } else {
+                wt[0] = d;
+            }
+            const double er = r < n ? decay(bv[u], right, it2) : 0.0;
+            const double el = r > 0 ? decay(left, bv[u], it2) : 0.0;
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
-                run[3 * w] += wv[j][w];
-                run[3 * w + 1] = fma(al[j], wv[j][w], run[3 * w + 1]);
-                run[3 * w + 2] = fma(be[j], wv[j][w], run[3 * w + 2]);
+                acc[3 * w] += wt[w];
+                acc[3 * w + 1] = fma(wt[w], er, acc[3 * w + 1]);
+                acc[3 * w + 2] = fma(wt[w], el, acc[3 * w + 2]);
             }
-        } else if ((is_a >> j) & 1u) {
-            if ((uint32_t)j == first_j) {
-#pragma unroll
-                for (int k = 0; k < K; ++k) head[k] = run[k];
-            } else {
-                gram_put<NW>(G, n, idx[j], run);
-            }
-#pragma unroll
-            for (int k = 0; k < K; ++k) run[k] = 0.0;
         }
     }
-    double mex, vex[K], vtot[K];
-    block_segscan<K>(is_a ? 0.0 : 1.0, run, sh, 0, mex, vex, vtot);
-    if (is_a) {
-        double tot[K];
 #pragma unroll
-        for (int k = 0; k < K; ++k) tot[k] = vex[k] + head[k];
-        if (mex != 0.0) {
-            // the tile's first anchor: earlier tiles may add to its interval
+    for (int q = 0; q < K; ++q) {
+        double x = acc[q];
 #pragma unroll
-            for (int k = 0; k < K; ++k) G.head[k * G.tiles + tile] = tot[k];
-        } else {
-            gram_put<NW>(G, n, idx[first_j], tot);
-        }
+        for (int d = kWave / 2; d > 0; d >>= 1) x += __shfl_down(x, d);
+        acc[q] = x;
     }
+    if (lane_id() == 0) {
+#pragma unroll
+        for (int q = 0; q < K; ++q) red[tid / kWave][q] = acc[q];
+    }
+    __syncthreads();
     if (tid == 0) {
+        double v[K];
 #pragma unroll
-        for (int k = 0; k < K; ++k) G.tail[k * G.tiles + tile] = vtot[k];
+        for (int q = 0; q < K; ++q) {
+            v[q] = 0.0;
+#pragma unroll
+            for (int i = 0; i < kBinThreads / kWave; ++i) v[q] += red[i][q];
+        }
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            G.sigma[w * (n + 1) + r] = v[3 * w];
+            if (r < n) G.p[w * n + r] = v[3 * w + 1];
+            if (r > 0) G.q[w * n + r - 1] = v[3 * w + 2];
+        }
+        if (r < n) G.mdec[r] = r > 0 ? decay(left, right, it2) : 0.0;
     }
 }
 
-// One workgroup: first the tiles' first intervals are completed (for each
-// of the 3 NW sums, a segmented scan over the tiles in chunks per thread,
-// thread 0 writing the run above the last anchor: sigma_n and q_{n-1}),
-// then S, P and Q over the intervals, written as stats by original index.
-// Each thread takes rounds of kGramRun consecutive ranks with every load of
-// a round issued before any is used.
-constexpr int kGramRun = 8;
+// One workgroup: S, P and Q over the intervals, written as stats by
+// original index.  Each thread takes rounds of kGramRun consecutive ranks
+// with every load of a round issued before any is used.
+constexpr int kGramRun = 16;
 
 template <int NW>
 __global__ __launch_bounds__(kGramScanThreads) void lx_gram_scan(GramArgs A, GramScratch G)
@@ -245,45 +196,7 @@ __global__ __launch_bounds__(kGramScanThreads) void lx_gram_scan(GramArgs A, Gra
     __shared__ Aff<double> sh[kGramScanThreads / kWave];
     constexpr int SW = gram_stride<NW>();
     const int tid = threadIdx.x;
-    const int64_t n = A.n, T = G.tiles;
-
-    // ---- tile carries
-    {
-        const int64_t per = (T + kGramScanThreads - 1) / kGramScanThreads;
-        int64_t t0 = (int64_t)tid * per;
-        if (t0 > T) t0 = T;
-        int64_t t1 = t0 + per;
-        if (t1 > T) t1 = T;
-#pragma unroll 1
-        for (int k = 0; k < 3 * NW; ++k) {
-            const int w = k / 3, kind = k % 3;
-            const double* hd = G.head + k * T;
-            const double* tl = G.tail + k * T;
-            Aff<double> f = aff_identity<double>();
-            for (int64_t t = t0; t < t1; ++t)
-                f = compose(f, Aff<double>{G.split[t + 1].y > G.split[t].y ? 0.0 : 1.0, tl[t]});
-            Aff<double> tot;
-            double c = block_exscan_up<double, kGramScanThreads / kWave>(f, sh, tot).v;
-            for (int64_t t = t0; t < t1; ++t) {
-                const uint32_t r = G.split[t].y;
-                if (G.split[t + 1].y > r) {
-                    const double v = c + hd[t];
-                    if (kind == 0) G.sigma[w * (n + 1) + r] = v;
-                    else if (kind == 1) G.p[w * n + r] = v;
-                    else if (r > 0) G.q[w * n + r - 1] = v;
-                    c = tl[t];
-                } else {
-                    c += tl[t];
-                }
-            }
-            if (tid == 0) {
-                if (kind == 0) G.sigma[w * (n + 1) + n] = tot.v;
-                else if (kind == 2) G.q[w * n + n - 1] = tot.v;
-            }
-        }
-    }
-    __syncthreads();  // global writes above are read below by other threads
-    __threadfence_block();
+    const int64_t n = A.n;
 
     // ---- scans over the intervals, in rounds of kGramScanThreads * kGramRun ranks
     constexpr int64_t kRound = (int64_t)kGramScanThreads * kGramRun;
@@ -493,8 +406,8 @@ __global__ __launch_bounds__(256) void lx_gram_tile(const double* __restrict__ s
 template <int NW>
 static hipError_t gram_launch_t(const GramArgs& a, hipStream_t s)
 {
-    const GramScratch G = gram_scratch_at(a.stats, a.n, a.k, NW);
-    LX_LAUNCH("gram_bins", s, (lx_gram_bins<NW><<<(unsigned)G.tiles, kMergeThreads, 0, s>>>(a, G)));
+    const GramScratch G = gram_scratch_at(a.stats, a.n, NW);
+    LX_LAUNCH("gram_bins", s, (lx_gram_bins<NW><<<(unsigned)(a.n + 1), kBinThreads, 0, s>>>(a, G)));
     LX_LAUNCH("gram_scan", s, (lx_gram_scan<NW><<<1, kGramScanThreads, 0, s>>>(a, G)));
     const unsigned nb = (unsigned)((a.n + kGT - 1) / kGT);
     LX_LAUNCH("gram_tile", s, (lx_gram_tile<NW><<<dim3(nb, nb), 256, 0, s>>>(G.st, a.n, a.inv_t, a.M)));

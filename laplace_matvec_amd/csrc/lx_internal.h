@@ -328,6 +328,7 @@ struct GramArgs {
     const float* sb = nullptr;      // sorted b [k]
     const uint32_t* pb = nullptr;   // perm of b
     const float* D = nullptr;       // [k], original order of b
+    const uint32_t* bound = nullptr;  // [n + 2]: interval r is sorted b [bound[r], bound[r+1])
     const float* cphi_r = nullptr;  // phased: cos/sin of phi by rank of a, of psi by rank of b
     const float* sphi_r = nullptr;
     const float* cpsi_r = nullptr;
@@ -336,6 +337,9 @@ struct GramArgs {
     float* M = nullptr;             // [n][n]
 };
 size_t gram_scratch_bytes(int64_t n, int64_t k, int weight_sets);
+// bound[r] = #{b <= s_{r-1}} (r = 1 .. n), bound[0] = 0, bound[n+1] = k.
+hipError_t gram_bounds_launch(const float* sa, int64_t n, const float* sb, int64_t k, uint32_t* bound,
+                              hipStream_t s);
 hipError_t gram_launch(const GramArgs& a, hipStream_t s);
 
 }  // namespace lx

@@ -292,6 +292,23 @@ def test_gram_general(gpu, n, k):
     assert oracle.rel_l2(M, ref) < TOL
 
 
+def test_gram_repeated_calls_and_temperature(gpu):
+    """One plan, several Gram calls: the interval bounds the first call
+    makes are reused, also after a temperature change and with new weights;
+    inputs outside the anchor range and many inputs per interval."""
+    rng = np.random.default_rng(77)
+    n, k = 300, 30001
+    a = (rng.standard_normal(n) * 15).astype(np.float32)
+    b = (rng.standard_normal(k) * 25).astype(np.float32)
+    with lx.laplex_plan_create(dev(a), b=dev(b)) as plan:
+        for t, seed in ((1.0, 1), (0.5, 2), (2.0, 3)):
+            lx.laplex_plan_set_temperature(plan, t)
+            D = np.random.default_rng(seed).uniform(-1, 1, k).astype(np.float32)
+            M = host(lx.laplex_gram(plan, dev(D)))
+            ref = oracle.gram_direct(a, b, D, t=t)
+            assert oracle.rel_l2(M, ref) < TOL, (t, seed)
+
+
 def test_gram_symmetric_plan(gpu):
     n = 2000
     a = anchors_with_ties(n, 10.0)
