@@ -255,6 +255,66 @@ void prof_end(int token, hipStream_t s)
 
 }  // namespace lx
 
+// ------------------------------------------------------- host-side helpers
+
+// Pinned host words for reading a plan's NaN/Inf flag back: a copy into
+// pinned memory is a plain DMA, where pageable memory would be staged.
+// One allocation per process, slots handed out under a lock; when all are
+// taken, the caller falls back to its own (pageable) word.
+struct PinnedFlags {
+    std::mutex mu;
+    uint32_t* base = nullptr;
+    bool tried = false;
+    std::vector<int> free;
+};
+PinnedFlags g_pinned;
+constexpr int kPinnedSlots = 256;
+
+uint32_t* take_pinned_flag()
+{
+    std::lock_guard<std::mutex> lk(g_pinned.mu);
+    if (!g_pinned.tried) {
+        g_pinned.tried = true;
+        void* p = nullptr;
+        if (hipHostMalloc(&p, kPinnedSlots * 64, hipHostMallocDefault) == hipSuccess) {
+            g_pinned.base = (uint32_t*)p;
+            for (int i = kPinnedSlots - 1; i >= 0; --i) g_pinned.free.push_back(i);
+        } else {
+            (void)hipGetLastError();
+        }
+    }
+    if (g_pinned.free.empty()) return nullptr;
+    const int i = g_pinned.free.back();
+    g_pinned.free.pop_back();
+    return g_pinned.base + (size_t)i * 16;  // one 64-byte line per slot
+}
+
+void give_pinned_flag(uint32_t* w)
+{
+    if (!w) return;
+    std::lock_guard<std::mutex> lk(g_pinned.mu);
+    g_pinned.free.push_back((int)((w - g_pinned.base) / 16));
+}
+
+// LDS bytes a workgroup may use on a device (looked up once per device).
+int lds_budget(int dev)
+{
+    static std::mutex mu;
+    static std::vector<int> cached;
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)cached.size() <= dev) cached.resize((size_t)dev + 1, 0);
+    if (!cached[dev]) {
+        int lds = 0;
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            lds = 65536;
+        }
+        if (lds > 160 * 1024) lds = 160 * 1024;
+        cached[dev] = lds - 1024;
+    }
+    return cached[dev];
+}
+
 // ----------------------------------------------------------------- plans
 
 struct laplex_plan_s {
@@ -522,7 +582,13 @@ laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, cons
     p->phased = phi != nullptr;
     void* scratch = nullptr;
     uint32_t* flag = nullptr;
-    uint32_t host_flag = 0;
+    uint32_t own_flag = 0;
+    uint32_t* pinned = take_pinned_flag();
+    uint32_t* host_flag = pinned ? pinned : &own_flag;
+    struct PinnedRelease {
+        uint32_t* w;
+        ~PinnedRelease() { give_pinned_flag(w); }
+    } pinned_release{pinned};
     auto bail = [&](laplex_status code) {
         if (scratch) dev_free(scratch, p->device, s);
         plan_release(p);
@@ -535,16 +601,13 @@ laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, cons
     } while (0)
 
     LX_PLAN_TRY(hipGetDevice(&p->device), "hipGetDevice");
-    {
-        int lds = 0;
-        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, p->device) != hipSuccess) lds = 65536;
-        if (lds > 160 * 1024) lds = 160 * 1024;
-        p->lds_bytes = lds - 1024;
-    }
+    p->lds_bytes = lds_budget(p->device);
     LX_PLAN_TRY(plan_alloc(p, (void**)&flag, 256, s), "alloc flag");
-    LX_PLAN_TRY(lx::fill_u32(flag, 0u, 1, s), "clear flag");
     LX_PLAN_TRY(plan_alloc(p, (void**)&p->sa, (size_t)n * 4, s), "alloc sorted a");
-    if (sym && n <= lx::kSmallMax && n < replay_min()) {
+    const bool small_plan = sym && n <= lx::kSmallMax && n < replay_min();
+    // the small plan kernel writes the flag whole; the others OR into it
+    if (!small_plan) LX_PLAN_TRY(lx::fill_u32(flag, 0u, 1, s), "clear flag");
+    if (small_plan) {
         // A small symmetric plan in one workgroup: the sorted anchors, the
         // permutation (the sort records are never needed below the replay
         // size) and the phase factors by rank; y = K x too for a few vectors.
@@ -579,9 +642,9 @@ laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, cons
         S.spsi = p->spsi;
         S.flag = flag;
         LX_PLAN_TRY(lx::small_sym_launch(S, s), "small plan");
-        LX_PLAN_TRY(hipMemcpyAsync(&host_flag, flag, 4, hipMemcpyDeviceToHost, s), "read flag");
+        LX_PLAN_TRY(hipMemcpyAsync(host_flag, flag, 4, hipMemcpyDeviceToHost, s), "read flag");
         LX_PLAN_TRY(hipStreamSynchronize(s), "synchronize");
-        if (host_flag & 1u) return bail(fail(LAPLEX_ERR_NONFINITE_ANCHOR, "NaN or Inf among anchors or phases"));
+        if (*host_flag & 1u) return bail(fail(LAPLEX_ERR_NONFINITE_ANCHOR, "NaN or Inf among anchors or phases"));
         if (x) {
             // x in its original order is kept for a later backward (copied
             // by the plan kernel when it computed y)
@@ -724,9 +787,9 @@ laplex_status plan_create_impl(laplex_plan* out, const float* a, int64_t n, cons
     }
     dev_free(scratch, p->device, s);
     scratch = nullptr;
-    LX_PLAN_TRY(hipMemcpyAsync(&host_flag, flag, 4, hipMemcpyDeviceToHost, s), "read flag");
+    LX_PLAN_TRY(hipMemcpyAsync(host_flag, flag, 4, hipMemcpyDeviceToHost, s), "read flag");
     LX_PLAN_TRY(hipStreamSynchronize(s), "synchronize");
-    if (host_flag & 1u) return bail(fail(LAPLEX_ERR_NONFINITE_ANCHOR, "NaN or Inf among anchors or phases"));
+    if (*host_flag & 1u) return bail(fail(LAPLEX_ERR_NONFINITE_ANCHOR, "NaN or Inf among anchors or phases"));
 #undef LX_PLAN_TRY
     if (x && !fuse) {
         // not fused (short side or too many rows): the plain apply, and a copy

@@ -315,7 +315,7 @@ struct SmallSymArgs {
     float* sphi = nullptr;
     float* cpsi = nullptr;
     float* spsi = nullptr;
-    uint32_t* flag = nullptr;              // bit 0 set for a NaN/Inf anchor or phase
+    uint32_t* flag = nullptr;              // written: 1 for a NaN/Inf anchor or phase, else 0
 };
 hipError_t small_sym_launch(const SmallSymArgs& a, hipStream_t s);
 

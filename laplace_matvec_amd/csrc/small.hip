@@ -29,6 +29,9 @@ constexpr int kSmallItems = kSmallMax / kSmallThreads;  // 8
 constexpr int kSmallRadix = 256;
 static_assert(kSmallThreads * kSmallItems == kSmallMax, "small plan size");
 
+// ITEMS keys per thread: 8 covers kSmallMax anchors, 4 covers up to 4096
+// with half the ranking and scan work.
+template <int ITEMS>
 __global__ __launch_bounds__(kSmallThreads) void lx_small_sym(SmallSymArgs A)
 {
     __shared__ uint32_t s_key[kSmallMax];
@@ -41,15 +44,15 @@ __global__ __launch_bounds__(kSmallThreads) void lx_small_sym(SmallSymArgs A)
     const int lane = lane_id();
     const int w = tid / kWave;
     const int n = (int)A.n;
-    const int wpos = w * (kSmallItems * kWave);
+    const int wpos = w * (ITEMS * kWave);
 
     // Keys in wave-striped order (item j of lane l is position wpos + 64 j +
     // l), so a wave's items in (j, lane) order are its keys in index order;
     // positions past n take the largest key and rank last.
-    uint32_t key[kSmallItems], idx[kSmallItems];
+    uint32_t key[ITEMS], idx[ITEMS];
     bool bad = false;
 #pragma unroll
-    for (int j = 0; j < kSmallItems; ++j) {
+    for (int j = 0; j < ITEMS; ++j) {
         const int p = wpos + j * kWave + lane;
         idx[j] = (uint32_t)p;
         const float f = p < n ? A.a[p] : 0.f;
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(kSmallThreads) void lx_small_sym(SmallSymArgs A)
         const int shift = 8 * pass;
         if (pass > 0) {
 #pragma unroll
-            for (int j = 0; j < kSmallItems; ++j) {
+            for (int j = 0; j < ITEMS; ++j) {
                 const int p = wpos + j * kWave + lane;
                 key[j] = s_key[p];
                 idx[j] = s_idx[p];
@@ -68,9 +71,9 @@ __global__ __launch_bounds__(kSmallThreads) void lx_small_sym(SmallSymArgs A)
         }
         for (int i = tid; i < kSmallWaves * kSmallRadix; i += kSmallThreads) (&s_hist[0][0])[i] = 0;
         __syncthreads();  // also: every item of the previous order has been read
-        uint32_t pos[kSmallItems];
+        uint32_t pos[ITEMS];
 #pragma unroll
-        for (int j = 0; j < kSmallItems; ++j) {
+        for (int j = 0; j < ITEMS; ++j) {
             const uint32_t d = (key[j] >> shift) & 0xFFu;
             const uint64_t peers = match_digit8(d);
             const uint32_t below = count_below(peers);
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(kSmallThreads) void lx_small_sym(SmallSymArgs A)
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < kSmallItems; ++j) {
+        for (int j = 0; j < ITEMS; ++j) {
             const uint32_t dst = s_hist[w][(key[j] >> shift) & 0xFFu] + pos[j];
             s_key[dst] = key[j];
             s_idx[dst] = (uint16_t)idx[j];
@@ -107,10 +110,10 @@ __global__ __launch_bounds__(kSmallThreads) void lx_small_sym(SmallSymArgs A)
     }
 
     // This thread's ranks r0 .. r0+7: the plan's arrays, the phase factors.
-    const int r0 = tid * kSmallItems;
-    float ci[kSmallItems], si[kSmallItems], co[kSmallItems], so[kSmallItems];  // input (psi), output (phi)
+    const int r0 = tid * ITEMS;
+    float ci[ITEMS], si[ITEMS], co[ITEMS], so[ITEMS];  // input (psi), output (phi)
 #pragma unroll
-    for (int i = 0; i < kSmallItems; ++i) {
+    for (int i = 0; i < ITEMS; ++i) {
         const int r = r0 + i;
         ci[i] = co[i] = 1.f;
         si[i] = so[i] = 0.f;
@@ -135,23 +138,25 @@ __global__ __launch_bounds__(kSmallThreads) void lx_small_sym(SmallSymArgs A)
             }
         }
     }
-    if (__any(bad) && lane == 0) atomicOr(A.flag, 1u);
+    // the flag word is written here, whole: no clear is needed before
+    const int any_bad = __syncthreads_or(bad ? 1 : 0);
+    if (tid == 0) *A.flag = any_bad ? 1u : 0u;
     if (A.x == nullptr) return;  // uniform: a plan without a product
     // the plan's own copy of x (original order) for a later backward
     if (A.x_keep)
         for (int64_t i = tid; i < (int64_t)A.batch * n; i += kSmallThreads) A.x_keep[i] = A.x[i];
 
     // decays between neighbouring ranks; 0 before rank 0 and from rank n on
-    double e[kSmallItems + 1];
+    double e[ITEMS + 1];
     {
-        float s[kSmallItems + 2];
+        float s[ITEMS + 2];
 #pragma unroll
-        for (int i = 0; i < kSmallItems + 2; ++i) {
+        for (int i = 0; i < ITEMS + 2; ++i) {
             const int r = r0 - 1 + i;
             s[i] = (r >= 0 && r < n) ? float_of_key(s_key[r]) : 0.f;
         }
 #pragma unroll
-        for (int i = 0; i <= kSmallItems; ++i) {
+        for (int i = 0; i <= ITEMS; ++i) {
             const int r = r0 + i;  // e[i] joins ranks r - 1 and r
             e[i] = (r > 0 && r < n) ? decay(s[i], s[i + 1], A.inv_t) : 0.0;
         }
@@ -159,34 +164,34 @@ __global__ __launch_bounds__(kSmallThreads) void lx_small_sym(SmallSymArgs A)
     const int C = A.phi ? 2 : 1;
     for (int v = 0; v < A.batch; ++v) {  // uniform loops: every thread takes part in the scans
         const float* xv = A.x + (int64_t)v * n;
-        float out[kSmallItems];
+        float out[ITEMS];
 #pragma unroll
-        for (int i = 0; i < kSmallItems; ++i) out[i] = 0.f;
+        for (int i = 0; i < ITEMS; ++i) out[i] = 0.f;
         for (int c = 0; c < C; ++c) {
-            float val[kSmallItems];
+            float val[ITEMS];
 #pragma unroll
-            for (int i = 0; i < kSmallItems; ++i) {
+            for (int i = 0; i < ITEMS; ++i) {
                 const int r = r0 + i;
                 const float xr = r < n ? xv[s_idx[r]] : 0.f;
                 val[i] = C == 2 ? (c == 0 ? ci[i] : si[i]) * xr : xr;
             }
             Aff<double> f = aff_identity<double>(), b = aff_identity<double>();
 #pragma unroll
-            for (int i = 0; i < kSmallItems; ++i) f = compose(f, Aff<double>{e[i], (double)val[i]});
+            for (int i = 0; i < ITEMS; ++i) f = compose(f, Aff<double>{e[i], (double)val[i]});
 #pragma unroll
-            for (int i = kSmallItems - 1; i >= 0; --i) b = compose(b, Aff<double>{e[i + 1], (double)val[i]});
+            for (int i = ITEMS - 1; i >= 0; --i) b = compose(b, Aff<double>{e[i + 1], (double)val[i]});
             const Aff<double> fx = block_exscan_up_lean<double, kSmallWaves>(f, s_aff);
             const Aff<double> bx = block_exscan_down_lean<double, kSmallWaves>(b, s_aff);
-            double Lr[kSmallItems];
+            double Lr[ITEMS];
             double L = fx.v;
 #pragma unroll
-            for (int i = 0; i < kSmallItems; ++i) {
+            for (int i = 0; i < ITEMS; ++i) {
                 L = e[i] * L + (double)val[i];
                 Lr[i] = L;
             }
             double U = bx.v;
 #pragma unroll
-            for (int i = kSmallItems - 1; i >= 0; --i) {
+            for (int i = ITEMS - 1; i >= 0; --i) {
                 U = e[i + 1] * U + (double)val[i];
                 const float yc = (float)(Lr[i] + U - (double)val[i]);
                 out[i] = C == 2 ? fmaf(c == 0 ? co[i] : so[i], yc, out[i]) : yc;
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(kSmallThreads) void lx_small_sym(SmallSymArgs A)
         }
         float* yv = A.y + (int64_t)v * n;
 #pragma unroll
-        for (int i = 0; i < kSmallItems; ++i)
+        for (int i = 0; i < ITEMS; ++i)
             if (r0 + i < n) yv[s_idx[r0 + i]] = out[i];
     }
 }
@@ -203,8 +208,9 @@ __global__ __launch_bounds__(kSmallThreads) void lx_small_sym(SmallSymArgs A)
 
 hipError_t small_sym_launch(const SmallSymArgs& a, hipStream_t s)
 {
-    if (a.n < 1 || a.n > kSmallMax) return hipErrorInvalidValue;
-    LX_LAUNCH("small_sym", s, (lx_small_sym<<<1, kSmallThreads, 0, s>>>(a)));
+    if (a.n < 1 || a.n > kSmallMax || a.flag == nullptr) return hipErrorInvalidValue;
+    if (a.n <= kSmallThreads * 4) LX_LAUNCH("small_sym", s, (lx_small_sym<4><<<1, kSmallThreads, 0, s>>>(a)));
+    else LX_LAUNCH("small_sym", s, (lx_small_sym<8><<<1, kSmallThreads, 0, s>>>(a)));
     return hipSuccess;
 }
 
