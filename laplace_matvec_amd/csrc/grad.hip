@@ -237,9 +237,11 @@ __device__ __forceinline__ void grad_store_out(const GradSymArgs& A, float* dst,
 // once per tile, and the second half re-reads the tile's inputs from cache.
 // Halves, vectors and channels run in loops that are not unrolled, and the
 // decays and tie masks are re-read from LDS in them, which keeps one step's
-// state live at a time.
+// state live at a time.  The phased form holds twice the channel state: it
+// runs at two waves per SIMD (one workgroup per CU, up to 256 VGPRs), so
+// nothing spills; the unphased form fits 128 VGPRs at four.
 template <int C, bool RANDOM>
-__global__ __launch_bounds__(kGradThreads, 4) void lx_grad_sym_apply(GradSymArgs A)
+__global__ __launch_bounds__(kGradThreads, C == 2 ? 2 : 4) void lx_grad_sym_apply(GradSymArgs A)
 {
     __shared__ Aff<double> sh[2 * kGradWaves * 4];
     int parity = 0;
