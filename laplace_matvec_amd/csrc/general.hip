@@ -54,7 +54,8 @@ constexpr int kGenThreads = 1024;
 // interval, so they are never visited.
 //
 // lx_bucket_sorted (per group of up to 8 vectors, one workgroup per group
-// and chunk of sub-chunks): the values of the group's vectors are placed
+// and chunk of sub-chunks, the groups of a chunk on one die so that they
+// share its layout through that die's L2): the values of the group's vectors are placed
 // in LDS by slot, and thread j owns u_j and v_j of every vector in
 // registers: it adds the alpha parts of interval j and the beta parts of
 // interval j+1, slot by slot (LDS reads and FMAs only).  The
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_layout(BucketArgs A, Bu
 
 template <int C, bool TIES>
 __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, BucketLayout L, int VG, int groups,
-                                                               int64_t chunk_len)
+                                                               int64_t chunks, int64_t chunk_len)
 {
     extern __shared__ float lds[];
     const int no = (int)A.n_out;  // <= kGenThreads
@@ -221,8 +222,9 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, Bu
     uint8_t* ts = reinterpret_cast<uint8_t*>(cs + kSub);        // [kSub]: tie flags by slot (TIES)
 
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-    const int g = (int)(blockIdx.x % groups);
-    const int64_t chunk = blockIdx.x / groups;
+    int g;
+    int64_t chunk;
+    if (!die_chunk_group(blockIdx.x, chunks, groups, &chunk, &g)) return;  // uniform
     const int64_t v0 = (int64_t)g * VG;
     const int nv = (int)((A.batch - v0) < VG ? (A.batch - v0) : VG);
 
@@ -431,7 +433,7 @@ hipError_t bucket_launch(BucketArgs& a, hipStream_t s)
     if (ties && !a.tie) return hipErrorInvalidValue;
     if (vg > 0 && a.partial && a.layout && a.n_in > 0) {
         const size_t shmem = bucket_sorted_lds(a.n_out, a.channels, ties);
-        const unsigned blocks = (unsigned)((int64_t)chunks * groups);
+        const unsigned blocks = (unsigned)die_chunk_group_blocks(chunks, groups);
         const BucketLayout L = bucket_layout_at(a.layout, a.n_in, a.n_out, ties);
         const unsigned subs = (unsigned)((a.n_in + kSub - 1) / kSub);
         if (two) LX_LAUNCH("bucket_layout", s, (lx_bucket_layout<2><<<subs, kGenThreads, 0, s>>>(a, L)));
@@ -441,7 +443,7 @@ hipError_t bucket_launch(BucketArgs& a, hipStream_t s)
         (void)hipFuncSetAttribute((const void*)lx_bucket_sorted<CC, TT>, hipFuncAttributeMaxDynamicSharedMemorySize, \
                                   (int)shmem);                                                                 \
         LX_LAUNCH("bucket_sorted", s,                                                                          \
-                  (lx_bucket_sorted<CC, TT><<<blocks, kGenThreads, shmem, s>>>(a, L, vg, groups, chunk_len)));  \
+                  (lx_bucket_sorted<CC, TT><<<blocks, kGenThreads, shmem, s>>>(a, L, vg, groups, chunks, chunk_len))); \
     } while (0)
         if (two) {
             if (ties) LX_BKS(2, true);
@@ -476,13 +478,15 @@ hipError_t bucket_launch(BucketArgs& a, hipStream_t s)
 // evaluates the current one.
 
 template <int C>
-__global__ __launch_bounds__(kGenThreads) void lx_eval_rows(EvalArgs A, int VG, int groups, int64_t chunk_len)
+__global__ __launch_bounds__(kGenThreads) void lx_eval_rows(EvalArgs A, int VG, int groups, int64_t chunks,
+                                                           int64_t chunk_len)
 {
     extern __shared__ float lds[];
     constexpr int RW = eval_row_words<C>();
     const int ni = (int)A.n_in;
-    const int g = (int)(blockIdx.x % groups);
-    const int64_t chunk = blockIdx.x / groups;
+    int g;
+    int64_t chunk;
+    if (!die_chunk_group(blockIdx.x, chunks, groups, &chunk, &g)) return;  // uniform
     const int64_t v0 = (int64_t)g * VG;
     const int nv = (int)((A.batch - v0) < VG ? (A.batch - v0) : VG);
     float* si = lds;                                                  // [ni]
@@ -562,12 +566,14 @@ __global__ __launch_bounds__(kGenThreads) void lx_eval_rows(EvalArgs A, int VG, 
 
 
 template <int C, bool USE_LDS>
-__global__ __launch_bounds__(kGenThreads) void lx_eval(EvalArgs A, int VG, int groups, int64_t chunk_len)
+__global__ __launch_bounds__(kGenThreads) void lx_eval(EvalArgs A, int VG, int groups, int64_t chunks,
+                                                      int64_t chunk_len)
 {
     extern __shared__ float lds[];
     const int64_t ni = A.n_in;
-    const int g = (int)(blockIdx.x % groups);
-    const int64_t chunk = blockIdx.x / groups;
+    int g;
+    int64_t chunk;
+    if (!die_chunk_group(blockIdx.x, chunks, groups, &chunk, &g)) return;  // uniform
     const int64_t v0 = (int64_t)g * VG;
     const int nv = (int)((A.batch - v0) < VG ? (A.batch - v0) : VG);
     const float* si = A.s_in;
@@ -637,14 +643,14 @@ hipError_t eval_launch(const EvalArgs& a, hipStream_t s)
         if (chunks < 1) chunks = 1;
         const int64_t chunk_len = (a.n_out + chunks - 1) / chunks;
         chunks = (a.n_out + chunk_len - 1) / chunk_len;
-        const unsigned blocks = (unsigned)(chunks * groups);
+        const unsigned blocks = (unsigned)die_chunk_group_blocks(chunks, (int)groups);
         const size_t shmem = eval_rows_lds(a.n_in, a.channels);
         if (a.channels == 2) {
             (void)hipFuncSetAttribute((const void*)lx_eval_rows<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-            LX_LAUNCH("eval", s, (lx_eval_rows<2><<<blocks, kGenThreads, shmem, s>>>(a, vg, (int)groups, chunk_len)));
+            LX_LAUNCH("eval", s, (lx_eval_rows<2><<<blocks, kGenThreads, shmem, s>>>(a, vg, (int)groups, chunks, chunk_len)));
         } else {
             (void)hipFuncSetAttribute((const void*)lx_eval_rows<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-            LX_LAUNCH("eval", s, (lx_eval_rows<1><<<blocks, kGenThreads, shmem, s>>>(a, vg, (int)groups, chunk_len)));
+            LX_LAUNCH("eval", s, (lx_eval_rows<1><<<blocks, kGenThreads, shmem, s>>>(a, vg, (int)groups, chunks, chunk_len)));
         }
         return hipSuccess;
     }
@@ -661,13 +667,13 @@ hipError_t eval_launch(const EvalArgs& a, hipStream_t s)
     if (chunks < 1) chunks = 1;
     const int64_t chunk_len = (a.n_out + chunks - 1) / chunks;
     chunks = (a.n_out + chunk_len - 1) / chunk_len;
-    const unsigned blocks = (unsigned)(chunks * groups);
+    const unsigned blocks = (unsigned)die_chunk_group_blocks(chunks, groups);
     const size_t shmem = use_lds ? (size_t)(pad64(a.n_in) + 2 * vg * a.channels * a.n_in) * 4 : 0;
     const int v = (int)vg;
 #define LX_EVAL(CC, LL)                                                                                  \
     do {                                                                                                 \
         if (LL) (void)hipFuncSetAttribute((const void*)lx_eval<CC, LL>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem); \
-        LX_LAUNCH("eval", s, (lx_eval<CC, LL><<<blocks, kGenThreads, shmem, s>>>(a, v, groups, chunk_len))); \
+        LX_LAUNCH("eval", s, (lx_eval<CC, LL><<<blocks, kGenThreads, shmem, s>>>(a, v, groups, chunks, chunk_len))); \
     } while (0)
     if (a.channels == 2) {
         if (use_lds) LX_EVAL(2, true);

@@ -83,6 +83,26 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t tiles)
     return x < r ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
 }
 
+// For a grid of chunks x groups in which the groups of one chunk read the
+// same inputs (vector groups over one range of anchors), workgroup b is
+// given chunk (b / 8 / groups) * 8 + b % 8 and group (b / 8) % groups: the
+// groups of a chunk run on one die in consecutive dispatch slots, so that
+// die's L2 serves the shared inputs to all of them after one read from
+// HBM.  The grid is rounded up to whole dies; returns false for a
+// workgroup past the last chunk.
+__device__ __forceinline__ bool die_chunk_group(int64_t b, int64_t chunks, int groups, int64_t* chunk, int* g)
+{
+    constexpr int64_t kDies = 8;
+    const int64_t k = b / kDies;
+    *g = (int)(k % groups);
+    *chunk = (k / groups) * kDies + b % kDies;
+    return *chunk < chunks;
+}
+__host__ __device__ inline int64_t die_chunk_group_blocks(int64_t chunks, int groups)
+{
+    return (chunks + 7) / 8 * 8 * groups;
+}
+
 template <class T>
 struct Aff {
     T m, v;
