@@ -8,20 +8,25 @@ is checked through the properties that define a stable ascending sort
 that only the oracle's own permutation satisfies, so the check is bit-exact.
 """
 import sys
+import time
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
+from dense_near import dense_rows_near
 from laplace_matvec_amd import laplex as lx
 from laplace_matvec_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
 
+_T0 = time.monotonic()
+
+
 def say(*a):
-    print(*a, flush=True)
+    print(f"[{time.monotonic() - _T0:7.1f}s]", *a, flush=True)
     sys.stdout.flush()
 
 
@@ -143,11 +148,7 @@ def test_config4_full_gram(gpu):
     assert e < 1e-5 and ed < 1e-5
 
 
-# Each sampled output is a dense row over all 2^30 inputs (about 1.5 s of
-# one host core); the oracle spreads a call over the host cores from 64
-# rows up, so the rows go in chunks of 64.
-C5_ROWS = 128
-
+C5_ROWS = 256
 
 @pytest.mark.timeout(1500)
 def test_config5_full_n2p30_end_to_end(gpu):
@@ -155,7 +156,7 @@ def test_config5_full_n2p30_end_to_end(gpu):
     launch configuration the benchmark times (x travelling through the
     key-value radix passes, the scans in place, four backward replays):
     the permutation is THE stable sort, y equals plan_create + apply bit for
-    bit, and 128 sampled outputs match the dense definition within 1e-4."""
+    bit, and 256 sampled outputs match the dense definition within 1e-4."""
     say("[full] config 5: n=2^30 symmetric, laplex_plan_create_apply")
     inp = wl.device_config_inputs(5, device=gpu)
     a_d, x_d = inp["a"], inp["x"]
@@ -177,10 +178,8 @@ def test_config5_full_n2p30_end_to_end(gpu):
     rows = sample(a.size, C5_ROWS + 16, 51)[:C5_ROWS]
     assert rows.size == C5_ROWS
     ys = y.reshape(-1)[torch.from_numpy(rows).to(gpu)].cpu().numpy()
-    ref = np.empty(rows.size)
-    for c in range(0, rows.size, 64):
-        ref[c:c + 64] = oracle.apply_dense(a, x, rows=rows[c:c + 64])
-        say(f"  oracle rows {c + 64}/{rows.size}")
+    say("  dense rows by value bucket")
+    ref = dense_rows_near(a, x, rows, progress=say)
     e = oracle.rel_l2(ys, ref)
     say(f"  sampled rel L2 over {rows.size} outputs {e:.3e}")
     assert e < 1e-4
