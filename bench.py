@@ -176,12 +176,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.calibrate_copy:
-        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch
-        # give the factor between those counters and bytes moved
+        # a plain copy of known size (1 GiB read, 1 GiB written, one
+        # dispatch): its FETCH_SIZE / WRITE_SIZE give the factor between
+        # those counters and bytes moved
         src = torch.ones(1 << 28, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            wl.device_copy(src, dst)
         torch.cuda.synchronize()
         del src, dst
     cfg = int(args.workload[1])

@@ -2,8 +2,9 @@
 
 Outputs, next to this file:
   liblaplex.so         the operator library (C ABI of include/laplex.h)
-  liblaplex_inputs.so  the device input generator (Philox4x32-10), kept
-                       separate because it is not part of the operator
+  liblaplex_inputs.so  the device input generator (Philox4x32-10) and a
+                       plain copy kernel for counter calibration, kept
+                       separate because they are not part of the operator
 """
 from __future__ import annotations
 
@@ -20,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("LAPLEX_ARCH", "gfx950")
 
 LIB_SOURCES = ["api.hip", "sort.hip", "small.hip", "scan.hip", "general.hip", "gram.hip", "grad.hip", "merge.hip"]
-INPUT_SOURCES = ["inputs_philox.hip"]
+INPUT_SOURCES = ["inputs_philox.hip", "calib_copy.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

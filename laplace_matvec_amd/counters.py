@@ -3,9 +3,12 @@
 Two rocprofv3 counter runs of the same benchmark command, one with
 ``--pmc FETCH_SIZE`` and one with ``--pmc WRITE_SIZE``, give per-dispatch
 counter values in KiB.  The command also runs a plain device copy of a known
-size (``bench.py --calibrate-copy``: 1 GiB, dispatched as two 512 MiB
-blits), so the factor between each counter and the bytes actually moved is
-measured on the same box in the same process.  This module folds the
+size (``bench.py --calibrate-copy``: 1 GiB read and written by one dispatch
+of the input library's copy kernel, 4-byte accesses like the operator's
+streaming kernels), so the factor between each counter and the bytes
+actually moved is measured on the same box in the same process.  (The
+runtime's own blit kernel is not used: its counters scale differently from
+those of plain loads and stores.)  This module folds the
 dispatches into HBM bytes per launch of each kernel label the library uses
 for its own timing events, and writes a text record that ``bench.py`` reads:
 
@@ -38,7 +41,8 @@ import re
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
-COPY_BYTES = 512 << 20  # bytes read (and written) by one calibration blit
+COPY_BYTES = 1 << 30  # bytes read (and written) by one calibration copy dispatch
+COPY_KERNEL = "lx_calib_copy"  # the input library's plain copy kernel
 
 
 def source_files(root: str = ROOT) -> list[str]:
@@ -66,11 +70,13 @@ def source_digest(root: str = ROOT) -> str:
 # rocprofv3 kernel name -> the label of the library's timing event for it
 # (the names passed to LX_LAUNCH in csrc/).
 def label_of(kernel: str) -> str | None:
-    k = kernel.strip()
+    k = kernel.strip().replace("(anonymous namespace)::", "")
     base = re.split(r"[<(]", k, 1)[0].strip()
     base = base.split("::")[-1]
     args = k[len(k.split("<", 1)[0]):] if "<" in k else ""
     targs = [t.strip() for t in args.strip("<>").split(">")[0].split(",")] if args else []
+    if base in ("lx_gen", "lx_calib_copy"):
+        return None  # the input library (inputs and the calibration copy), not the operator
     if base in ("lx_fill_u32", "lx_sort_clear"):
         return "util_fill"
     if base in ("lx_sort_hist", "lx_sort_scan_hist", "lx_sort_pass"):
@@ -125,14 +131,12 @@ def dispatch_counters(path: str, counter: str) -> list[tuple[str, float]]:
 
 
 def calibration_factor(disp: list[tuple[str, float]], bytes_per_dispatch: int) -> float:
-    """Bytes per counter KiB, from the calibration copy's blit dispatches:
-    the copy kernel dispatches whose value is largest (the 512 MiB blits)."""
-    vals = [v for name, v in disp if "copyBuffer" in name or "copy_buffer" in name.lower()]
+    """Bytes per counter KiB, from the dispatches of the calibration copy
+    kernel (each moves `bytes_per_dispatch` one way)."""
+    vals = [v for name, v in disp if COPY_KERNEL in name]
     if not vals:
         raise ValueError("no calibration copy dispatch found (run the command with --calibrate-copy)")
-    top = max(vals)
-    blits = [v for v in vals if v >= 0.98 * top]
-    mean = sum(blits) / len(blits)
+    mean = sum(vals) / len(vals)
     return bytes_per_dispatch / (mean * 1024.0)
 
 
@@ -145,14 +149,14 @@ def make_record(fetch_csv: str, write_csv: str, workload: str, steps: int, comma
     for disp, fac in ((f, ff), (w, wf)):
         for name, v in disp:
             lab = label_of(name)
-            if lab is None or name.split("<")[0].strip().endswith("lx_gen"):
+            if lab is None:
                 continue
             per.setdefault(lab, [0, 0.0, 0])
             per[lab][1] += v * 1024.0 * fac
     counts = {}
     for name, _ in f:
         lab = label_of(name)
-        if lab is None or name.split("<")[0].strip().endswith("lx_gen"):
+        if lab is None:
             continue
         counts[lab] = counts.get(lab, 0) + 1
     lines = [f"# rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated against a plain 1 GiB device copy;",

@@ -210,8 +210,26 @@ def _gen():
         lib.laplex_inputs_generate.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                                ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int,
                                                ctypes.c_double, ctypes.c_double, ctypes.c_void_p]
+        lib.laplex_inputs_copy.restype = ctypes.c_int
+        lib.laplex_inputs_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         _gen_lib = lib
     return _gen_lib
+
+
+def device_copy(src, dst) -> None:
+    """dst[:] = src through the input library's plain copy kernel (one
+    dispatch, 4-byte accesses): the known-size reference of the HBM traffic
+    counters.  Both are contiguous device tensors of 4-byte elements."""
+    import ctypes
+    import torch
+    if src.numel() != dst.numel() or src.element_size() != 4 or dst.element_size() != 4:
+        raise ValueError("device_copy: same number of 4-byte elements needed")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("device_copy: contiguous tensors needed")
+    rc = _gen().laplex_inputs_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                   src.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"laplex_inputs_copy failed ({rc})")
 
 
 def _device_draw(shape, key0, key1, kind, p, q, device, dtype=None):

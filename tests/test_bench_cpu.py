@@ -95,6 +95,23 @@ def test_counter_labels_follow_the_library_timing_names():
     assert counters.label_of("lx::lx_scan_apply<1, 2, true, 8>(lx::ScanArgs)") == "scan_apply_tables"
     assert counters.label_of("lx::lx_eval_rows<2>(lx::EvalArgs, int, int, long)") == "eval"
     assert counters.label_of("__amd_rocclr_copyBuffer") is None
+    assert counters.label_of("(anonymous namespace)::lx_calib_copy(unsigned int const*, unsigned int*, long)") is None
+    assert counters.label_of("(anonymous namespace)::lx_gen(void*, long, long, unsigned int)") is None
+    assert counters.label_of("void lx::(anonymous namespace)::lx_small_sym<4>(lx::SmallSymArgs)") == "small_sym"
+
+
+def test_calibration_uses_the_plain_copy_kernel():
+    """The factor comes from the input library's copy kernel (1 GiB each
+    way per dispatch), not from the runtime's blits, whose counters scale
+    differently."""
+    from laplace_matvec_amd import counters
+    copy = "(anonymous namespace)::lx_calib_copy(unsigned int const*, unsigned int*, long)"
+    disp = [("__amd_rocclr_copyBuffer", 524308.0), (copy, 524288.0), (copy, 524290.0),
+            ("lx::lx_sort_hist(float const*)", 2.0e6)]
+    f = counters.calibration_factor(disp, counters.COPY_BYTES)
+    assert abs(f - (1 << 30) / (524289.0 * 1024.0)) < 1e-12
+    with pytest.raises(ValueError):
+        counters.calibration_factor([("__amd_rocclr_copyBuffer", 524308.0)], counters.COPY_BYTES)
     # every launch label in the sources is reachable from some kernel
     import re
     labels = set()
