@@ -53,10 +53,10 @@ constexpr int kGenThreads = 1024;
 // sin of its phase.  Inputs past the end go to a bin after the last
 // interval, so they are never visited.
 //
-// lx_bucket_sorted (per group of up to 8 vectors, one workgroup per group
-// and chunk of sub-chunks, the groups of a chunk on one die so that they
-// share its layout through that die's L2): the values of the group's vectors are placed
-// in LDS by slot, and thread j owns u_j and v_j of every vector in
+// lx_bucket_sorted (per group of 4 vectors, 8 with tie sums, one workgroup
+// per group and chunk of sub-chunks, the groups of a chunk on one die so
+// that they share its layout through that die's L2): the values of the
+// group's vectors are placed in LDS by slot, and thread j owns u_j and v_j of every vector in
 // registers: it adds the alpha parts of interval j and the beta parts of
 // interval j+1, slot by slot (LDS reads and FMAs only).  The
 // next sub-chunk's inputs load while the current one is accumulated.  No
@@ -68,7 +68,7 @@ constexpr int kGenThreads = 1024;
 constexpr int kSub = 2048;                      // inputs per sub-chunk
 constexpr int kSubItems = kSub / kGenThreads;   // 2 per thread
 constexpr int kGenWaves = kGenThreads / kWave;  // 16
-constexpr int kBucketVG = 8;                    // vectors per workgroup (max)
+constexpr int kBucketVG = 8;                    // vectors per workgroup (at most)
 constexpr int kBinStride = 1032;                // per-wave counter row: bins 0 .. n_out + 1 (<= 1025), padded
 
 __device__ __forceinline__ uint64_t match_bits11(uint32_t d) { return match_bits<11>(d); }
@@ -208,17 +208,21 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_layout(BucketArgs A, Bu
     }
 }
 
-template <int C, bool TIES>
-__global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, BucketLayout L, int VG, int groups,
-                                                               int64_t chunks, int64_t chunk_len)
+// VGT vectors per workgroup (8, or 4: half the LDS, so that two workgroups
+// share a CU and one's loads overlap the other's accumulation)
+template <int C, bool TIES, int VGT>
+__global__ __launch_bounds__(kGenThreads, VGT == 4 ? 8 : 4) void lx_bucket_sorted(BucketArgs A, BucketLayout L, int VG,
+                                                                                 int groups, int64_t chunks,
+                                                                                 int64_t chunk_len)
 {
     extern __shared__ float lds[];
+    constexpr int XW = VGT / 4;  // float4 words of vector values per slot
     const int no = (int)A.n_out;  // <= kGenThreads
     // intervals 0 .. no: thread t owns interval t; interval no has no thread
     // of its own when no == kGenThreads and goes to thread 0
     const bool last_extra = no == kGenThreads && threadIdx.x == 0;
-    float4* xs = reinterpret_cast<float4*>(lds);                // [kSub][2]: 8 vectors by slot
-    float4* cs = xs + 2 * kSub;                                 // [kSub]: factors by slot
+    float4* xs = reinterpret_cast<float4*>(lds);                // [kSub][XW]: the vectors by slot
+    float4* cs = xs + XW * kSub;                                // [kSub]: factors by slot
     uint8_t* ts = reinterpret_cast<uint8_t*>(cs + kSub);        // [kSub]: tie flags by slot (TIES)
 
     const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
@@ -228,14 +232,14 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, Bu
     const int64_t v0 = (int64_t)g * VG;
     const int nv = (int)((A.batch - v0) < VG ? (A.batch - v0) : VG);
 
-    float au[kBucketVG][C], av[kBucketVG][C];  // u_tid and v_tid of each vector
-    float at[TIES ? kBucketVG : 1][C];         // tie_tid
+    float au[VGT][C], av[VGT][C];  // u_tid and v_tid of each vector
+    float at[TIES ? VGT : 1][C];         // tie_tid
 #pragma unroll
-    for (int vi = 0; vi < kBucketVG; ++vi)
+    for (int vi = 0; vi < VGT; ++vi)
 #pragma unroll
         for (int c = 0; c < C; ++c) au[vi][c] = av[vi][c] = 0.f;
 #pragma unroll
-    for (int vi = 0; vi < (TIES ? kBucketVG : 1); ++vi)
+    for (int vi = 0; vi < (TIES ? VGT : 1); ++vi)
 #pragma unroll
         for (int c = 0; c < C; ++c) at[vi][c] = 0.f;
 
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, Bu
     // 128 w + 64 j + lane, and the starts of intervals tid .. tid + 2.
     // (Slots, flags and starts stay narrow until used: a widening next to
     // the load would make the accumulation wait for the whole prefetch.)
-    float xin[kSubItems][kBucketVG];
+    float xin[kSubItems][VGT];
     float cfn[kSubItems][4];
     uint8_t tfn[TIES ? kSubItems : 1];
     uint16_t sln[kSubItems], stn[4];
@@ -261,7 +265,7 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, Bu
             const int64_t id = base + p;
             const int64_t idc = id < j1 ? id : j0;  // a valid address; the value is not used
 #pragma unroll
-            for (int vi = 0; vi < kBucketVG; ++vi) {
+            for (int vi = 0; vi < VGT; ++vi) {
                 const int64_t vv = v0 + (vi < nv ? vi : 0);
                 xin[j][vi] = A.x[vv * A.n_in + idc];
             }
@@ -288,11 +292,12 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, Bu
             const int p = w * (kSubItems * kWave) + j * kWave + lane;
             if (sub0 + p < j1) {
                 const uint32_t sl = sln[j];
-                float x8[kBucketVG];
+                float x8[VGT];
 #pragma unroll
-                for (int vi = 0; vi < kBucketVG; ++vi) x8[vi] = vi < nv ? xin[j][vi] : 0.f;
-                xs[2 * sl] = make_float4(x8[0], x8[1], x8[2], x8[3]);
-                xs[2 * sl + 1] = make_float4(x8[4], x8[5], x8[6], x8[7]);
+                for (int vi = 0; vi < VGT; ++vi) x8[vi] = vi < nv ? xin[j][vi] : 0.f;
+#pragma unroll
+                for (int q = 0; q < XW; ++q)
+                    xs[XW * sl + q] = make_float4(x8[4 * q], x8[4 * q + 1], x8[4 * q + 2], x8[4 * q + 3]);
             }
             cs[p] = make_float4(cfn[j][0], cfn[j][1], cfn[j][2], cfn[j][3]);
             if (TIES) ts[p] = tfn[TIES ? j : 0];
@@ -305,10 +310,17 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, Bu
         if (tid <= no) {
             for (uint32_t sl = s0; sl < s1; ++sl) {
                 const float4 f = cs[sl];
-                const float4 xa = xs[2 * sl], xb = xs[2 * sl + 1];
-                const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+                float xv[VGT];
 #pragma unroll
-                for (int vi = 0; vi < kBucketVG; ++vi) {
+                for (int q = 0; q < XW; ++q) {
+                    const float4 xq = xs[XW * sl + q];
+                    xv[4 * q] = xq.x;
+                    xv[4 * q + 1] = xq.y;
+                    xv[4 * q + 2] = xq.z;
+                    xv[4 * q + 3] = xq.w;
+                }
+#pragma unroll
+                for (int vi = 0; vi < VGT; ++vi) {
                     au[vi][0] = fmaf(f.x, xv[vi], au[vi][0]);
                     if (C == 2) au[vi][C - 1] = fmaf(f.y, xv[vi], au[vi][C - 1]);
                     av[vi][0] = fmaf(f.z, xv[vi], av[vi][0]);
@@ -317,7 +329,7 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, Bu
                 if (TIES) {  // a tie's alpha is exactly 1: its factors are the phase's cos, sin
                     const float tw = ts[sl] ? 1.f : 0.f;
 #pragma unroll
-                    for (int vi = 0; vi < (TIES ? kBucketVG : 1); ++vi) {
+                    for (int vi = 0; vi < (TIES ? VGT : 1); ++vi) {
                         at[vi][0] = fmaf(tw * f.x, xv[vi], at[vi][0]);
                         if (C == 2) at[vi][C - 1] = fmaf(tw * f.y, xv[vi], at[vi][C - 1]);
                     }
@@ -328,10 +340,17 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, Bu
         // kept by thread 0 (whose own interval 0 has none)
         for (uint32_t sl = e0; sl < e1; ++sl) {
             const float2 f = *reinterpret_cast<const float2*>(&cs[sl].z);
-            const float4 xa = xs[2 * sl], xb = xs[2 * sl + 1];
-            const float xv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+            float xv[VGT];
 #pragma unroll
-            for (int vi = 0; vi < kBucketVG; ++vi) {
+            for (int q = 0; q < XW; ++q) {
+                const float4 xq = xs[XW * sl + q];
+                xv[4 * q] = xq.x;
+                xv[4 * q + 1] = xq.y;
+                xv[4 * q + 2] = xq.z;
+                xv[4 * q + 3] = xq.w;
+            }
+#pragma unroll
+            for (int vi = 0; vi < VGT; ++vi) {
                 av[vi][0] = fmaf(f.x, xv[vi], av[vi][0]);
                 if (C == 2) av[vi][C - 1] = fmaf(f.y, xv[vi], av[vi][C - 1]);
             }
@@ -343,7 +362,7 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, Bu
     // kept interval no
     const int vt = tid > 0 ? tid - 1 : (last_extra ? no - 1 : -1);
 #pragma unroll
-    for (int vi = 0; vi < kBucketVG; ++vi)
+    for (int vi = 0; vi < VGT; ++vi)
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             if (vi >= nv) continue;
@@ -356,12 +375,18 @@ __global__ __launch_bounds__(kGenThreads) void lx_bucket_sorted(BucketArgs A, Bu
         }
 }
 
-static size_t bucket_sorted_lds(int64_t no, int C, bool ties)
+static size_t bucket_sorted_lds(int64_t no, int C, bool ties, int vg = kBucketVG)
 {
     (void)no;
     (void)C;
-    return (size_t)kSub * 32 + (size_t)kSub * 16 + (ties ? (size_t)kSub : 0);
+    return (size_t)kSub * 4 * (vg <= 4 ? 4 : 8) + (size_t)kSub * 16 + (ties ? (size_t)kSub : 0);
 }
+
+// Vectors per bucketing workgroup.  Four (32 KB of vector slots, 64 VGPRs):
+// two workgroups share a CU and one's loads overlap the other's
+// accumulation; general n=2^26, k=1024, 64 phased vectors: 8.0 -> 6.3 ms.
+// With the tie sums of a gradient the four-vector form spills, so eight.
+static int bucket_vg(bool ties) { return ties ? kBucketVG : 4; }
 
 // Sums the per-workgroup partials in chunk order (float64) into u, v and,
 // with P = 3, the tie sums.
@@ -387,15 +412,16 @@ __global__ __launch_bounds__(256) void lx_bucket_reduce(const float* __restrict_
 
 static void bucket_shape(const BucketArgs& a, int* vg, int* groups, int* chunks, int64_t* chunk_len)
 {
+    const int vmax = bucket_vg(a.ties);
     const bool fits = a.n_out <= kGenThreads && a.lds_bytes > 0 &&
-                      (int64_t)bucket_sorted_lds(a.n_out, a.channels, a.ties) <= a.lds_bytes;
+                      (int64_t)bucket_sorted_lds(a.n_out, a.channels, a.ties, vmax) <= a.lds_bytes;
     if (!fits) {
         *vg = 0;
         *groups = *chunks = 0;
         *chunk_len = 0;
         return;
     }
-    int64_t v = kBucketVG;
+    int64_t v = vmax;
     if (v > a.batch) v = a.batch;
     *vg = (int)v;
     *groups = (int)((a.batch + v - 1) / v);
@@ -432,18 +458,24 @@ hipError_t bucket_launch(BucketArgs& a, hipStream_t s)
     const bool ties = a.ties;
     if (ties && !a.tie) return hipErrorInvalidValue;
     if (vg > 0 && a.partial && a.layout && a.n_in > 0) {
-        const size_t shmem = bucket_sorted_lds(a.n_out, a.channels, ties);
+        const size_t shmem = bucket_sorted_lds(a.n_out, a.channels, ties, vg);
         const unsigned blocks = (unsigned)die_chunk_group_blocks(chunks, groups);
         const BucketLayout L = bucket_layout_at(a.layout, a.n_in, a.n_out, ties);
         const unsigned subs = (unsigned)((a.n_in + kSub - 1) / kSub);
         if (two) LX_LAUNCH("bucket_layout", s, (lx_bucket_layout<2><<<subs, kGenThreads, 0, s>>>(a, L)));
         else LX_LAUNCH("bucket_layout", s, (lx_bucket_layout<1><<<subs, kGenThreads, 0, s>>>(a, L)));
-#define LX_BKS(CC, TT)                                                                                         \
+#define LX_BKS1(CC, TT, VV)                                                                                    \
     do {                                                                                                       \
-        (void)hipFuncSetAttribute((const void*)lx_bucket_sorted<CC, TT>, hipFuncAttributeMaxDynamicSharedMemorySize, \
-                                  (int)shmem);                                                                 \
+        (void)hipFuncSetAttribute((const void*)lx_bucket_sorted<CC, TT, VV>,                                   \
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);                     \
         LX_LAUNCH("bucket_sorted", s,                                                                          \
-                  (lx_bucket_sorted<CC, TT><<<blocks, kGenThreads, shmem, s>>>(a, L, vg, groups, chunks, chunk_len))); \
+                  (lx_bucket_sorted<CC, TT, VV><<<blocks, kGenThreads, shmem, s>>>(a, L, vg, groups, chunks,   \
+                                                                                   chunk_len)));               \
+    } while (0)
+#define LX_BKS(CC, TT)                     \
+    do {                                   \
+        if (vg <= 4) LX_BKS1(CC, TT, 4);   \
+        else LX_BKS1(CC, TT, 8);           \
     } while (0)
         if (two) {
             if (ties) LX_BKS(2, true);
@@ -453,6 +485,7 @@ hipError_t bucket_launch(BucketArgs& a, hipStream_t s)
             else LX_BKS(1, false);
         }
 #undef LX_BKS
+#undef LX_BKS1
         const int P = ties ? 3 : 2;
         const int64_t total = a.batch * a.channels * P * a.n_out;
         int64_t rb = (total + 255) / 256;
