@@ -332,9 +332,10 @@ struct laplex_plan_s {
     // permutations (rank -> original index), made from the records on demand
     uint32_t* pa = nullptr;
     uint32_t* pb = nullptr;
-    // Gram: first sorted-b position of every interval of the sorted a, made
-    // on the first gram call
+    // Gram: first sorted-b position of every interval of the sorted a, and
+    // the rank of each original index of a, made on the first gram call
     uint32_t* gbound = nullptr;
+    uint32_t* grank = nullptr;
     // copies in original order (general only)
     float* a0 = nullptr;
     float* b0 = nullptr;
@@ -1505,6 +1506,12 @@ laplex_status laplex_gram(laplex_plan p, const float* D, float* M, void* stream)
         LX_TRY(lx::gram_bounds_launch(p->sa, p->n, p->sb, p->k, (uint32_t*)gb, s), "gram bounds");
         p->gbound = (uint32_t*)gb;
     }
+    if (!p->grank) {
+        void* gr = nullptr;
+        LX_TRY(plan_alloc(p, &gr, (size_t)p->n * 4, s), "alloc gram ranks");
+        LX_TRY(lx::gram_ranks_launch(p->pa, p->n, (uint32_t*)gr, s), "gram ranks");
+        p->grank = (uint32_t*)gr;
+    }
     LX_TRY(ensure_ws(p, lx::gram_scratch_bytes(p->n, p->k, p->phased ? 3 : 1), s), "workspace");
     lx::GramArgs G;
     G.n = p->n;
@@ -1516,6 +1523,7 @@ laplex_status laplex_gram(laplex_plan p, const float* D, float* M, void* stream)
     G.pb = p->pb;
     G.D = D;
     G.bound = p->gbound;
+    G.rank_a = p->grank;
     if (p->phased) {
         G.cphi_r = p->cphi;
         G.sphi_r = p->sphi;

@@ -26,18 +26,20 @@
 //
 //   lx_gram_bounds : once per plan, the first sorted-b position of every
 //                    interval (bisection of each a over the sorted b);
+//   lx_gram_ranks  : once per plan, the rank of each original index of a;
 //   lx_gram_bins   : one workgroup per interval: its run of sorted b summed
 //                    (sigma, p, q per weight set) in float64 and a fixed
 //                    order, and the decay between the interval's two a;
-//   lx_gram_scan   : one workgroup: S, P, Q over the intervals, written as
-//                    stats by original index;
-//   lx_gram_tile   : 64 x 64 tiles of M in the original order, O(1) per entry.
+//   lx_gram_scan   : one workgroup: S, P, Q over the intervals, written by
+//                    rank in coalesced runs;
+//   lx_gram_tile   : 64 x 64 tiles of M in the original order, O(1) per entry,
+//                    each row's and column's stats fetched through its rank.
 #include "lx_device.h"
 #include "lx_internal.h"
 
 namespace lx {
 
-constexpr int kGramScanThreads = 256;
+constexpr int kGramScanThreads = 512;
 constexpr int kGT = 64;  // tile edge
 
 // Weight sets: one (D) for the plain operator; three for a phased one,
@@ -50,7 +52,7 @@ constexpr int gram_stride() { return 1 + 3 * NW + (NW == 3 ? 2 : 0); }
 
 // Scratch (doubles, 256-byte aligned regions):
 //   sigma [NW][n+1], p [NW][n], q [NW][n], mdec [n] (e^{-2(s_r - s_{r-1})/t}),
-//   st [n][SW] (stats by original index)
+//   st [n][3 NW] (P, S, Q of each weight set, by rank)
 struct GramScratch {
     double *sigma, *p, *q, *mdec, *st;
 };
@@ -185,105 +187,125 @@ __global__ __launch_bounds__(kBinThreads) void lx_gram_bins(GramArgs A, GramScra
     }
 }
 
-// One workgroup: S, P and Q over the intervals, written as stats by
-// original index.  Each thread takes rounds of kGramRun consecutive ranks
-// with every load of a round issued before any is used.
-constexpr int kGramRun = 16;
+// One workgroup: S, P and Q over the intervals, written by rank, 3 NW
+// doubles per rank (P, S, Q of each weight set), in coalesced runs.  Each
+// thread takes rounds of kGramRun consecutive ranks with every load of a
+// round issued before any is used.
+template <int NW>
+constexpr int gram_run() { return NW == 3 ? 4 : 8; }  // three weight sets hold three times the values
 
 template <int NW>
 __global__ __launch_bounds__(kGramScanThreads) void lx_gram_scan(GramArgs A, GramScratch G)
 {
-    __shared__ Aff<double> sh[kGramScanThreads / kWave];
-    constexpr int SW = gram_stride<NW>();
+    constexpr int kGramRun = gram_run<NW>();
+    constexpr int kWaves = kGramScanThreads / kWave;
+    constexpr int SR = 3 * NW;  // doubles per rank
+    __shared__ Aff<double> sh[kWaves];
     const int tid = threadIdx.x;
     const int64_t n = A.n;
-
-    // ---- scans over the intervals, in rounds of kGramScanThreads * kGramRun ranks
     constexpr int64_t kRound = (int64_t)kGramScanThreads * kGramRun;
-    const float* s = A.sa;
     double* st = G.st;
-#pragma unroll 1
-    for (int w = 0; w < NW; ++w) {
-        const double* sg = G.sigma + w * (n + 1);
-        const double* pw = G.p + w * n;
-        const double* qw = G.q + w * n;
-        double carS = 0.0, carP = 0.0;
-#pragma unroll 1
-        for (int64_t base = 0; base < n; base += kRound) {
-            const int64_t r0 = base + (int64_t)tid * kGramRun;
-            double vs[kGramRun], vp[kGramRun], m[kGramRun];
+
+    // the values carried in from earlier rounds (the same in every thread)
+    double carS[NW], carP[NW], carQ[NW];
 #pragma unroll
-            for (int i = 0; i < kGramRun; ++i) {
-                const int64_t r = r0 + i;
-                const bool ok = r < n;
-                vs[i] = ok ? sg[r] : 0.0;
-                vp[i] = ok ? pw[r] : 0.0;
-                m[i] = ok ? G.mdec[r] : 1.0;
+    for (int w = 0; w < NW; ++w) carS[w] = carP[w] = carQ[w] = 0.0;
+
+    // ---- forward: S_r = S_{r-1} + sigma_r, P_r = e^{-2 d_{r-1}} P_{r-1} + p_r
+#pragma unroll 1
+    for (int64_t base = 0; base < n; base += kRound) {
+        const int64_t r0 = base + (int64_t)tid * kGramRun;
+        double vs[NW][kGramRun], vp[NW][kGramRun], m[kGramRun];
+#pragma unroll
+        for (int i = 0; i < kGramRun; ++i) {
+            const int64_t r = r0 + i;
+            const bool ok = r < n;
+            const int64_t rc = ok ? r : 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                vs[w][i] = ok ? G.sigma[w * (n + 1) + rc] : 0.0;
+                vp[w][i] = ok ? G.p[w * n + rc] : 0.0;
             }
+            m[i] = ok ? G.mdec[rc] : 1.0;
+        }
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
             Aff<double> S = aff_identity<double>(), P = aff_identity<double>();
 #pragma unroll
             for (int i = 0; i < kGramRun; ++i) {
-                S = compose(S, Aff<double>{1.0, vs[i]});
-                P = compose(P, Aff<double>{m[i], vp[i]});
+                S = compose(S, Aff<double>{1.0, vs[w][i]});
+                P = compose(P, Aff<double>{m[i], vp[w][i]});
             }
             Aff<double> totS, totP;
-            const Aff<double> xS = block_exscan_up<double, kGramScanThreads / kWave>(S, sh, totS);
-            const Aff<double> xP = block_exscan_up<double, kGramScanThreads / kWave>(P, sh, totP);
-            double runS = xS.m * carS + xS.v, runP = xP.m * carP + xP.v;
-            carS = totS.m * carS + totS.v;
-            carP = totP.m * carP + totP.v;
+            const Aff<double> xS = block_exscan_up<double, kWaves>(S, sh, totS);
+            const Aff<double> xP = block_exscan_up<double, kWaves>(P, sh, totP);
+            double runS = xS.m * carS[w] + xS.v, runP = xP.m * carP[w] + xP.v;
+            carS[w] = totS.m * carS[w] + totS.v;
+            carP[w] = totP.m * carP[w] + totP.v;
 #pragma unroll
             for (int i = 0; i < kGramRun; ++i) {
-                const int64_t r = r0 + i;
-                runS += vs[i];
-                runP = m[i] * runP + vp[i];
-                if (r < n) {
-                    double* o = st + (int64_t)A.pa[r] * SW;
-                    o[1 + 3 * w] = runP;
-                    o[2 + 3 * w] = runS;
-                    if (w == 0) {
-                        o[0] = (double)s[r];
-                        if (NW == 3) {
-                            o[SW - 2] = A.cphi_r[r];
-                            o[SW - 1] = A.sphi_r[r];
-                        }
-                    }
+                runS += vs[w][i];
+                runP = m[i] * runP + vp[w][i];
+                if (r0 + i < n) {
+                    double* o = st + (r0 + i) * SR + 3 * w;
+                    o[0] = runP;
+                    o[1] = runS;
                 }
             }
         }
-        // backward: Q_r = e^{-2 (s_{r+1} - s_r)} Q_{r+1} + q_r, rounds from the top
-        double carQ = 0.0;
-        const int64_t rounds = (n + kRound - 1) / kRound;
+    }
+
+    // ---- backward: Q_r = e^{-2 (s_{r+1} - s_r)} Q_{r+1} + q_r, rounds from the top
+    const int64_t rounds = (n + kRound - 1) / kRound;
 #pragma unroll 1
-        for (int64_t rd = rounds - 1; rd >= 0; --rd) {
-            const int64_t r0 = rd * kRound + (int64_t)tid * kGramRun;
-            double vq[kGramRun], m1[kGramRun];
+    for (int64_t rd = rounds - 1; rd >= 0; --rd) {
+        const int64_t r0 = rd * kRound + (int64_t)tid * kGramRun;
+        double vq[NW][kGramRun], m1[kGramRun];
 #pragma unroll
-            for (int i = 0; i < kGramRun; ++i) {
-                const int64_t r = r0 + i;
-                vq[i] = r < n ? qw[r] : 0.0;
-                m1[i] = r + 1 < n ? G.mdec[r + 1] : (r + 1 == n ? 0.0 : 1.0);
-            }
+        for (int i = 0; i < kGramRun; ++i) {
+            const int64_t r = r0 + i;
+            const int64_t rc = r < n ? r : 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) vq[w][i] = r < n ? G.q[w * n + rc] : 0.0;
+            m1[i] = r + 1 < n ? G.mdec[r + 1] : (r + 1 == n ? 0.0 : 1.0);
+        }
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
             Aff<double> Q = aff_identity<double>();
 #pragma unroll
-            for (int i = kGramRun - 1; i >= 0; --i) Q = compose(Q, Aff<double>{m1[i], vq[i]});
+            for (int i = kGramRun - 1; i >= 0; --i) Q = compose(Q, Aff<double>{m1[i], vq[w][i]});
             Aff<double> totQ;
-            const Aff<double> xQ = block_exscan_down<double, kGramScanThreads / kWave>(Q, sh, totQ);
-            double runQ = xQ.m * carQ + xQ.v;
-            carQ = totQ.m * carQ + totQ.v;
+            const Aff<double> xQ = block_exscan_down<double, kWaves>(Q, sh, totQ);
+            double runQ = xQ.m * carQ[w] + xQ.v;
+            carQ[w] = totQ.m * carQ[w] + totQ.v;
 #pragma unroll
             for (int i = kGramRun - 1; i >= 0; --i) {
-                const int64_t r = r0 + i;
-                runQ = m1[i] * runQ + vq[i];
-                if (r < n) st[(int64_t)A.pa[r] * SW + 3 + 3 * w] = runQ;
+                runQ = m1[i] * runQ + vq[w][i];
+                if (r0 + i < n) st[(r0 + i) * SR + 3 * w + 2] = runQ;
             }
         }
     }
 }
 
+// rank[perm[r]] = r: the rank of each original index.
+__global__ __launch_bounds__(256) void lx_gram_ranks(const uint32_t* __restrict__ perm, int64_t n,
+                                                    uint32_t* __restrict__ rank)
+{
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r < n) rank[perm[r]] = (uint32_t)r;
+}
+
+hipError_t gram_ranks_launch(const uint32_t* perm, int64_t n, uint32_t* rank, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    LX_LAUNCH("gram_ranks", s, (lx_gram_ranks<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(perm, n, rank)));
+    return hipSuccess;
+}
+
 // Tiles of M, 64 x 64 entries in the original order.  Thread (column jj,
 // row group) computes column jj of 16 rows and stores a wave's 64 columns
-// of one row at once.  With lo / hi the entry's smaller / larger anchor,
+// of one row at once.  The stats of a row or column come by its rank
+// (the rank of each original index is kept with the plan).  With lo / hi the entry's smaller / larger anchor,
 //   M = e^{-(hi - lo)/t} (P_lo + (S_hi - S_lo) + Q_hi)
 // (weight sets combined with the cos/sin of phi when phased).  When the
 // tile's anchors span at most 600 t, the decay is split around the tile's
@@ -293,9 +315,11 @@ __global__ __launch_bounds__(kGramScanThreads) void lx_gram_scan(GramArgs A, Gra
 // equal anchors, so small entries next to a large S keep their precision.)
 // Otherwise, and at t = 0, each entry takes its own decay.
 template <int NW>
-__global__ __launch_bounds__(256) void lx_gram_tile(const double* __restrict__ st, int64_t n, double inv_t,
-                                                   float* __restrict__ M)
+__global__ __launch_bounds__(256) void lx_gram_tile(GramArgs A, const double* __restrict__ st)
 {
+    const int64_t n = A.n;
+    const double inv_t = A.inv_t;
+    float* __restrict__ M = A.M;
     constexpr int SW = gram_stride<NW>();
     constexpr int FW = SW + 2;  // a, E+, E-, then the stats after a: (P, S, Q) per set, (cos, sin)
     __shared__ double rs[kGT][SW];
@@ -304,10 +328,25 @@ __global__ __launch_bounds__(256) void lx_gram_tile(const double* __restrict__ s
     __shared__ float sred[4][2];
     const int tid = threadIdx.x;
     const int64_t i0 = (int64_t)blockIdx.y * kGT, j0 = (int64_t)blockIdx.x * kGT;
-    for (int t = tid; t < kGT * SW; t += 256) {
-        const int e = t / SW, f = t % SW;
-        rs[e][f] = (i0 + e < n) ? st[(i0 + e) * SW + f] : 0.0;
-        cs[e][f] = (j0 + e < n) ? st[(j0 + e) * SW + f] : 0.0;
+    // the stats of the tile's 64 rows and 64 columns, by rank: the anchor,
+    // (P, S, Q) per weight set, then the phase factors
+    for (int t = tid; t < 2 * kGT; t += 256) {
+        const int e = t % kGT;
+        const int64_t i = (t < kGT ? i0 : j0) + e;
+        double* o = t < kGT ? rs[e] : cs[e];
+        if (i < n) {
+            const uint32_t r = A.rank_a[i];
+            o[0] = (double)A.sa[r];
+#pragma unroll
+            for (int q = 0; q < 3 * NW; ++q) o[1 + q] = st[(int64_t)r * (3 * NW) + q];
+            if (NW == 3) {
+                o[SW - 2] = A.cphi_r[r];
+                o[SW - 1] = A.sphi_r[r];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < SW; ++q) o[q] = 0.0;
+        }
     }
     __syncthreads();
     // the tile's anchor range (valid rows and columns only), for the centre
@@ -410,7 +449,7 @@ static hipError_t gram_launch_t(const GramArgs& a, hipStream_t s)
     LX_LAUNCH("gram_bins", s, (lx_gram_bins<NW><<<(unsigned)(a.n + 1), kBinThreads, 0, s>>>(a, G)));
     LX_LAUNCH("gram_scan", s, (lx_gram_scan<NW><<<1, kGramScanThreads, 0, s>>>(a, G)));
     const unsigned nb = (unsigned)((a.n + kGT - 1) / kGT);
-    LX_LAUNCH("gram_tile", s, (lx_gram_tile<NW><<<dim3(nb, nb), 256, 0, s>>>(G.st, a.n, a.inv_t, a.M)));
+    LX_LAUNCH("gram_tile", s, (lx_gram_tile<NW><<<dim3(nb, nb), 256, 0, s>>>(a, G.st)));
     return hipSuccess;
 }
 

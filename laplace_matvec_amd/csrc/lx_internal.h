@@ -329,6 +329,7 @@ struct GramArgs {
     const uint32_t* pb = nullptr;   // perm of b
     const float* D = nullptr;       // [k], original order of b
     const uint32_t* bound = nullptr;  // [n + 2]: interval r is sorted b [bound[r], bound[r+1])
+    const uint32_t* rank_a = nullptr;  // [n]: rank of each original index of a
     const float* cphi_r = nullptr;  // phased: cos/sin of phi by rank of a, of psi by rank of b
     const float* sphi_r = nullptr;
     const float* cpsi_r = nullptr;
@@ -340,6 +341,8 @@ size_t gram_scratch_bytes(int64_t n, int64_t k, int weight_sets);
 // bound[r] = #{b <= s_{r-1}} (r = 1 .. n), bound[0] = 0, bound[n+1] = k.
 hipError_t gram_bounds_launch(const float* sa, int64_t n, const float* sb, int64_t k, uint32_t* bound,
                               hipStream_t s);
+// rank[perm[r]] = r for r < n.
+hipError_t gram_ranks_launch(const uint32_t* perm, int64_t n, uint32_t* rank, hipStream_t s);
 hipError_t gram_launch(const GramArgs& a, hipStream_t s);
 
 }  // namespace lx
