@@ -2,6 +2,10 @@
 
 Outputs, next to this file:
   liblaplex.so         the operator library (C ABI of include/laplex.h)
+  liblaplex_stress.so  the same library with 4096-key sort tiles and a
+                       look-back that reads one predecessor per round: twice
+                       the tiles and the longest look-back walks, for the
+                       sort stress test only
   liblaplex_inputs.so  the device input generator (Philox4x32-10) and a
                        plain copy kernel for counter calibration, kept
                        separate because they are not part of the operator
@@ -32,9 +36,14 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+STRESS_DEFINES = ["-DLX_SORT_THREADS=256", "-DLX_SORT_ITEMS=16", "-DLX_LOOKBACK=1"]
+
+
+def _compile(src: str, variant: str = "", defines: tuple = ()) -> str:
+    out_dir = os.path.join(BUILD, variant) if variant else BUILD
+    os.makedirs(out_dir, exist_ok=True)
+    obj = os.path.join(out_dir, os.path.splitext(os.path.basename(src))[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *defines, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -59,9 +68,12 @@ def build(jobs: int = 8) -> list[str]:
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         lib_objs = list(ex.map(_compile, LIB_SOURCES))
         in_objs = list(ex.map(_compile, INPUT_SOURCES))
-    outs = [os.path.join(PKG, "liblaplex.so"), os.path.join(PKG, "liblaplex_inputs.so")]
+        stress_objs = list(ex.map(lambda f: _compile(f, "stress", tuple(STRESS_DEFINES)), LIB_SOURCES))
+    outs = [os.path.join(PKG, "liblaplex.so"), os.path.join(PKG, "liblaplex_inputs.so"),
+            os.path.join(PKG, "liblaplex_stress.so")]
     _link(lib_objs, outs[0])
     _link(in_objs, outs[1])
+    _link(stress_objs, outs[2])
     return outs
 
 

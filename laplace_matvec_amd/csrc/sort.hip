@@ -701,7 +701,7 @@ struct PairShared {
 
 // Builds the merged order of tiles t0 and t0 + 1 (ntile of them exist) and
 // returns, for merged slot m = q * kPairThreads + tid, its tile-pair
-// position src = tile << 13 | position (two per word in srcp) and its global
+// position src = tile * kSortTile + position (two per word in srcp) and its global
 // position dst (0xFFFFFFFF past the pair's slots).  A slot past the pair
 // (one tile only) gets src = m, a position of the absent second tile.  Slots
 // whose dst is n or more hold the padding of the last tile: every pass sorts
@@ -718,6 +718,9 @@ __device__ __forceinline__ void pair_maps(PairShared& S, const uint16_t* __restr
     uint16_t* msrc = reinterpret_cast<uint16_t*>(sbin + 2 * kSortTile);  // [2 kSortTile]
     uint8_t* mbin = reinterpret_cast<uint8_t*>(msrc + 2 * kSortTile);    // [2 kSortTile]
     static_assert(2 * kSortTile + 4 * kSortTile + 2 * kSortTile <= (int)sizeof(S.words), "map layout");
+    static_assert(2 * kSortTile <= 65536, "tile-pair positions are packed in 16 bits");
+    static_assert(kPairThreads * 16 == 2 * kSortTile && kSortThreads * 16 == kSortTile,
+                  "each thread clears and scans 16 bytes of the bin maps");
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int h = tid / kSortThreads;  // tile of the pair this thread maps
@@ -730,7 +733,7 @@ __device__ __forceinline__ void pair_maps(PairShared& S, const uint16_t* __restr
 #pragma unroll
         for (int q = 0; q < kReplayItems; ++q) pos[q] = rec[(t0 + h) * kSortTile + q * kSortThreads + ht];
     }
-    reinterpret_cast<uint4*>(sbin)[tid] = make_uint4(0u, 0u, 0u, 0u);  // 1024 x 16 B = both tiles' bin maps
+    reinterpret_cast<uint4*>(sbin)[tid] = make_uint4(0u, 0u, 0u, 0u);  // 16 B per thread: both tiles' bin maps
     if (ht < kRadix) {
         const bool have = h < ntile;
         S.start[h][ht] = have ? tab_start[(t0 + h) * kRadix + ht] : 0u;
@@ -782,7 +785,7 @@ __device__ __forceinline__ void pair_maps(PairShared& S, const uint16_t* __restr
             const uint32_t i = (uint32_t)(q * kSortThreads + ht);
             const uint32_t b = sbin[h * kSortTile + i];
             const uint32_t m = i + (h == 0 ? S.start[1][b] : S.start[0][b + 1]);
-            msrc[m] = (uint16_t)(pos[q] | ((uint32_t)h << 13));
+            msrc[m] = (uint16_t)(pos[q] + (uint32_t)h * kSortTile);
             mbin[m] = (uint8_t)b;
         }
     }
