@@ -336,6 +336,12 @@ struct laplex_plan_s {
     // the rank of each original index of a, made on the first gram call
     uint32_t* gbound = nullptr;
     uint32_t* grank = nullptr;
+    // Gram: b's inputs split by original index into one slice per die
+    uint32_t* gslice_off = nullptr;
+    uint32_t* gslice_src = nullptr;
+    float* gslice_b = nullptr;
+    float* gslice_c = nullptr;
+    float* gslice_s = nullptr;
     // copies in original order (general only)
     float* a0 = nullptr;
     float* b0 = nullptr;
@@ -1530,6 +1536,28 @@ laplex_status laplex_gram(laplex_plan p, const float* D, float* M, void* stream)
         G.cpsi_r = p->cpsi;
         G.spsi_r = p->spsi;
     }
+    if (!p->gslice_off) {
+        void *off = nullptr, *src = nullptr, *bv = nullptr, *cv = nullptr, *sv = nullptr;
+        LX_TRY(plan_alloc(p, &off, ((size_t)lx::kGramSlices * (p->n + 1) + 1) * 4, s), "alloc gram slices");
+        LX_TRY(plan_alloc(p, &src, (size_t)p->k * 4, s), "alloc gram slices");
+        LX_TRY(plan_alloc(p, &bv, (size_t)p->k * 4, s), "alloc gram slices");
+        if (p->phased) {
+            LX_TRY(plan_alloc(p, &cv, (size_t)p->k * 4, s), "alloc gram slices");
+            LX_TRY(plan_alloc(p, &sv, (size_t)p->k * 4, s), "alloc gram slices");
+        }
+        LX_TRY(lx::gram_slices_launch(G, (uint32_t*)off, (uint32_t*)src, (float*)bv, (float*)cv, (float*)sv, s),
+               "gram slices");
+        p->gslice_off = (uint32_t*)off;
+        p->gslice_src = (uint32_t*)src;
+        p->gslice_b = (float*)bv;
+        p->gslice_c = (float*)cv;
+        p->gslice_s = (float*)sv;
+    }
+    G.slice_off = p->gslice_off;
+    G.slice_src = p->gslice_src;
+    G.slice_b = p->gslice_b;
+    G.slice_c = p->gslice_c;
+    G.slice_s = p->gslice_s;
     G.stats = (double*)p->ws;
     G.M = M;
     LX_TRY(lx::gram_launch(G, s), "gram");

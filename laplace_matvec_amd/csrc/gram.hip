@@ -52,9 +52,10 @@ constexpr int gram_stride() { return 1 + 3 * NW + (NW == 3 ? 2 : 0); }
 
 // Scratch (doubles, 256-byte aligned regions):
 //   sigma [NW][n+1], p [NW][n], q [NW][n], mdec [n] (e^{-2(s_r - s_{r-1})/t}),
-//   st [n][3 NW] (P, S, Q of each weight set, by rank)
+//   st [n][3 NW] (P, S, Q of each weight set, by rank),
+//   part [slice][3 NW][n+1] (each slice's sums per interval)
 struct GramScratch {
-    double *sigma, *p, *q, *mdec, *st;
+    double *sigma, *p, *q, *mdec, *st, *part;
 };
 
 static inline size_t al256g(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -67,7 +68,8 @@ static GramScratch gram_scratch_at(void* base, int64_t n, int nw)
     g.p = (double*)c; c += al256g((size_t)nw * n * 8);
     g.q = (double*)c; c += al256g((size_t)nw * n * 8);
     g.mdec = (double*)c; c += al256g((size_t)n * 8);
-    g.st = (double*)c;
+    g.st = (double*)c; c += al256g((size_t)n * (1 + 3 * nw + (nw == 3 ? 2 : 0)) * 8);
+    g.part = (double*)c;
     return g;
 }
 
@@ -76,7 +78,7 @@ size_t gram_scratch_bytes(int64_t n, int64_t k, int nw)
     (void)k;
     const int sw = 1 + 3 * nw + (nw == 3 ? 2 : 0);
     return al256g((size_t)nw * (n + 1) * 8) + 2 * al256g((size_t)nw * n * 8) + al256g((size_t)n * 8) +
-           al256g((size_t)n * sw * 8);
+           al256g((size_t)n * sw * 8) + al256g((size_t)kGramSlices * 3 * nw * (n + 1) * 8);
 }
 
 // bound[r] = #{l : b_l <= s_{r-1}} for r = 1 .. n, bound[0] = 0,
@@ -97,46 +99,163 @@ hipError_t gram_bounds_launch(const float* sa, int64_t n, const float* sb, int64
     return hipSuccess;
 }
 
-// Interval r: thread tid takes sorted b positions lo + tid, lo + tid + 256,
-// ... in rounds of kBinLoads with every load of a round in flight before any
-// is used; the per-thread sums are folded over the workgroup in a fixed
-// order (wave shuffles, then the waves in order).
+// ---------------------------------------------------------------- slices
+//
+// The weights D arrive in the original order of b, and an interval's inputs
+// sit at random original indices: gathering D for sorted b pulls a whole
+// cache line per 4-byte weight from all of D.  So the inputs are split by
+// original index into kGramSlices ranges, one per compute die, and each
+// interval's inputs of one slice are stored together (made once per plan):
+// the workgroups summing slice s run on die s, whose L2 then holds the
+// 1/8 of D they gather from.  Each slice gives partial sums per interval;
+// a fold adds the slices in a fixed order, so results stay deterministic.
+
+__device__ __forceinline__ uint32_t gram_slice_of(uint32_t l, int64_t k)
+{
+    return (uint32_t)(((uint64_t)l * kGramSlices) / (uint64_t)k);
+}
+
+// cnt[s (n+1) + r] = inputs of interval r in slice s; one workgroup per interval.
+__global__ __launch_bounds__(256) void lx_gram_slice_count(const uint32_t* __restrict__ pb,
+                                                          const uint32_t* __restrict__ bound, int64_t n,
+                                                          int64_t k, uint32_t* __restrict__ cnt)
+{
+    __shared__ uint32_t sc[kGramSlices];
+    const int tid = threadIdx.x;
+    const int64_t r = blockIdx.x;
+    if (tid < kGramSlices) sc[tid] = 0;
+    __syncthreads();
+    uint32_t c[kGramSlices] = {};
+    for (int64_t j = bound[r] + tid; j < bound[r + 1]; j += 256) {
+        const uint32_t sl = gram_slice_of(pb[j], k);
+#pragma unroll
+        for (int q = 0; q < kGramSlices; ++q) c[q] += sl == (uint32_t)q ? 1u : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < kGramSlices; ++q) {
+        uint32_t x = c[q];
+#pragma unroll
+        for (int d = kWave / 2; d > 0; d >>= 1) x += __shfl_down(x, d);
+        if (lane_id() == 0 && x) atomicAdd(&sc[q], x);  // integer sums: any order gives the same
+    }
+    __syncthreads();
+    if (tid < kGramSlices) cnt[(int64_t)tid * (n + 1) + r] = sc[tid];
+}
+
+// In place: off[i] = sum of cnt[0 .. i), off[len] = the total (one workgroup).
+__global__ __launch_bounds__(1024) void lx_gram_slice_scan(uint32_t* __restrict__ off, int64_t len)
+{
+    __shared__ uint32_t sh[1024 / kWave];
+    uint32_t carry = 0;
+    for (int64_t base = 0; base < len; base += 1024) {
+        const int64_t i = base + threadIdx.x;
+        const uint32_t v = i < len ? off[i] : 0u;
+        uint32_t tot;
+        const uint32_t ex = block_exsum_u32<1024 / kWave>(v, sh, tot);
+        if (i < len) off[i] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) off[len] = carry;
+}
+
+// Places every input of interval r at its slice's next free position, in
+// ascending sorted position within each (slice, interval): the original
+// index, b, and (phased) the cos / sin of psi.  One workgroup per interval.
+__global__ __launch_bounds__(256) void lx_gram_slice_place(GramArgs A, const uint32_t* __restrict__ off,
+                                                          uint32_t* __restrict__ s_src, float* __restrict__ s_b,
+                                                          float* __restrict__ s_c, float* __restrict__ s_s)
+{
+    constexpr int kW = 256 / kWave;
+    __shared__ uint32_t base[kGramSlices];
+    __shared__ uint32_t wcnt[kW][kGramSlices + 1];
+    const int tid = threadIdx.x, w = tid / kWave;
+    const int64_t n = A.n, r = blockIdx.x;
+    const int64_t lo = A.bound[r], hi = A.bound[r + 1];
+    if (tid < kGramSlices) base[tid] = off[(int64_t)tid * (n + 1) + r];
+    for (int64_t c0 = lo; c0 < hi; c0 += 256) {
+        if (tid < kW * (kGramSlices + 1)) (&wcnt[0][0])[tid] = 0;
+        __syncthreads();  // also: the previous chunk's bases are final
+        const int64_t j = c0 + tid;
+        const bool valid = j < hi;
+        const uint32_t l = valid ? A.pb[j] : 0u;
+        const uint32_t sl = valid ? gram_slice_of(l, A.k) : (uint32_t)kGramSlices;
+        const uint64_t peers = match_bits<4>(sl);
+        const uint32_t below = count_below(peers);
+        if (below == 0) wcnt[w][sl] = (uint32_t)__popcll(peers);
+        __syncthreads();
+        uint32_t chunk = 0;  // this chunk's inputs of slice tid
+        if (tid < kGramSlices)
+            for (int i = 0; i < kW; ++i) chunk += wcnt[i][tid];
+        if (valid) {
+            uint32_t dst = base[sl] + below;
+            for (int i = 0; i < w; ++i) dst += wcnt[i][sl];
+            s_src[dst] = l;
+            s_b[dst] = A.sb[j];
+            if (s_c) {
+                s_c[dst] = A.cpsi_r[j];
+                s_s[dst] = A.spsi_r[j];
+            }
+        }
+        __syncthreads();  // every read of the bases and counts of this chunk is done
+        if (tid < kGramSlices) base[tid] += chunk;
+    }
+}
+
+hipError_t gram_slices_launch(const GramArgs& a, uint32_t* off, uint32_t* s_src, float* s_b, float* s_c, float* s_s,
+                              hipStream_t s)
+{
+    if (a.n <= 0 || a.k <= 0) return hipSuccess;
+    const unsigned iv = (unsigned)(a.n + 1);
+    LX_LAUNCH("gram_slices", s, (lx_gram_slice_count<<<iv, 256, 0, s>>>(a.pb, a.bound, a.n, a.k, off)));
+    LX_LAUNCH("gram_slices", s, (lx_gram_slice_scan<<<1, 1024, 0, s>>>(off, (int64_t)kGramSlices * (a.n + 1))));
+    LX_LAUNCH("gram_slices", s, (lx_gram_slice_place<<<iv, 256, 0, s>>>(a, off, s_src, s_b, s_c, s_s)));
+    return hipSuccess;
+}
+
+// Interval sums of one slice: workgroup b takes slice b % kGramSlices (so
+// on die b % 8) and four intervals, one per wave; each lane takes the
+// slice's inputs of its wave's interval at stride 64, kBinLoads at a time
+// with every load in flight before any is used, and the wave folds its
+// lanes in a fixed order.
 constexpr int kBinThreads = 256;
+constexpr int kBinWaves = kBinThreads / kWave;
 constexpr int kBinLoads = 4;
 
 template <int NW>
 __global__ __launch_bounds__(kBinThreads) void lx_gram_bins(GramArgs A, GramScratch G)
 {
     constexpr int K = 3 * NW;  // per weight set: sigma, p, q
-    __shared__ double red[kBinThreads / kWave][K];
-    const int tid = threadIdx.x;
     const int64_t n = A.n;
-    const int64_t r = blockIdx.x;  // 0 .. n
+    const int sl = (int)(blockIdx.x % kGramSlices);
+    const int64_t r = (int64_t)(blockIdx.x / kGramSlices) * kBinWaves + threadIdx.x / kWave;
+    if (r > n) return;  // a whole wave; no barriers below
+    const int lane = lane_id();
     const double it2 = 2.0 * A.inv_t;  // e^{-2 d / t}
-    const int64_t lo = A.bound[r], hi = A.bound[r + 1];
+    const int64_t io = (int64_t)sl * (n + 1) + r;
+    const int64_t lo = A.slice_off[io], hi = A.slice_off[io + 1];
     const float right = r < n ? A.sa[r] : 0.f;
     const float left = r > 0 ? A.sa[r - 1] : 0.f;
     double acc[K];
 #pragma unroll
     for (int q = 0; q < K; ++q) acc[q] = 0.0;
-    for (int64_t j0 = lo + tid; j0 < hi; j0 += (int64_t)kBinThreads * kBinLoads) {
+    for (int64_t m0 = lo + lane; m0 < hi; m0 += (int64_t)kWave * kBinLoads) {
         uint32_t src[kBinLoads];
         float bv[kBinLoads], cc[kBinLoads], ss[kBinLoads];
 #pragma unroll
         for (int u = 0; u < kBinLoads; ++u) {
-            const int64_t j = j0 + (int64_t)u * kBinThreads;
-            const int64_t jc = j < hi ? j : lo;  // a valid position; its terms are not used
-            src[u] = A.pb[jc];
-            bv[u] = A.sb[jc];
-            cc[u] = NW == 3 ? A.cpsi_r[jc] : 1.f;
-            ss[u] = NW == 3 ? A.spsi_r[jc] : 0.f;
+            const int64_t m = m0 + (int64_t)u * kWave;
+            const int64_t mc = m < hi ? m : lo;  // a valid position; its terms are not used
+            src[u] = A.slice_src[mc];
+            bv[u] = A.slice_b[mc];
+            cc[u] = NW == 3 ? A.slice_c[mc] : 1.f;
+            ss[u] = NW == 3 ? A.slice_s[mc] : 0.f;
         }
         float dv[kBinLoads];
 #pragma unroll
         for (int u = 0; u < kBinLoads; ++u) dv[u] = A.D[src[u]];
 #pragma unroll
         for (int u = 0; u < kBinLoads; ++u) {
-            if (j0 + (int64_t)u * kBinThreads >= hi) continue;
+            if (m0 + (int64_t)u * kWave >= hi) continue;
             const double d = (double)dv[u];
             double wt[NW];
             if (NW == 3) {
@@ -164,27 +283,32 @@ __global__ __launch_bounds__(kBinThreads) void lx_gram_bins(GramArgs A, GramScra
         for (int d = kWave / 2; d > 0; d >>= 1) x += __shfl_down(x, d);
         acc[q] = x;
     }
-    if (lane_id() == 0) {
+    if (lane == 0) {
 #pragma unroll
-        for (int q = 0; q < K; ++q) red[tid / kWave][q] = acc[q];
+        for (int q = 0; q < K; ++q) G.part[((int64_t)sl * K + q) * (n + 1) + r] = acc[q];
+        if (sl == 0 && r < n) G.mdec[r] = r > 0 ? decay(left, right, it2) : 0.0;
     }
-    __syncthreads();
-    if (tid == 0) {
-        double v[K];
+}
+
+// sigma, p, q of every interval: the slices' sums added in slice order.
+template <int NW>
+__global__ __launch_bounds__(256) void lx_gram_fold(int64_t n, GramScratch G)
+{
+    constexpr int K = 3 * NW;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= K * (n + 1)) return;
+    const int q = (int)(i / (n + 1));
+    const int64_t r = i - (int64_t)q * (n + 1);
+    double v[kGramSlices];
 #pragma unroll
-        for (int q = 0; q < K; ++q) {
-            v[q] = 0.0;
+    for (int sl = 0; sl < kGramSlices; ++sl) v[sl] = G.part[((int64_t)sl * K + q) * (n + 1) + r];
+    double t = 0.0;
 #pragma unroll
-            for (int i = 0; i < kBinThreads / kWave; ++i) v[q] += red[i][q];
-        }
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            G.sigma[w * (n + 1) + r] = v[3 * w];
-            if (r < n) G.p[w * n + r] = v[3 * w + 1];
-            if (r > 0) G.q[w * n + r - 1] = v[3 * w + 2];
-        }
-        if (r < n) G.mdec[r] = r > 0 ? decay(left, right, it2) : 0.0;
-    }
+    for (int sl = 0; sl < kGramSlices; ++sl) t += v[sl];
+    const int w = q / 3, kind = q % 3;
+    if (kind == 0) G.sigma[w * (n + 1) + r] = t;
+    else if (kind == 1) { if (r < n) G.p[w * n + r] = t; }
+    else if (r > 0) G.q[w * n + r - 1] = t;
 }
 
 // One workgroup: S, P and Q over the intervals, written by rank, 3 NW
@@ -446,7 +570,10 @@ template <int NW>
 static hipError_t gram_launch_t(const GramArgs& a, hipStream_t s)
 {
     const GramScratch G = gram_scratch_at(a.stats, a.n, NW);
-    LX_LAUNCH("gram_bins", s, (lx_gram_bins<NW><<<(unsigned)(a.n + 1), kBinThreads, 0, s>>>(a, G)));
+    const int64_t groups = (a.n + 1 + kBinWaves - 1) / kBinWaves;
+    LX_LAUNCH("gram_bins", s, (lx_gram_bins<NW><<<(unsigned)(groups * kGramSlices), kBinThreads, 0, s>>>(a, G)));
+    const int64_t fold = 3 * NW * (a.n + 1);
+    LX_LAUNCH("gram_fold", s, (lx_gram_fold<NW><<<(unsigned)((fold + 255) / 256), 256, 0, s>>>(a.n, G)));
     LX_LAUNCH("gram_scan", s, (lx_gram_scan<NW><<<1, kGramScanThreads, 0, s>>>(a, G)));
     const unsigned nb = (unsigned)((a.n + kGT - 1) / kGT);
     LX_LAUNCH("gram_tile", s, (lx_gram_tile<NW><<<dim3(nb, nb), 256, 0, s>>>(a, G.st)));

@@ -330,6 +330,14 @@ struct GramArgs {
     const float* D = nullptr;       // [k], original order of b
     const uint32_t* bound = nullptr;  // [n + 2]: interval r is sorted b [bound[r], bound[r+1])
     const uint32_t* rank_a = nullptr;  // [n]: rank of each original index of a
+    // b's inputs split by original index into kGramSlices ranges: the inputs
+    // of interval r in slice s are slice_*[slice_off[s (n+1) + r] ..
+    // slice_off[s (n+1) + r + 1]), in ascending sorted position
+    const uint32_t* slice_off = nullptr;  // [kGramSlices (n + 1) + 1]
+    const uint32_t* slice_src = nullptr;  // [k] original index
+    const float* slice_b = nullptr;       // [k] b
+    const float* slice_c = nullptr;       // [k] phased: cos psi
+    const float* slice_s = nullptr;       // [k] phased: sin psi
     const float* cphi_r = nullptr;  // phased: cos/sin of phi by rank of a, of psi by rank of b
     const float* sphi_r = nullptr;
     const float* cpsi_r = nullptr;
@@ -337,7 +345,12 @@ struct GramArgs {
     double* stats = nullptr;        // scratch: see gram.hip
     float* M = nullptr;             // [n][n]
 };
+constexpr int kGramSlices = 8;  // one per compute die
 size_t gram_scratch_bytes(int64_t n, int64_t k, int weight_sets);
+// Fills slice_off (sized kGramSlices (n + 1) + 1) and the slice arrays from
+// a.pb, a.sb, a.bound (and a.cpsi_r, a.spsi_r when s_c is given).
+hipError_t gram_slices_launch(const GramArgs& a, uint32_t* off, uint32_t* s_src, float* s_b, float* s_c, float* s_s,
+                              hipStream_t s);
 // bound[r] = #{b <= s_{r-1}} (r = 1 .. n), bound[0] = 0, bound[n+1] = k.
 hipError_t gram_bounds_launch(const float* sa, int64_t n, const float* sb, int64_t k, uint32_t* bound,
                               hipStream_t s);
