@@ -530,15 +530,23 @@ __global__ __launch_bounds__(kGenThreads) void lx_eval_rows(EvalArgs A, int VG, 
     // entry (t, vi): PL_{t-1} of channels 0, 1 then PR_t of channels 0, 1
     // (C == 2), or PL_{t-1}, PR_t (C == 1); tables read along t (coalesced)
     constexpr int E = 2 * C;  // words per entry
-    for (int64_t i = tid; i < (int64_t)kEvalVG * C * (ni + 1); i += kGenThreads) {
-        const int64_t rowc = i / (ni + 1);  // vi * C + c
-        const int t = (int)(i - rowc * (ni + 1));
-        const int vi = (int)(rowc / C), c = (int)(rowc - (int64_t)vi * C);
-        const int64_t src = ((int64_t)c * A.batch + v0 + vi) * A.ld;
-        const bool have = vi < nv;
-        float* e = rows + (int64_t)t * RW + vi * E;
-        e[c] = have && t > 0 ? A.pl[src + t - 1] : 0.f;
-        e[C + c] = have && t < ni ? A.pr[src + t] : 0.f;
+    for (int t = tid; t <= ni; t += kGenThreads) {
+        // all of this t's entries loaded before any is stored
+        float lv[kEvalVG * C], rv[kEvalVG * C];
+#pragma unroll
+        for (int rowc = 0; rowc < kEvalVG * C; ++rowc) {
+            const int vi = rowc / C, c = rowc % C;
+            const bool have = vi < nv;
+            const int64_t src = ((int64_t)c * A.batch + v0 + (have ? vi : 0)) * A.ld;
+            lv[rowc] = have && t > 0 ? A.pl[src + t - 1] : 0.f;
+            rv[rowc] = have && t < ni ? A.pr[src + t] : 0.f;
+        }
+#pragma unroll
+        for (int rowc = 0; rowc < kEvalVG * C; ++rowc) {
+            float* e = rows + (int64_t)t * RW + (rowc / C) * E;
+            e[rowc % C] = lv[rowc];
+            e[C + rowc % C] = rv[rowc];
+        }
     }
     __syncthreads();
     const float lo_v = si[0], hi_v = si[ni - 1];

@@ -403,7 +403,7 @@ constexpr int kEvalThreads = 1024;
 // sums -- in registers across all vector groups: the searches and decays
 // are done once per output, the weights w of each group are read once, and
 // the sums are written once at the end.
-constexpr int kGradOuts = 4;
+constexpr int kGradOuts = 6;
 
 template <int C>
 __global__ __launch_bounds__(kEvalThreads) void lx_eval_grad_rows(EvalGradArgs A, int VG)
@@ -456,15 +456,26 @@ __global__ __launch_bounds__(kEvalThreads) void lx_eval_grad_rows(EvalGradArgs A
         const int64_t v0 = (int64_t)g * VG;
         const int nv = (int)((A.batch - v0) < VG ? (A.batch - v0) : VG);
         __syncthreads();  // the previous group's rows have been read
-        for (int64_t i = tid; i < (int64_t)kEvalVG * C * (ni + 1); i += kEvalThreads) {
-            const int64_t rowc = i / (ni + 1);  // vi * C + c
-            const int t = (int)(i - rowc * (ni + 1));
-            const int vi = (int)(rowc / C), c = (int)(rowc - (int64_t)vi * C);
-            const int64_t src = ((int64_t)c * A.batch + v0 + vi) * A.ld;
-            const bool have = vi < nv;
-            float* e = rows + (int64_t)t * RW + vi * E;
-            e[c] = have && t > 0 ? A.pl[src + t - 1] : 0.f;
-            e[C + c] = have && t < ni ? A.pr[src + t] : 0.f;
+        // table rows along t (coalesced reads): for each t this thread fills,
+        // all the group's entries are loaded before any is stored, so the
+        // group costs one memory latency, not one per vector and channel
+        for (int t = tid; t <= ni; t += kEvalThreads) {
+            float lv[kEvalVG * C], rv[kEvalVG * C];
+#pragma unroll
+            for (int rowc = 0; rowc < kEvalVG * C; ++rowc) {
+                const int vi = rowc / C, c = rowc % C;
+                const bool have = vi < nv;
+                const int64_t src = ((int64_t)c * A.batch + v0 + (have ? vi : 0)) * A.ld;
+                lv[rowc] = have && t > 0 ? A.pl[src + t - 1] : 0.f;
+                rv[rowc] = have && t < ni ? A.pr[src + t] : 0.f;
+            }
+#pragma unroll
+            for (int rowc = 0; rowc < kEvalVG * C; ++rowc) {
+                const int vi = rowc / C, c = rowc % C;
+                float* e = rows + (int64_t)t * RW + vi * E;
+                e[c] = lv[rowc];
+                e[C + c] = rv[rowc];
+            }
         }
         __syncthreads();
 #pragma unroll
