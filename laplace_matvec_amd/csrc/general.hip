@@ -53,13 +53,12 @@ constexpr int kGenThreads = 1024;
 // sin of its phase.  Inputs past the end go to a bin after the last
 // interval, so they are never visited.
 //
-// lx_bucket_sorted (per group of 4 vectors, 8 with tie sums, one workgroup
-// per group and chunk of sub-chunks, the groups of a chunk on one die so
+// lx_bucket_sorted (per group of 4 vectors, one workgroup per group and
+// chunk of sub-chunks, two workgroups per CU, the groups of a chunk on one die so
 // that they share its layout through that die's L2): the values of the
 // group's vectors are placed in LDS by slot, and thread j owns u_j and v_j of every vector in
 // registers: it adds the alpha parts of interval j and the beta parts of
-// interval j+1, slot by slot (LDS reads and FMAs only).  The
-// next sub-chunk's inputs load while the current one is accumulated.  No
+// interval j+1, slot by slot (LDS reads and FMAs only).  No
 // float atomics, and a fixed summation order, so results are deterministic.
 //
 // The search, the sort and the factors depend on the anchors and phases
@@ -284,8 +283,15 @@ __global__ __launch_bounds__(kGenThreads, VGT == 4 ? 8 : 4) void lx_bucket_sorte
         stn[2] = st[last_extra ? no : 0];
         stn[3] = st[last_extra ? no + 1 : 0];
     };
-    if (j0 < j1) load_sub(j0);
+    // With eight vectors (one workgroup per CU) the next sub-chunk loads
+    // during this one's accumulation; with four, the other workgroup on the
+    // CU covers the load, and the registers a load ahead would hold are
+    // better left free (general n=2^26, k=1024, 64 phased vectors: 6.3 ->
+    // 5.8 ms, and the form with tie sums stays clear of spills).
+    constexpr bool kAhead = VGT != 4;
+    if (kAhead && j0 < j1) load_sub(j0);
     for (int64_t sub0 = j0; sub0 < j1; sub0 += kSub) {
+        if (!kAhead) load_sub(sub0);
         __syncthreads();  // the previous sub-chunk's slots have been read
 #pragma unroll
         for (int j = 0; j < kSubItems; ++j) {
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(kGenThreads, VGT == 4 ? 8 : 4) void lx_bucket_sorte
         }
         const uint32_t s0 = stn[0], s1 = stn[1], e0 = stn[2], e1 = stn[3];
         __syncthreads();
-        if (sub0 + kSub < j1) load_sub(sub0 + kSub);
+        if (kAhead && sub0 + kSub < j1) load_sub(sub0 + kSub);
         // interval tid: every slot read once, its alpha part into u_tid and
         // its beta part into v_{tid-1} (interval 0 has no beta part)
         if (tid <= no) {
@@ -384,9 +390,9 @@ static size_t bucket_sorted_lds(int64_t no, int C, bool ties, int vg = kBucketVG
 
 // Vectors per bucketing workgroup.  Four (32 KB of vector slots, 64 VGPRs):
 // two workgroups share a CU and one's loads overlap the other's
-// accumulation; general n=2^26, k=1024, 64 phased vectors: 8.0 -> 6.3 ms.
-// With the tie sums of a gradient the four-vector form spills, so eight.
-static int bucket_vg(bool ties) { return ties ? kBucketVG : 4; }
+// accumulation; general n=2^26, k=1024, 64 phased vectors: 8.0 -> 5.8 ms,
+// and with the tie sums of a gradient 10.9 -> 8.2 ms.
+static int bucket_vg(bool ties) { return (void)ties, 4; }
 
 // Sums the per-workgroup partials in chunk order (float64) into u, v and,
 // with P = 3, the tie sums.
@@ -472,11 +478,7 @@ hipError_t bucket_launch(BucketArgs& a, hipStream_t s)
                   (lx_bucket_sorted<CC, TT, VV><<<blocks, kGenThreads, shmem, s>>>(a, L, vg, groups, chunks,   \
                                                                                    chunk_len)));               \
     } while (0)
-#define LX_BKS(CC, TT)                     \
-    do {                                   \
-        if (vg <= 4) LX_BKS1(CC, TT, 4);   \
-        else LX_BKS1(CC, TT, 8);           \
-    } while (0)
+#define LX_BKS(CC, TT) LX_BKS1(CC, TT, 4)
         if (two) {
             if (ties) LX_BKS(2, true);
             else LX_BKS(2, false);
