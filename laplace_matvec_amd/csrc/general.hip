@@ -73,6 +73,7 @@ constexpr int kBinStride = 1032;                // per-wave counter row: bins 0 
 __device__ __forceinline__ uint64_t match_bits11(uint32_t d) { return match_bits<11>(d); }
 
 constexpr int kLut = 4096;  // cells of the interval lookup table (lower_bound_lut)
+constexpr int kEvalOuts = 4;  // outputs per thread and step of lx_eval_rows
 
 // Layout arrays in the scratch (bytes, each region 256-byte aligned):
 //   slot  : uint16[n_in]           slot of each input inside its sub-chunk
@@ -509,8 +510,8 @@ hipError_t bucket_launch(BucketArgs& a, hipStream_t s)
 // t reads one 16-byte entry per vector; rows are padded to 36 words so
 // that the rows of different outputs spread over the LDS banks.  The
 // interval comes from a lookup table over the sorted inputs, and each
-// thread loads its next output's anchor and phase factors while it
-// evaluates the current one.
+// thread takes four outputs per step, whose loads, searches and decays
+// overlap.
 
 template <int C>
 __global__ __launch_bounds__(kGenThreads) void lx_eval_rows(EvalArgs A, int VG, int groups, int64_t chunks,
@@ -561,31 +562,35 @@ __global__ __launch_bounds__(kGenThreads) void lx_eval_rows(EvalArgs A, int VG, 
     const int64_t i0 = chunk * chunk_len;
     int64_t i1 = i0 + chunk_len;
     if (i1 > A.n_out) i1 = A.n_out;
-    int64_t i = i0 + tid;
     const int64_t last = i1 > i0 ? i1 - 1 : i0;
-    float o_n = 0.f, c_n = 1.f, s_n = 0.f;
-    auto load_out = [&](int64_t k) {
-        const int64_t kc = k < i1 ? k : last;
-        o_n = A.out_anchor[kc];
-        if (C == 2) {
-            c_n = A.out_cos[kc];
-            s_n = A.out_sin[kc];
+    // kEvalOuts outputs per thread per step (i, i + 1024, ...): their loads,
+    // searches and decays are independent, so their latencies overlap
+    for (int64_t ib = i0 + tid; ib < i1; ib += (int64_t)kEvalOuts * kGenThreads) {
+        float o[kEvalOuts], gc[kEvalOuts][C];
+#pragma unroll
+        for (int u = 0; u < kEvalOuts; ++u) {
+            const int64_t k = ib + (int64_t)u * kGenThreads;
+            const int64_t kc = k < i1 ? k : last;
+            o[u] = A.out_anchor[kc];
+            gc[u][0] = C == 2 ? A.out_cos[kc] : 1.f;
+            if (C == 2) gc[u][C - 1] = A.out_sin[kc];
         }
-    };
-    if (i < i1) load_out(i);
-    for (; i < i1; i += kGenThreads) {
-        const float o = o_n;
-        float gc[C];
-        gc[0] = C == 2 ? c_n : 1.f;
-        if (C == 2) gc[C - 1] = s_n;
-        load_out(i + kGenThreads);
-        const int t = (int)lower_bound_lut<kEvalLut>(si, ni, tab, lo_v, inv_w, o);
-        const float al = t > 0 ? decay_f(si[t - 1], o, A.inv_t) : 0.f;
-        const float be = t < ni ? decay_f(o, si[t], A.inv_t) : 0.f;
-        const float* row = rows + (int64_t)t * RW;
+        int t[kEvalOuts];
+#pragma unroll
+        for (int u = 0; u < kEvalOuts; ++u) t[u] = (int)lower_bound_lut<kEvalLut>(si, ni, tab, lo_v, inv_w, o[u]);
+        float al[kEvalOuts], be[kEvalOuts];
+#pragma unroll
+        for (int u = 0; u < kEvalOuts; ++u) {
+            al[u] = t[u] > 0 ? decay_f(si[t[u] - 1], o[u], A.inv_t) : 0.f;
+            be[u] = t[u] < ni ? decay_f(o[u], si[t[u]], A.inv_t) : 0.f;
+        }
 #pragma unroll
         for (int vi = 0; vi < kEvalVG; ++vi) {
-            if (vi < nv) {
+            if (vi >= nv) continue;
+#pragma unroll
+            for (int u = 0; u < kEvalOuts; ++u) {
+                const int64_t k = ib + (int64_t)u * kGenThreads;
+                const float* row = rows + (int64_t)t[u] * RW;
                 float lv[C], rv[C];
                 if (C == 2) {
                     const float4 e = *reinterpret_cast<const float4*>(row + vi * E);
@@ -600,8 +605,8 @@ __global__ __launch_bounds__(kGenThreads) void lx_eval_rows(EvalArgs A, int VG, 
                 }
                 float acc = 0.f;
 #pragma unroll
-                for (int c = 0; c < C; ++c) acc = fmaf(gc[c], fmaf(al, lv[c], be * rv[c]), acc);
-                A.y[(v0 + vi) * A.n_out + i] = acc;
+                for (int c = 0; c < C; ++c) acc = fmaf(gc[u][c], fmaf(al[u], lv[c], be[u] * rv[c]), acc);
+                if (k < i1) A.y[(v0 + vi) * A.n_out + k] = acc;
             }
         }
     }
