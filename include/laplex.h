@@ -158,7 +158,11 @@ laplex_status laplex_apply_noalloc(laplex_plan plan, const float* x, float* y, i
  *   For a phased plan A carries the phases too (A_il = exp(-|a_i - b_l|)
  *   cos(phi_i - psi_l)); the product of two cosines splits into three
  *   unphased Grams with weights D cos^2 psi, D cos psi sin psi, D sin^2 psi.
- *   Asynchronous on `stream`.
+ *   Asynchronous on `stream`.  The first call on a plan also makes tables
+ *   the plan keeps for later calls (interval bounds and ranks, 4 (n + 2) +
+ *   4 n + 32 (n + 1) bytes; b's inputs grouped by interval and by eighth
+ *   of the original order, 8 k bytes, 16 k when phased); the workspace
+ *   grows on demand as for laplex_apply.
  */
 laplex_status laplex_gram(laplex_plan plan, const float* D, float* M, void* stream);
 
