@@ -309,6 +309,29 @@ def test_gram_repeated_calls_and_temperature(gpu):
             assert oracle.rel_l2(M, ref) < TOL, (t, seed)
 
 
+@pytest.mark.parametrize("n,k,phased", [(5037, 6000, False), (2531, 4000, True)])
+def test_gram_scan_over_several_rounds(gpu, n, k, phased):
+    """More intervals than one round of the scan (4096 per round, 2048 with
+    three weight sets), with a ragged last round: 64 sampled rows of M
+    against the definition."""
+    say(f"[gram rounds] n={n} k={k} phased={phased}")
+    rng = np.random.default_rng(n + 3 * k)
+    a = (rng.standard_normal(n) * 20).astype(np.float32)
+    b = (rng.standard_normal(k) * 20).astype(np.float32)
+    b[rng.integers(0, k, 100)] = a[rng.integers(0, n, 100)]
+    phi = rng.uniform(-np.pi, np.pi, n).astype(np.float32) if phased else None
+    psi = rng.uniform(-np.pi, np.pi, k).astype(np.float32) if phased else None
+    D = rng.uniform(-1, 1, k).astype(np.float32)
+    with lx.laplex_plan_create(dev(a), b=dev(b), phi=None if phi is None else dev(phi),
+                               psi=None if psi is None else dev(psi)) as plan:
+        M = host(lx.laplex_gram(plan, dev(D)))
+    rows = np.unique(np.concatenate([[0, n - 1, n // 2, 4095, 4096, 2047, 2048],
+                                     rng.integers(0, n, 64)]))
+    rows = rows[rows < n]
+    ref = oracle.gram_direct(a, b, D, phi=phi, psi=psi, rows=rows, cols=np.arange(n))
+    assert oracle.rel_l2(M[rows], ref) < TOL
+
+
 def test_gram_symmetric_plan(gpu):
     n = 2000
     a = anchors_with_ties(n, 10.0)
