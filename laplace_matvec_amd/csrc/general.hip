@@ -309,11 +309,17 @@ __global__ __launch_bounds__(kGenThreads, VGT == 4 ? 8 : 4) void lx_bucket_sorte
             cs[p] = make_float4(cfn[j][0], cfn[j][1], cfn[j][2], cfn[j][3]);
             if (TIES) ts[p] = tfn[TIES ? j : 0];
         }
+        bool tied = false;  // any input of this sub-chunk equal to an output anchor
+        if (TIES) {
+#pragma unroll
+            for (int j = 0; j < kSubItems; ++j) tied = tied || tfn[TIES ? j : 0] != 0;
+        }
         const uint32_t s0 = stn[0], s1 = stn[1], e0 = stn[2], e1 = stn[3];
-        __syncthreads();
+        tied = TIES ? __syncthreads_or(tied ? 1 : 0) != 0 : (__syncthreads(), false);
         if (kAhead && sub0 + kSub < j1) load_sub(sub0 + kSub);
         // interval tid: every slot read once, its alpha part into u_tid and
-        // its beta part into v_{tid-1} (interval 0 has no beta part)
+        // its beta part into v_{tid-1} (interval 0 has no beta part); the
+        // tie sums only in sub-chunks that hold a tie (a uniform branch)
         if (tid <= no) {
             for (uint32_t sl = s0; sl < s1; ++sl) {
                 const float4 f = cs[sl];
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(kGenThreads, VGT == 4 ? 8 : 4) void lx_bucket_sorte
                     av[vi][0] = fmaf(f.z, xv[vi], av[vi][0]);
                     if (C == 2) av[vi][C - 1] = fmaf(f.w, xv[vi], av[vi][C - 1]);
                 }
-                if (TIES) {  // a tie's alpha is exactly 1: its factors are the phase's cos, sin
+                if (TIES && tied) {  // a tie's alpha is exactly 1: its factors are the phase's cos, sin
                     const float tw = ts[sl] ? 1.f : 0.f;
 #pragma unroll
                     for (int vi = 0; vi < (TIES ? VGT : 1); ++vi) {
