@@ -245,11 +245,17 @@ laplex_status laplex_plan_set_option(laplex_plan plan, int option, int64_t value
 laplex_status laplex_plan_set_temperature(laplex_plan plan, double t);
 
 /* Kernel timing: while enabled, every kernel the library launches is
- * bracketed by HIP events on its stream.  laplex_profile_collect waits for
- * the recorded events and folds their durations into per-kernel totals;
+ * bracketed by HIP events on its stream (timing-only events, recorded
+ * without a system-scope fence, so they order no memory for the host).
+ * laplex_profile_collect waits for the recorded events and folds their
+ * durations into per-kernel totals;
  * laplex_profile_entry reads entry `i` (returns INVALID_ARGUMENT past the
  * end).  Names are static strings.  Not thread-safe; for benchmarks. */
 laplex_status laplex_profile_enable(int on);
+/* While enabled, bracket only the launches whose label equals `label`
+ * (copied; NULL or "" brackets every launch, the default): fewer event
+ * records between launches when only one kernel's time is wanted. */
+laplex_status laplex_profile_only(const char* label);
 laplex_status laplex_profile_reset(void);
 laplex_status laplex_profile_collect(void);
 laplex_status laplex_profile_entry(int i, const char** name, int64_t* launches, double* total_ms);

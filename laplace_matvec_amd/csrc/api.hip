@@ -217,6 +217,7 @@ struct Pending {
     hipEvent_t a, b;
 };
 bool g_prof_on = false;
+std::string g_prof_only;  // when not empty: the one label bracketed
 std::vector<ProfEntry> g_prof;
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_event_pool;
@@ -228,8 +229,11 @@ hipEvent_t take_event()
         g_event_pool.pop_back();
         return e;
     }
+    // Timing only: read after the caller has synchronised the device, so the
+    // record needs no system-scope fence (a fence per record flushes caches
+    // and adds microseconds between short launches).
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
 }
 
@@ -240,6 +244,7 @@ namespace lx {
 int prof_begin(const char* name, hipStream_t s)
 {
     if (!g_prof_on) return -1;
+    if (!g_prof_only.empty() && g_prof_only != name) return -1;
     Pending p{name, take_event(), take_event()};
     if (!p.a || !p.b) return -1;
     (void)hipEventRecord(p.a, s);
@@ -1567,6 +1572,12 @@ laplex_status laplex_gram(laplex_plan p, const float* D, float* M, void* stream)
 laplex_status laplex_profile_enable(int on)
 {
     g_prof_on = on != 0;
+    return LAPLEX_OK;
+}
+
+laplex_status laplex_profile_only(const char* label)
+{
+    g_prof_only = label ? label : "";
     return LAPLEX_OK;
 }
 

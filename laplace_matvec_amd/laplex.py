@@ -43,6 +43,7 @@ SIGNATURES = {
     "laplex_plan_set_temperature": (_I32, [_VP, ctypes.c_double]),
     "laplex_backward": (_I32, [_VP, _VP, _VP, _I64, _I32, _VP, _VP, _VP, _VP, _VP, _VP]),
     "laplex_profile_enable": (_I32, [_I32]),
+    "laplex_profile_only": (_I32, [ctypes.c_char_p]),
     "laplex_profile_reset": (_I32, []),
     "laplex_profile_collect": (_I32, []),
     "laplex_profile_entry": (_I32, [_I32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_I64),
@@ -300,6 +301,11 @@ def laplex_plan_destroy(plan: Plan):
 
 def profile_enable(on: bool = True):
     load().laplex_profile_enable(int(on))
+
+
+def profile_only(label: str | None = None):
+    """Bracket only launches labelled `label` (None: every launch)."""
+    load().laplex_profile_only(None if label is None else label.encode())
 
 
 def profile_reset():

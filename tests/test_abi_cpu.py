@@ -96,6 +96,17 @@ def test_apply_and_gram_reject_bad_arguments():
         assert lib.laplex_status_str(s)
 
 
+def test_profile_label_filter_host_side():
+    # host state only: no launch, no event; set, clear, and read back nothing
+    lx.profile_only("sort_pass")
+    lx.profile_only(None)
+    lx.profile_only("")
+    lib = lx.load()
+    assert lib.laplex_profile_enable(0) == lx.OK
+    assert lib.laplex_profile_reset() == lx.OK
+    assert lx.profile_read() == {}
+
+
 def test_valid_arguments_without_gpu_report_no_device():
     try:
         import torch
