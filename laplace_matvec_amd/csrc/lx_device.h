@@ -415,6 +415,24 @@ __device__ __forceinline__ double decay(float lo, float hi, double inv_t)
     return lo == hi ? 1.0 : exp_nonpos(((double)lo - (double)hi) * inv_t);
 }
 
+// e^x for x <= 0 (x = -inf gives 0) to about 1e-7 relative error, in nine
+// instructions: x / ln 2 split in float64 into an integer k and a fraction
+// f in [-1/2, 1/2] (exact), 2^f by the hardware's float32 exp2 (1 ulp),
+// scaled by 2^k in float64 (results below 2^-1074 flush to 0).  For sums of
+// positive terms whose results are stored in float32.
+__device__ __forceinline__ double exp_nonpos_fast(double x)
+{
+    const double y = fmax(x * 1.4426950408889634, -1100.0);  // log2(e); 2^-1100 is 0 in float64
+    const double k = rint(y);
+    return ldexp((double)__builtin_amdgcn_exp2f((float)(y - k)), (int)k);
+}
+
+// decay() to about 1e-7 relative error (exp_nonpos_fast); 1 for lo == hi.
+__device__ __forceinline__ double decay_fast(float lo, float hi, double inv_t)
+{
+    return lo == hi ? 1.0 : exp_nonpos_fast(((double)lo - (double)hi) * inv_t);
+}
+
 // exp(-(hi - lo) / t) in float32 for anchors lo <= hi, it = 1 / t.
 __device__ __forceinline__ float decay_f(float lo, float hi, float it)
 {

@@ -309,6 +309,28 @@ def test_gram_repeated_calls_and_temperature(gpu):
             assert oracle.rel_l2(M, ref) < TOL, (t, seed)
 
 
+@pytest.mark.parametrize("phased", [False, True])
+def test_gram_wide_anchor_span(gpu, phased):
+    """Anchors spanning 2500 t, in ascending original order: no centre
+    serves all the anchors, so tiles near the diagonal (64 neighbouring
+    anchors, about 230 t) split the decay about their own centre and tiles
+    far from it take a decay per entry."""
+    rng = np.random.default_rng(2500 + phased)
+    n, k = 700, 6000
+    a = np.sort(rng.uniform(0, 2500, n)).astype(np.float32)
+    b = rng.uniform(-100, 2600, k).astype(np.float32)
+    phi = rng.uniform(-np.pi, np.pi, n).astype(np.float32) if phased else None
+    psi = rng.uniform(-np.pi, np.pi, k).astype(np.float32) if phased else None
+    D = rng.uniform(0, 1, k).astype(np.float32)
+    with lx.laplex_plan_create(dev(a), b=dev(b), phi=None if phi is None else dev(phi),
+                               psi=None if psi is None else dev(psi)) as plan:
+        M = host(lx.laplex_gram(plan, dev(D)))
+    ref = oracle.gram_direct(a, b, D, phi=phi, psi=psi)
+    assert oracle.rel_l2(M, ref) < TOL
+    near = np.abs(np.subtract.outer(np.arange(n), np.arange(n))) < 64
+    assert oracle.rel_l2(M[near], ref[near]) < TOL
+
+
 @pytest.mark.parametrize("n,k,phased", [(5037, 6000, False), (2531, 4000, True)])
 def test_gram_scan_over_several_rounds(gpu, n, k, phased):
     """More intervals than one round of the scan (4096 per round, 2048 with
