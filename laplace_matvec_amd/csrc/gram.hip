@@ -300,12 +300,7 @@ __global__ __launch_bounds__(kBinThreads) void lx_gram_bins(GramArgs A, GramScra
         }
     }
 #pragma unroll
-    for (int q = 0; q < K; ++q) {
-        double x = acc[q];
-#pragma unroll
-        for (int d = kWave / 2; d > 0; d >>= 1) x += __shfl_down(x, d);
-        acc[q] = x;
-    }
+    for (int q = 0; q < K; ++q) acc[q] = wave_sum_dpp(acc[q]);
     if (lane == 0) {
 #pragma unroll
         for (int q = 0; q < K; ++q) G.part[((int64_t)sl * K + q) * (n + 1) + r] = acc[q];

@@ -177,6 +177,23 @@ __device__ __forceinline__ Aff<double> read_lane(Aff<double> x, int l)
     return Aff<double>{read_lane(x.m, l), read_lane(x.v, l)};
 }
 
+// Sum of x over the 64 lanes of a wave, returned in every lane, in a fixed
+// order: distances 1, 2, 4, 8 inside each row of 16 lanes by DPP (lane 15
+// of each row then holds its row's sum), rows 0 + 1 and 2 + 3 by a row
+// broadcast of lane 15, the two halves by a broadcast of lane 31; lane 63
+// holds the total.  All lanes of the wave must be active.  No LDS round
+// trip, unlike a shuffle per step.
+__device__ __forceinline__ double wave_sum_dpp(double x)
+{
+    x += dpp_move<0x111>(x, 0.0);
+    x += dpp_move<0x112>(x, 0.0);
+    x += dpp_move<0x114>(x, 0.0);
+    x += dpp_move<0x118>(x, 0.0);
+    x += dpp_move<0x142, 0xA>(x, 0.0);  // rows 1, 3 += lane 15 of rows 0, 2
+    x += dpp_move<0x143, 0xC>(x, 0.0);  // rows 2, 3 += lane 31
+    return read_lane(x, kWave - 1);
+}
+
 // Inclusive scan over the lanes of a wave in ascending lane order.  All
 // lanes of the wave must be active.  Float64 composites: distances 1, 2, 4,
 // 8 inside each row of 16 lanes by DPP, then each row takes the composite
