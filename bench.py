@@ -60,7 +60,13 @@ def parse():
 #    writes key + index, 12 B for the first pass and 16 B for each later
 #    one; the scan reads s and x twice and writes y once; the gather and the
 #    scatter each move an index, the value in and the value out).  The
-#    roofline fraction is quoted on these.
+#    roofline fraction is quoted on these.  When x travels through the
+#    radix passes as value rows (plan_create_apply), those passes carry out
+#    the gather, so each of the four launches is credited with a quarter of
+#    the gather's bytes (4 + 8B per element); the sort's own share is given
+#    beside it.  General case: the evaluation reads the output anchors and
+#    phase factors and writes y (4 + 8 + 4B), the bucketing reads w (4B) and
+#    its layout pass the input anchors and phase factors (4 + 8).
 #  * design bytes: what this design's kernels must move: radix passes carry
 #    x as a value row and write replay records (2 B per key plus a 6 B x 256
 #    table per 8192-key tile) instead of an index; the four backward replays
@@ -70,11 +76,15 @@ TILE_TABLE = 6.0 * 256 / 8192
 SURVEY_SORT_PASS = (12.0 + 16.0 + 16.0 + 16.0) / 4  # average over the four launches of one sort
 
 
-def survey_bytes(kernel: str, n: int, batch: int = 1, channels: int = 1) -> float | None:
+def survey_bytes(kernel: str, n: int, batch: int = 1, channels: int = 1, carried_rows: int = 0) -> float | None:
     factors = 8.0 if channels == 2 else 0.0
     per = {
         "sort_hist": 4.0,
-        "sort_pass": SURVEY_SORT_PASS,
+        "sort_pass": SURVEY_SORT_PASS + ((4.0 + 8.0 * carried_rows) / 4 if carried_rows else 0.0),
+        "eval": 4.0 + factors + 4.0 * batch,
+        "bucket_layout": 4.0 + factors,
+        "bucket_sorted": 4.0 * batch,
+        "small_sym": 4.0 + factors + 8.0 * batch,
         # one gather (index, value in, value out) and one scatter, each
         # spread over the four replays that carry it out
         "replay_forward": (4.0 + 8.0 * batch) / 4,
@@ -296,6 +306,8 @@ def main():
 
     rec = counter_record(W.name)
     rec_labels = rec["labels"] if rec else {}
+    channels = 2 if W.phased else 1
+    carried = batch if W.kind == "sym" else 0  # value rows through the radix passes
     roof = None
     if dominant and dominant_avg_ms:
         avg_s = dominant_avg_ms / 1e3
@@ -303,8 +315,8 @@ def main():
             ab = gram_bytes(dominant, n, W.k)
             design = ab
         else:
-            ab = survey_bytes(dominant, n, batch)
-            design = model_bytes(dominant, n, batch, vals=batch if W.kind == "sym" else 0)
+            ab = survey_bytes(dominant, n, batch, channels, carried)
+            design = model_bytes(dominant, n, batch, vals=carried)
         if ab is not None:
             ach = ab / avg_s / 1e9
             traffic = rec_labels.get(dominant, (None, None))[1]
@@ -314,6 +326,13 @@ def main():
                     "design_bytes_per_launch": design,
                     "design_frac": None if design is None else round(design / avg_s / 1e9 / PEAK_HBM_GBPS, 4),
                     "counter_record": rec["path"] if rec else None}
+            if dominant == "sort_pass" and carried:
+                sort_only = survey_bytes("sort_pass", n, batch)
+                roof["sort_only_bytes_per_launch"] = sort_only
+                roof["sort_only_frac"] = round(sort_only / avg_s / 1e9 / PEAK_HBM_GBPS, 4)
+                roof["bytes_note"] = ("scope-table bytes of one radix pass (12 B per element for the first, "
+                                      "16 for the others) plus a quarter of the gather's (4 + 8B per element), "
+                                      "which these passes carry out with x travelling as value rows")
     extra = {}
     # per phase: time in this run, survey / design bytes, and what the counters saw
     phases = {}
@@ -322,8 +341,8 @@ def main():
         if ms_ph == 0:
             continue
         d = {"ms_per_step": round(ms_ph, 4)}
-        sb = [survey_bytes(k, n, batch) * kernels[k]["launches_per_step"] for k in labels
-              if k in kernels and survey_bytes(k, n, batch) is not None]
+        sb = [survey_bytes(k, n, batch, channels, carried) * kernels[k]["launches_per_step"] for k in labels
+              if k in kernels and survey_bytes(k, n, batch, channels, carried) is not None]
         if W.kind == "sym" and sb:
             d["survey_gbps"] = round(sum(sb) / (ms_ph / 1e3) / 1e9, 1)
         cb = [rec_labels[k][0] * rec_labels[k][1] for k in labels if k in kernels and k in rec_labels]

@@ -48,6 +48,16 @@ def test_step_byte_model_symmetric_one_vector():
     # passes 12 + 3 x 16, scans 8 + 12, scatter 12 (the gather rides in the
     # sort; the table's sort total of 68 is 4 more than its listed items)
     assert four == pytest.approx(96.0 * n)
+    # x travelling through the passes: the four launches carry the gather's
+    # 4 + 8B bytes per element between them, on top of the sort's 15 each
+    for batch in (1, 16):
+        with_rows = b.survey_bytes("sort_pass", n, batch, carried_rows=batch)
+        assert 4 * (with_rows - b.survey_bytes("sort_pass", n, batch)) == pytest.approx((4.0 + 8.0 * batch) * n)
+    # general case, 64 phased vectors: the bucketing reads w, its layout the
+    # anchors and phase factors, the evaluation those and writes y
+    assert b.survey_bytes("bucket_sorted", n, 64, 2) == pytest.approx(256.0 * n)
+    assert b.survey_bytes("bucket_layout", n, 64, 2) == pytest.approx(12.0 * n)
+    assert b.survey_bytes("eval", n, 64, 2) == pytest.approx(268.0 * n)
     assert b.gram_bytes("gram_tile", 4096, 3 << 20) == 4.0 * 4096 * 4096
 
 
