@@ -158,6 +158,9 @@ laplex_status laplex_apply_noalloc(laplex_plan plan, const float* x, float* y, i
  *   For a phased plan A carries the phases too (A_il = exp(-|a_i - b_l|)
  *   cos(phi_i - psi_l)); the product of two cosines splits into three
  *   unphased Grams with weights D cos^2 psi, D cos psi sin psi, D sin^2 psi.
+ *   Precision: interval sums, scans and the per-entry combination in
+ *   float64 (each input's decay to about 1e-7 relative, the decays between
+ *   anchors exact to float64), M rounded once to float32.
  *   Asynchronous on `stream`.  The first call on a plan also makes tables
  *   the plan keeps for later calls (interval bounds and ranks, 4 (n + 2) +
  *   4 n + 32 (n + 1) bytes; b's inputs grouped by interval and by eighth

@@ -238,7 +238,7 @@ hipError_t gram_slices_launch(const GramArgs& a, uint32_t* off, uint32_t* s_src,
 // made this kernel bound by its vector instructions.
 constexpr int kBinThreads = 256;
 constexpr int kBinWaves = kBinThreads / kWave;
-constexpr int kBinLoads = 4;
+constexpr int kBinLoads = 2;  // 3 * 2^20 inputs over 4097 intervals and 8 slices: about 96 per wave
 
 template <int NW>
 __global__ __launch_bounds__(kBinThreads) void lx_gram_bins(GramArgs A, GramScratch G)

@@ -218,6 +218,31 @@ def test_general_both_directions(gpu, n, k, phased, algo):
     assert max_rel(z, oracle.apply_dense(a, w, b=b, transpose=True, **kw)) < TOL
 
 
+@pytest.mark.parametrize("algo", [lx.ALGO_BUCKET, lx.ALGO_EVALUATE])
+def test_general_repeat_bitwise(gpu, algo):
+    """A small sorted side (1024 anchors, the bucketing in LDS or the
+    evaluation): the same products three times, on the same plan and on a
+    new one, give the same bits (no atomics; fixed summation order)."""
+    rng = np.random.default_rng(1024)
+    n, k = 200000, 1024
+    a = (rng.standard_normal(n) * 100).astype(np.float32)
+    b = rng.uniform(-300, 300, k).astype(np.float32)
+    kw = dict(phi=rng.uniform(0, 6.3, n).astype(np.float32), psi=rng.uniform(0, 6.3, k).astype(np.float32))
+    x = dev(rng.standard_normal((5, k)))
+    w = dev(rng.standard_normal((5, n)))
+    ys, zs = [], []
+    for rep in range(2):
+        with lx.laplex_plan_create(dev(a), b=dev(b), **{key: dev(v) for key, v in kw.items()}) as plan:
+            lx.laplex_plan_set_option(plan, lx.OPT_GENERAL_ALGO, algo)
+            for _ in range(2 if rep == 0 else 1):
+                ys.append(host(lx.laplex_apply(plan, x)))
+                zs.append(host(lx.laplex_apply(plan, w, transpose=True)))
+    assert all(np.array_equal(ys[0], y) for y in ys[1:])
+    assert all(np.array_equal(zs[0], z) for z in zs[1:])
+    assert max_rel(ys[0], oracle.apply_sweep(a, host(x), b=b, **kw)) < TOL
+    assert max_rel(zs[0], oracle.apply_sweep(a, host(w), b=b, transpose=True, **kw)) < TOL
+
+
 @pytest.mark.parametrize("phased", [False, True])
 @pytest.mark.parametrize("algo", [lx.ALGO_BUCKET, lx.ALGO_EVALUATE])
 def test_general_partial_vector_groups(gpu, phased, algo):
@@ -352,6 +377,30 @@ def test_gram_scan_over_several_rounds(gpu, n, k, phased):
     rows = rows[rows < n]
     ref = oracle.gram_direct(a, b, D, phi=phi, psi=psi, rows=rows, cols=np.arange(n))
     assert oracle.rel_l2(M[rows], ref) < TOL
+
+
+@pytest.mark.parametrize("phased", [False, True])
+def test_gram_repeat_bitwise(gpu, phased):
+    """Gram calls on one plan and on a new plan give the same bits: the
+    per-plan grouping of the inputs is stable, and the slices, intervals and
+    lanes are added in a fixed order."""
+    rng = np.random.default_rng(31 + phased)
+    n, k = 900, 120000
+    a = (rng.standard_normal(n) * 20).astype(np.float32)
+    b = (rng.standard_normal(k) * 20).astype(np.float32)
+    kw = {}
+    if phased:
+        kw = dict(phi=rng.uniform(0, 6.3, n).astype(np.float32), psi=rng.uniform(0, 6.3, k).astype(np.float32))
+    D = dev(rng.uniform(-1, 1, k))
+    outs = []
+    for rep in range(2):
+        with lx.laplex_plan_create(dev(a), b=dev(b), **{key: dev(v) for key, v in kw.items()}) as plan:
+            for _ in range(2 if rep == 0 else 1):
+                outs.append(host(lx.laplex_gram(plan, D)))
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+    rows = np.arange(0, n, 37)
+    ref = oracle.gram_direct(a, b, host(D), rows=rows, cols=np.arange(n), **kw)
+    assert oracle.rel_l2(outs[0][rows], ref) < TOL
 
 
 def test_gram_symmetric_plan(gpu):
