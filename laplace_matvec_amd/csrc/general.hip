@@ -590,12 +590,15 @@ __global__ __launch_bounds__(kGenThreads) void lx_eval_rows(EvalArgs A, int VG, 
             al[u] = t[u] > 0 ? decay_f(si[t[u] - 1], o[u], A.inv_t) : 0.f;
             be[u] = t[u] < ni ? decay_f(o[u], si[t[u]], A.inv_t) : 0.f;
         }
+        // every value of the step first (a vector past nv reads its zero
+        // table entries), then the stores: a table read whose only use is a
+        // guarded store is otherwise moved behind the guard, one LDS wait
+        // per value instead of one for all of them
+        float outv[kEvalVG][kEvalOuts];
 #pragma unroll
         for (int vi = 0; vi < kEvalVG; ++vi) {
-            if (vi >= nv) continue;
 #pragma unroll
             for (int u = 0; u < kEvalOuts; ++u) {
-                const int64_t k = ib + (int64_t)u * kGenThreads;
                 const float* row = rows + (int64_t)t[u] * RW;
                 float lv[C], rv[C];
                 if (C == 2) {
@@ -612,7 +615,20 @@ __global__ __launch_bounds__(kGenThreads) void lx_eval_rows(EvalArgs A, int VG, 
                 float acc = 0.f;
 #pragma unroll
                 for (int c = 0; c < C; ++c) acc = fmaf(gc[u][c], fmaf(al[u], lv[c], be[u] * rv[c]), acc);
-                if (k < i1) A.y[(v0 + vi) * A.n_out + k] = acc;
+                outv[vi][u] = acc;
+            }
+        }
+#pragma unroll
+        for (int vi = 0; vi < kEvalVG; ++vi)
+#pragma unroll
+            for (int u = 0; u < kEvalOuts; ++u) asm volatile("" : "+v"(outv[vi][u]));
+#pragma unroll
+        for (int vi = 0; vi < kEvalVG; ++vi) {
+            if (vi >= nv) continue;
+#pragma unroll
+            for (int u = 0; u < kEvalOuts; ++u) {
+                const int64_t k = ib + (int64_t)u * kGenThreads;
+                if (k < i1) A.y[(v0 + vi) * A.n_out + k] = outv[vi][u];
             }
         }
     }
