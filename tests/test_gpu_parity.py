@@ -176,6 +176,34 @@ def test_determinism_repeated(gpu):
     assert all(np.array_equal(outs[0], o) for o in outs)
 
 
+def test_profile_only_one_label(gpu):
+    """Kernel timing limited to one label: the same launches of that label
+    are timed, and no other label is."""
+    n = 70000
+    a = dev(RNG.standard_normal(n))
+    x = dev(RNG.standard_normal((2, n)))
+
+    def timed(label):
+        lx.profile_only(label)
+        lx.profile_reset()
+        lx.profile_enable(True)
+        try:
+            with lx.laplex_plan_create(a) as plan:
+                lx.laplex_apply(plan, x)
+            torch.cuda.synchronize()
+            return lx.profile_read()
+        finally:
+            lx.profile_enable(False)
+            lx.profile_only(None)
+
+    every = timed(None)
+    assert len(every) >= 2
+    label = max(every, key=lambda k: every[k][1])
+    only = timed(label)
+    assert set(only) == {label}
+    assert only[label][0] == every[label][0] and only[label][1] > 0
+
+
 def test_apply_overlap_rejected(gpu):
     a = dev(RNG.standard_normal(100))
     buf = torch.zeros(300, device="cuda")
