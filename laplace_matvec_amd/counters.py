@@ -218,7 +218,7 @@ def stats_markdown(stats_csv: str, title: str, command: str, note: str = "") -> 
         pct = float(_col(r, "Percentage", "Percent"))
         rows.append((name, calls, avg, pct))
     rows.sort(key=lambda t: -t[3])
-    out = [f"# rocprofv3 kernel statistics: {title}", "", "Command (repository root on the GPU box, committed files only):",
+    out = [f"# rocprofv3 kernel statistics: {title}", "", "Command (run from the repository root; committed files only):",
            "", "```"] + command.split(" ;; ") + ["```", ""]
     if note:
         out += [note, ""]
